@@ -1,0 +1,213 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: pa_write_kv stores the new
+token of every sequence into its slot, then pa_decode (plus its partition merge when
+the plan splits) attends over every sequence's context.  Block tables come from the
+library's block manager before timing (allocation is host work, off the timed path).
+Inputs are synthetic, seeded, and resident in HBM before the timed region starts.
+
+Prints one JSON line: value = algorithmic KV bytes read per step / step time (GB/s),
+plus decode tokens/s, a roofline entry for the decode kernel (HIP events on the launch
+stream) and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload opt13b_layer]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="opt13b_layer")
+    ap.add_argument("--partition-size", type=int, default=-1,
+                    help="-1: the workload's setting (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one device copy of 1 GiB (for hardware-counter scaling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this operator is built and measured on a single "
+              "MI355X (no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_89_amd as pa
+    import workloads
+
+    torch.cuda.set_device(0)
+    names = list(workloads.SPECS)
+    sp = workloads.SPECS[args.workload]
+    seed = 8900 + names.index(args.workload)
+    P = sp.partition_size if args.partition_size < 0 else args.partition_size
+
+    # ---- inputs (untimed): lengths, block tables from the block manager, pools, new rows
+    ctx, free = workloads.draw_lengths(sp, seed)
+    pg, pl = workloads.prefix_groups(sp)
+    bm = pa.BlockManager(sp.num_blocks, sp.block_size, free)
+    tables, _ = bm.alloc_tables(ctx, sp.max_blocks, pg, pl)
+    q, kc, vc, k_scale, v_scale = workloads.device_pool(sp, seed)
+    S, Hq, Hkv, D, B = sp.num_seqs, sp.num_heads, sp.num_kv_heads, sp.head_dim, sp.block_size
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 1)
+    src_t = {"f16": torch.float16, "bf16": torch.bfloat16}[sp.src_dtype]
+    k_new = torch.randn((S, Hkv, D), generator=g, device="cuda").to(src_t)
+    v_new = torch.randn((S, Hkv, D), generator=g, device="cuda").to(src_t)
+    tables_d = torch.from_numpy(tables).cuda()
+    ctx_d = torch.from_numpy(ctx).cuda()
+    seq_ids = torch.arange(S, dtype=torch.int32, device="cuda")
+    positions = (ctx_d - 1).to(torch.int32)
+    max_ctx = int(ctx.max())
+    out = torch.empty_like(q)
+    used_P, nparts = pa.decode_plan(S, Hq, Hkv, D, B, max_ctx, P)
+    ws_bytes = pa.decode_workspace_size(S, Hq, Hkv, D, B, max_ctx, P)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    k_inv = 1.0 / k_scale if sp.kv_dtype == "e4m3" else 1.0
+    v_inv = 1.0 / v_scale if sp.kv_dtype == "e4m3" else 1.0
+    stream = torch.cuda.current_stream()
+
+    def write():
+        pa.write_kv(k_new, v_new, kc, vc, tables_d, seq_ids, positions, k_inv, v_inv,
+                    stream=stream)
+
+    def decode():
+        pa.decode(q, kc, vc, tables_d, ctx_d, max_ctx, sp.scale, k_scale, v_scale,
+                  partition_size=P, out=out, workspace=ws, stream=stream)
+
+    kv_bytes = workloads.kv_bytes(sp, ctx)  # algorithmic K+V bytes one decode pass reads
+
+    for _ in range(args.warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, device synchronised on both sides
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        write()
+        ev[i][0].record(stream)
+        decode()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_ms_mean = float(np.mean(dec_ms))
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (dec_ms_mean * 1e-3) / 1e9
+
+    if args.copy_calibration:
+        # A plain device copy of known size: the hardware-counter runs scale FETCH_SIZE /
+        # WRITE_SIZE of the decode kernel by what the counters read for this copy.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, args.cpu_seconds)
+
+    line = {
+        "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + decode tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp.kv_dtype,
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "config": {
+            "workload": sp.name, "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv,
+            "head_dim": D, "block_size": B, "context_lens": f"U[{sp.ctx_lo},{sp.ctx_hi}]"
+            + (f"+{sp.prompt_len}" if sp.prompt_len else ""), "num_blocks": sp.num_blocks,
+            "q_dtype": sp.q_dtype, "kv_dtype": sp.kv_dtype, "partition_size": used_P,
+            "num_partitions": nparts, "kv_bytes_per_step": kv_bytes, "seed": seed,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "paged_decode_kernel" + (" + merge_partitions_kernel" if nparts > 1 else ""),
+            "mean_launch_ms": round(dec_ms_mean, 5),
+            "median_launch_ms": round(float(np.median(dec_ms)), 5),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, target_s):
+    """The oracle (plain fp64 C++) on the host cores, over a bounded sample of sequences
+    (all heads of the first few), scaled to the same GB/s metric."""
+    import torch
+
+    import oracle
+    import workloads
+
+    dt = {"f16": oracle.F16, "bf16": oracle.BF16, "e4m3": oracle.E4M3}
+    threads = min(os.cpu_count() or 1, 16)
+
+    def sample(nseq):
+        rows = tables[:nseq]
+        used = np.unique(rows[rows >= 0])
+        remap = np.full(sp.num_blocks, -1, np.int32)
+        remap[used] = np.arange(used.size, dtype=np.int32)
+        t = np.where(rows >= 0, remap[np.maximum(rows, 0)], -1).astype(np.int32)
+        idx = torch.from_numpy(used.astype(np.int64)).cuda()
+
+        def bits(x):
+            x = x.index_select(0, idx).cpu().contiguous()
+            return x.numpy() if x.dtype == torch.uint8 else x.view(torch.int16).numpy().view(np.uint16)
+
+        qb = q[:nseq].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        return qb, bits(kc), bits(vc), t, ctx[:nseq].copy()
+
+    def run(nseq):
+        qb, kb, vb, t, c = sample(nseq)
+        t0 = time.perf_counter()
+        oracle.decode(qb, dt[sp.q_dtype], kb, vb, dt[sp.kv_dtype], t, c, sp.num_kv_heads,
+                      sp.block_size, sp.scale, k_scale, v_scale, threads=threads)
+        return time.perf_counter() - t0, workloads.kv_bytes(sp, c)
+
+    dt1, _ = run(1)  # probe: one sequence
+    nseq = int(max(1, min(sp.num_seqs, target_s / max(dt1, 1e-3))))
+    secs, nbytes = run(nseq)
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(secs, 2),
+            "sample": f"{nseq} of {sp.num_seqs} sequences, all {sp.num_heads} heads "
+                      f"({nbytes} KV bytes), fp64 C++ oracle with {threads} threads"}
+
+
+if __name__ == "__main__":
+    main()

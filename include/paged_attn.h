@@ -1,0 +1,194 @@
+/*
+ * libpaged_attn — paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Every call returns a pa_status (0 = OK,
+ * negative = error) unless stated otherwise; pa_last_error() then gives a message.
+ *
+ * The operation and its vocabulary come from:
+ *   [P1] "PagedAttention: Mathematical Foundations, Virtual Memory Block Allocation,
+ *        and Zero-Waste KV Cache Serving" (llms.blog)
+ *   [P2] "Pytorch implementation of paper: Efficient Memory Management for Large
+ *        Language Model Serving with PagedAttention (2023)" (aishastr.live)
+ *   [P3] the 10100.com article on the retirement of vLLM's PagedAttention kernel
+ *
+ * Conventions for the device calls (pa_write_kv, pa_decode):
+ *   - every pointer is device memory owned by the caller, every tensor is contiguous
+ *     row-major with the shape written beside it;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream);
+ *     the call only enqueues work and never synchronises; argument errors are found
+ *     on the host before anything is launched and leave device memory untouched;
+ *   - device-resident tables and lengths are read by the kernels as given; entries
+ *     outside [0, num_blocks) are never dereferenced (the decode clamps them to block 0,
+ *     the writer skips them) so malformed tables give wrong numbers, not faults;
+ *   - the library allocates no device memory: scratch space is a caller-provided
+ *     workspace sized by pa_decode_workspace_size().
+ *
+ * Cache layout (both K and V, every dtype): [num_blocks][num_kv_heads][block_size][head_dim],
+ * i.e. the per-block [block_size, head_dim] key and value tiles of [P1] sec. 3 (eq. for
+ * K_j, V_j) and sec. 7 (pseudocode), one tile per KV head.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,     /* null pointer, inconsistent sizes, bad handle, short workspace */
+  PA_ERR_UNSUPPORTED = -2,     /* shape or dtype outside the compiled set */
+  PA_ERR_NO_BLOCKS = -3,       /* the free list cannot satisfy the request (state unchanged) */
+  PA_ERR_TABLE_OVERFLOW = -4,  /* a sequence needs more than max_blocks_per_seq blocks */
+  PA_ERR_HIP = -5              /* the HIP runtime reported an error at launch */
+} pa_status;
+
+/* Storage / arithmetic types.  PA_FP8_E4M3 is the OCP 8-bit E4M3 format (no infinities,
+ * S.1111.111 = NaN, largest finite 448), stored one byte per element. */
+typedef enum { PA_F16 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+
+typedef struct pa_block_manager pa_block_manager; /* opaque, host memory only */
+
+/* Message for the last error on the calling thread ("" if none).  Owned by the library,
+ * valid until the next call on the same thread. */
+const char* pa_last_error(void);
+
+/* Library version string, e.g. "0.1.0". */
+const char* pa_version(void);
+
+/* ------------------------------------------------------------------------------------
+ * CPU block manager.
+ * [P1] sec. 4 "Allocation Lifecycle": a prompt of N tokens takes ceil(N / B) blocks from
+ * the free list; blocks whose reference count drops to zero return to the pool.
+ * [P2] sec. 3 "The Block Manager": the free list is consumed from its front and returned
+ * blocks are appended at its back.
+ * [P1] sec. 5 "Parallel Sampling" / "System Prompt Prefix Sharing": the prompt of K
+ * sequences is stored once, in blocks whose reference count is K.
+ * ------------------------------------------------------------------------------------ */
+
+/* Create a manager over num_blocks physical blocks of block_size tokens (any block_size
+ * >= 1).  free_order: host [num_blocks], a permutation of 0..num_blocks-1 giving the
+ * initial free-list order (NULL = ascending).  *out receives the handle. */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       pa_block_manager** out);
+
+/* Destroy a manager (NULL is ignored). */
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* Allocate block tables for num_seqs new sequences, in index order.
+ *   context_lens  host [num_seqs], each >= 0 tokens;
+ *   prefix_group  host [num_seqs] or NULL: group id in [0, num_groups) or -1 for none;
+ *   prefix_lens   host [num_groups] tokens: the group's first floor(len / B) blocks are
+ *                 shared by all its members (taken from the free list when the group is
+ *                 first met; reference count = number of members).  A member needs
+ *                 context_len >= its prefix length.  The prompt's remaining tokens, and
+ *                 everything after, go in private blocks;
+ *   block_tables  host out [num_seqs, max_blocks_per_seq] int32, row s = physical ids of
+ *                 sequence s's logical blocks, unused entries -1;
+ *   seq_handles   host out [num_seqs]: handles for pa_bm_free.
+ * All-or-nothing: on PA_ERR_NO_BLOCKS / PA_ERR_TABLE_OVERFLOW / PA_ERR_INVALID_ARG the
+ * manager is unchanged and the outputs are untouched. */
+pa_status pa_alloc_tables(pa_block_manager* bm, int32_t num_seqs, const int32_t* context_lens,
+                          const int32_t* prefix_group, const int32_t* prefix_lens,
+                          int32_t num_groups, int32_t max_blocks_per_seq,
+                          int32_t* block_tables, int32_t* seq_handles);
+
+/* Release sequences: each of their blocks loses one reference; blocks reaching zero are
+ * appended to the back of the free list in table order ([P1] sec. 4 "Completion").
+ * A handle that is not live (never issued, or already freed) gives PA_ERR_INVALID_ARG and
+ * nothing is released. */
+pa_status pa_bm_free(pa_block_manager* bm, int32_t n, const int32_t* seq_handles);
+
+/* Counters.  refcounts: host [num_blocks] or NULL; num_free, waste_slots: may be NULL.
+ * waste_slots = sum over live sequences of (blocks * B - context_len), the internal
+ * fragmentation that [P1] sec. 4 bounds by B - 1 slots per sequence. */
+pa_status pa_bm_stats(const pa_block_manager* bm, int32_t* refcounts, int32_t* num_free,
+                      int64_t* waste_slots);
+
+/* Copy the current free list (front first) into out[capacity]; *count = its length. */
+pa_status pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int32_t capacity,
+                          int32_t* count);
+
+/* ------------------------------------------------------------------------------------
+ * KV write: [P1] sec. 7 "Fused Reshape and Block Write" and sec. 4 "Decoding Step".
+ * Token t (sequence seq_ids[t], position positions[t]) is stored in block
+ * block_tables[seq][pos / B] at slot pos % B, for every KV head.
+ *   k_src, v_src      [num_tokens, num_kv_heads, head_dim] in src_dtype (PA_F16 / PA_BF16)
+ *   k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim] in cache_dtype
+ *   block_tables      [num_seqs, max_blocks_per_seq] int32; seq_ids, positions [num_tokens]
+ * cache_dtype == src_dtype: the source bits are copied unchanged.
+ * cache_dtype == PA_FP8_E4M3: byte = e4m3(float(src) * inv_scale), the product rounded to
+ * binary32 and then to E4M3 round-to-nearest-even, saturating at +-448 (NaN stays NaN);
+ * [P3] sec. 4: K/V stored in fp8 with per-tensor scales.
+ * A token whose sequence id is outside [0, num_seqs), whose position is negative or at or
+ * beyond max_blocks_per_seq * block_size, or whose table entry is outside [0, num_blocks),
+ * is skipped.  Two tokens naming the same slot race (last writer wins, unordered).
+ * Supported: head_dim in {64, 128}, block_size in {8, 16, 32}. */
+pa_status pa_write_kv(const void* k_src, const void* v_src, void* k_cache, void* v_cache,
+                      const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                      const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                      int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, pa_dtype src_dtype, pa_dtype cache_dtype,
+                      float k_inv_scale, float v_inv_scale, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Decode attention.
+ * [P1] sec. 3: for sequence s and query head h, with n = context_lens[s],
+ *   o = sum_{t<n} softmax_t(scale * q . k_t) v_t,
+ * where token t's key/value rows sit in block block_tables[s][t / B], slot t % B, of KV
+ * head h / (num_heads / num_kv_heads).  Slots at or beyond n are never read into the
+ * arithmetic (the partial-last-block rule of [P1] sec. 3); only table entries
+ * j < ceil(n / B) are read ([P2] sec. 2).  n = 0 gives a zero row.
+ * The kernel walks the table block by block with the online rescaling of [P1] sec. 7,
+ * one pass over K and V ([P3] sec. 3), accumulating in fp32.  Long contexts are cut into
+ * partitions of partition_size tokens whose partial (max, sum, output) triples are
+ * combined by a second, log-sum-exp merge kernel.
+ *   out           [num_seqs, num_heads, head_dim] in q_dtype (round to nearest even)
+ *   query         [num_seqs, num_heads, head_dim] in q_dtype
+ *   k/v_cache     [num_blocks, num_kv_heads, block_size, head_dim] in kv_dtype
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32;  context_lens [num_seqs] int32
+ *   max_context_len  host upper bound of context_lens (sizes the grid; larger values in
+ *                 context_lens are clamped to it and to max_blocks_per_seq * block_size)
+ *   k_scale, v_scale  dequantisation scales of an e4m3 cache (value = code * scale);
+ *                 ignored for fp16/bf16 caches
+ *   partition_size 0 = library choice, else a positive multiple of block_size
+ *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes
+ *                 (may be NULL when that size is 0)
+ * Supported: head_dim in {64, 128}; block_size in {8, 16, 32}; num_heads / num_kv_heads in
+ * {1, 2, 4, 8}; (q, kv) in {(f16, f16), (bf16, bf16), (f16, e4m3), (bf16, e4m3)}. */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                int32_t partition_size);
+
+/* The partition size pa_decode will use for these arguments (0 = no split) and the
+ * resulting number of partitions per sequence. */
+pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                         int32_t partition_size, int32_t* used_partition_size,
+                         int32_t* num_partitions);
+
+pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                    int32_t num_blocks, int32_t max_context_len, float scale,
+                    pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Footprint: [P1] sec. 1 "KV Cache Memory Footprint" — a token stores one key and one
+ * value vector per layer, so it costs 2 * num_layers * num_kv_heads * head_dim * e bytes
+ * (e = 2 for fp16/bf16, 1 for e4m3); with fp16 and num_kv_heads * head_dim = d_model this
+ * is the page's 4 * L * d_model.  Returns 0 for a bad dtype or negative size. */
+uint64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                               pa_dtype kv_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

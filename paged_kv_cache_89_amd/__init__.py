@@ -1,0 +1,247 @@
+"""Python binding of libpaged_attn, the gfx950 paged KV-cache decode library.
+
+Argument marshalling only: every computation runs in the HIP library
+(``libpaged_attn.so``, built in-tree by ``python -m paged_kv_cache_89_amd._build``).
+Tensors are torch tensors on the GPU (``data_ptr()`` is passed through); the
+stream is torch's current stream unless one is given.  If the library is not
+built, importing works but every call raises :class:`LibraryNotBuilt`; there is
+no fallback implementation.
+
+Cache layout: K and V are ``[num_blocks, num_kv_heads, block_size, head_dim]``;
+an e4m3 cache is a ``torch.uint8`` (or ``torch.float8_e4m3fn``) tensor.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "F16", "BF16", "FP8_E4M3", "PagedAttnError", "LibraryNotBuilt", "lib", "library_path",
+    "BlockManager", "write_kv", "decode", "decode_plan", "decode_workspace_size",
+    "kv_bytes_per_token", "version",
+]
+
+F16, BF16, FP8_E4M3 = 0, 1, 2
+_STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED",
+           -3: "PA_ERR_NO_BLOCKS", -4: "PA_ERR_TABLE_OVERFLOW", -5: "PA_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpaged_attn.so")
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises LibraryNotBuilt if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise LibraryNotBuilt(f"{library_path} is missing; build it with "
+                              "`python -m paged_kv_cache_89_amd._build`")
+    L = ctypes.CDLL(library_path)
+    c = ctypes
+    vp, i32, f32, sz = c.c_void_p, c.c_int32, c.c_float, c.c_size_t
+    L.pa_last_error.restype = c.c_char_p
+    L.pa_version.restype = c.c_char_p
+    L.pa_bm_create.argtypes = [i32, i32, vp, c.POINTER(vp)]
+    L.pa_bm_destroy.argtypes = [vp]
+    L.pa_bm_destroy.restype = None
+    L.pa_alloc_tables.argtypes = [vp, i32, vp, vp, vp, i32, i32, vp, vp]
+    L.pa_bm_free.argtypes = [vp, i32, vp]
+    L.pa_bm_stats.argtypes = [vp, vp, vp, vp]
+    L.pa_bm_free_list.argtypes = [vp, vp, i32, vp]
+    L.pa_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32,
+                              c.c_int, c.c_int, f32, f32, vp]
+    L.pa_decode_workspace_size.argtypes = [i32] * 7
+    L.pa_decode_workspace_size.restype = sz
+    L.pa_decode_plan.argtypes = [i32] * 7 + [vp, vp]
+    L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                            f32, c.c_int, c.c_int, f32, f32, i32, vp, sz, vp]
+    L.pa_kv_bytes_per_token.argtypes = [i32, i32, i32, c.c_int]
+    L.pa_kv_bytes_per_token.restype = c.c_uint64
+    for name in ("pa_bm_create", "pa_alloc_tables", "pa_bm_free", "pa_bm_stats",
+                 "pa_bm_free_list", "pa_write_kv", "pa_decode_plan", "pa_decode"):
+        getattr(L, name).restype = c.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise PagedAttnError(status, lib().pa_last_error().decode())
+
+
+def version() -> str:
+    return lib().pa_version().decode()
+
+
+def _np(a, dtype=np.int32):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ------------------------------------------------------------------ block manager
+class BlockManager:
+    """Host-side free list, block tables and reference counts (pa_bm_* / pa_alloc_tables)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        h = ctypes.c_void_p()
+        fo = None if free_order is None else _np(free_order)
+        _check(lib().pa_bm_create(self.num_blocks, self.block_size, _ptr(fo), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_tables(self, context_lens, max_blocks_per_seq: int, prefix_group=None,
+                     prefix_lens=None):
+        """Returns (block_tables int32 [S, MB] numpy, seq_handles int32 [S])."""
+        ctx = _np(context_lens)
+        S = ctx.size
+        pg = None if prefix_group is None else _np(prefix_group)
+        pl = None if prefix_lens is None else _np(prefix_lens)
+        tables = np.empty((S, int(max_blocks_per_seq)), np.int32)
+        handles = np.empty(S, np.int32)
+        _check(lib().pa_alloc_tables(self._h, S, _ptr(ctx), _ptr(pg), _ptr(pl),
+                                     0 if pl is None else pl.size, int(max_blocks_per_seq),
+                                     _ptr(tables), _ptr(handles)))
+        return tables, handles
+
+    def free(self, seq_handles):
+        h = _np(seq_handles)
+        _check(lib().pa_bm_free(self._h, h.size, _ptr(h)))
+
+    def stats(self):
+        """(refcounts int32 [NB], num_free, waste_slots)."""
+        ref = np.empty(self.num_blocks, np.int32)
+        nf = np.zeros(1, np.int32)
+        w = np.zeros(1, np.int64)
+        _check(lib().pa_bm_stats(self._h, _ptr(ref), _ptr(nf), _ptr(w)))
+        return ref, int(nf[0]), int(w[0])
+
+    def free_list(self) -> np.ndarray:
+        out = np.empty(self.num_blocks, np.int32)
+        cnt = np.zeros(1, np.int32)
+        _check(lib().pa_bm_free_list(self._h, _ptr(out), self.num_blocks, _ptr(cnt)))
+        return out[: cnt[0]].copy()
+
+
+# ------------------------------------------------------------------ device ops
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None)):
+        return FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def write_kv(k_src, v_src, k_cache, v_cache, block_tables, seq_ids, positions,
+             k_inv_scale: float = 1.0, v_inv_scale: float = 1.0, stream=None):
+    """pa_write_kv: store rows k_src/v_src [T, Hkv, D] into their cache slots."""
+    T, Hkv, D = k_src.shape
+    NB, Hkv2, B, D2 = k_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or v_cache.shape != k_cache.shape or v_src.shape != k_src.shape:
+        raise ValueError("write_kv: shape mismatch")
+    S, MB = block_tables.shape
+    _check(lib().pa_write_kv(_dev(k_src, "k_src"), _dev(v_src, "v_src"),
+                             _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                             _dev(block_tables, "block_tables"), S, MB,
+                             _dev(seq_ids, "seq_ids"), _dev(positions, "positions"), T, NB,
+                             Hkv, D, B, _dtype_code(k_src), _dtype_code(k_cache),
+                             float(k_inv_scale), float(v_inv_scale), _stream(stream)))
+
+
+def decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                partition_size=0):
+    """(partition size pa_decode will use (0 = no split), partitions per sequence)."""
+    p = np.zeros(1, np.int32)
+    n = np.zeros(1, np.int32)
+    _check(lib().pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                int(max_context_len), int(partition_size), _ptr(p), _ptr(n)))
+    return int(p[0]), int(n[0])
+
+
+def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                          max_context_len, partition_size=0) -> int:
+    return int(lib().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                              block_size, int(max_context_len),
+                                              int(partition_size)))
+
+
+def decode(query, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+           scale: float, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+           out=None, workspace=None, stream=None):
+    """pa_decode.  query [S, Hq, D]; returns out [S, Hq, D] (query dtype)."""
+    torch = _torch()
+    S, Hq, D = query.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("decode: shape mismatch")
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    need = decode_workspace_size(S, Hq, Hkv, D, B, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode(_dev(out, "out"), _dev(query, "query"), _dev(k_cache, "k_cache"),
+                           _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+                           _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B, MB, NB,
+                           int(max_context_len), float(scale), _dtype_code(query),
+                           _dtype_code(k_cache), float(k_scale), float(v_scale),
+                           int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, kv_dtype: int) -> int:
+    return int(lib().pa_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, kv_dtype))

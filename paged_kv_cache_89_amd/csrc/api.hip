@@ -1,0 +1,251 @@
+// C-ABI layer of libpaged_attn: argument checks, launch planning, error reporting.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "launch.h"
+#include "paged_attn.h"
+
+static thread_local std::string g_last_error;
+
+void pa_set_error(const std::string& msg) { g_last_error = msg; }
+
+namespace {
+
+using namespace pa;
+
+bool dtype_kind(pa_dtype d, int* kind) {
+  switch (d) {
+    case PA_F16: *kind = KIND_F16; return true;
+    case PA_BF16: *kind = KIND_BF16; return true;
+    case PA_FP8_E4M3: *kind = KIND_E4M3; return true;
+  }
+  return false;
+}
+
+pa_status fail(pa_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+pa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("PA_LOG");
+    return v && *v && *v != '0';
+  }();
+  return on;
+}
+
+struct Plan {
+  int32_t partition_size;  // 0 = whole context in one unit
+  int32_t num_parts;
+};
+
+// Library choice of the partition length.  A unit is one wavefront; short sequences run
+// unsplit, longer ones are cut into partitions so the grid holds many more, and more
+// uniform, units than the chip has wave slots (the length mix of a batch is ragged, and a
+// few long units would otherwise leave most CUs idle at the end of the launch).
+int32_t auto_partition(int32_t max_ctx) {
+  if (max_ctx <= 256) return 0;
+  if (max_ctx <= 4096) return 256;
+  return 512;
+}
+
+pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                    Plan* plan) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
+      max_context_len < 0 || partition_size < 0)
+    return fail(PA_ERR_INVALID_ARG, "decode plan: negative or zero size");
+  if (partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "decode plan: partition_size must be a multiple of block_size");
+  int32_t P = partition_size > 0 ? partition_size : auto_partition(max_context_len);
+  if (P > 0 && P % block_size != 0) P = ((P + block_size - 1) / block_size) * block_size;
+  if (P == 0 || P >= max_context_len) {
+    plan->partition_size = 0;
+    plan->num_parts = 1;
+  } else {
+    plan->partition_size = P;
+    plan->num_parts = (max_context_len + P - 1) / P;
+  }
+  return PA_OK;
+}
+
+size_t workspace_bytes(const Plan& p, int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
+  if (p.num_parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_heads * p.num_parts;
+  return rows * head_dim * sizeof(float) + rows * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+const char* pa_version(void) { return "0.1.0"; }
+
+uint64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                               pa_dtype kv_dtype) {
+  int kind;
+  if (!dtype_kind(kv_dtype, &kind) || num_layers < 0 || num_kv_heads < 0 || head_dim < 0) return 0;
+  const uint64_t e = kind == KIND_E4M3 ? 1 : 2;
+  // one key and one value vector of num_kv_heads * head_dim elements per layer
+  return 2ull * (uint64_t)num_layers * (uint64_t)num_kv_heads * (uint64_t)head_dim * e;
+}
+
+pa_status pa_write_kv(const void* k_src, const void* v_src, void* k_cache, void* v_cache,
+                      const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                      const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                      int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, pa_dtype src_dtype, pa_dtype cache_dtype,
+                      float k_inv_scale, float v_inv_scale, void* stream) {
+  g_last_error.clear();
+  int sk, ck;
+  if (!dtype_kind(src_dtype, &sk) || !dtype_kind(cache_dtype, &ck))
+    return fail(PA_ERR_INVALID_ARG, "pa_write_kv: unknown dtype");
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      num_kv_heads < 1 || head_dim < 1 || block_size < 1)
+    return fail(PA_ERR_INVALID_ARG, "pa_write_kv: bad size");
+  if (!write_supported(head_dim, block_size, sk, ck))
+    return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: unsupported head_dim/block_size/dtype pair");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_src || !v_src || !k_cache || !v_cache || !block_tables || !seq_ids || !positions)
+    return fail(PA_ERR_INVALID_ARG, "pa_write_kv: NULL pointer");
+  if (ck == KIND_E4M3 && !(std::isfinite(k_inv_scale) && std::isfinite(v_inv_scale)))
+    return fail(PA_ERR_INVALID_ARG, "pa_write_kv: non-finite inverse scale");
+  WriteArgs a;
+  a.k_src = k_src; a.v_src = v_src; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.tables = block_tables; a.seq_ids = seq_ids; a.positions = positions;
+  a.num_seqs = num_seqs; a.max_blocks = max_blocks_per_seq; a.num_tokens = num_tokens;
+  a.num_blocks = num_blocks; a.num_kv_heads = num_kv_heads;
+  a.k_inv_scale = k_inv_scale; a.v_inv_scale = v_inv_scale;
+  return hip_status(launch_write_kv(head_dim, block_size, sk, ck, a, (hipStream_t)stream),
+                    "pa_write_kv launch");
+}
+
+pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                         int32_t partition_size, int32_t* used_partition_size,
+                         int32_t* num_partitions) {
+  g_last_error.clear();
+  Plan p;
+  const pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                 max_context_len, partition_size, &p);
+  if (st != PA_OK) return st;
+  if (used_partition_size) *used_partition_size = p.partition_size;
+  if (num_partitions) *num_partitions = p.num_parts;
+  return PA_OK;
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                int32_t partition_size) {
+  Plan p;
+  if (make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                partition_size, &p) != PA_OK)
+    return 0;
+  return workspace_bytes(p, num_seqs, num_heads, head_dim);
+}
+
+pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                    int32_t num_blocks, int32_t max_context_len, float scale,
+                    pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes_given,
+                    void* stream) {
+  g_last_error.clear();
+  int qk, kk;
+  if (!dtype_kind(q_dtype, &qk) || !dtype_kind(kv_dtype, &kk))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype");
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
+      max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0 || partition_size < 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: bad size");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: num_heads must be a multiple of num_kv_heads");
+  if (partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: partition_size must be a multiple of block_size");
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: non-finite scale");
+  DecodeShape shape{head_dim, block_size, qk, kk, num_heads / num_kv_heads};
+  if (!decode_supported(shape))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: unsupported head_dim/block_size/group/dtype pair");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: NULL pointer");
+
+  // Tokens beyond the table's reach can never be addressed.
+  const int64_t reach = (int64_t)max_blocks_per_seq * block_size;
+  const int32_t max_ctx = (int32_t)(max_context_len < reach ? max_context_len : reach);
+  Plan plan;
+  pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
+                           partition_size, &plan);
+  if (st != PA_OK) return st;
+  const size_t need = workspace_bytes(plan, num_seqs, num_heads, head_dim);
+  if (need > 0 && (!workspace || workspace_bytes_given < need))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace needs " + std::to_string(need) +
+                                        " bytes, got " + std::to_string(workspace_bytes_given));
+
+  DecodeArgs a;
+  a.out = out; a.q = query; a.k = k_cache; a.v = v_cache;
+  a.tables = block_tables; a.ctx = context_lens;
+  a.part_acc = need ? (float*)workspace : nullptr;
+  a.part_ml = need ? (float*)workspace + (size_t)num_seqs * num_heads * plan.num_parts * head_dim
+                   : nullptr;
+  a.num_seqs = num_seqs; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks; a.max_ctx = max_ctx;
+  a.num_parts = plan.num_parts;
+  a.blocks_per_part = plan.num_parts > 1 ? plan.partition_size / block_size
+                                         : (int32_t)((reach + block_size - 1) / block_size);
+  const int64_t units = (int64_t)num_seqs * num_kv_heads * plan.num_parts;
+  if (units > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
+  a.num_units = (int32_t)units;
+  const bool f8 = kk == KIND_E4M3;
+  a.qk_scale = scale * kLog2e * (f8 ? k_scale : 1.0f);
+  a.v_scale = f8 ? v_scale : 1.0f;
+  if (log_enabled())
+    std::fprintf(stderr, "[paged_attn] decode S=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d P=%d parts=%d units=%lld\n",
+                 num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
+                 plan.partition_size, plan.num_parts, (long long)units);
+  st = hip_status(launch_decode(shape, a, (hipStream_t)stream), "pa_decode launch");
+  if (st != PA_OK || plan.num_parts <= 1) return st;
+  MergeArgs m;
+  m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
+  m.num_seqs = num_seqs; m.num_heads = num_heads; m.num_parts = plan.num_parts;
+  m.partition_size = plan.partition_size; m.max_ctx = max_ctx;
+  m.v_scale = a.v_scale;
+  return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream), "pa_decode merge launch");
+}
+
+}  // extern "C"
+
+namespace pa {
+
+hipError_t launch_decode_64(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_128(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+
+bool decode_supported(const DecodeShape& s) {
+  if (s.head_dim != 64 && s.head_dim != 128) return false;
+  if (s.block_size != 8 && s.block_size != 16 && s.block_size != 32) return false;
+  if (s.group != 1 && s.group != 2 && s.group != 4 && s.group != 8) return false;
+  if (s.q_kind == KIND_E4M3) return false;
+  return s.kv_kind == s.q_kind || s.kv_kind == KIND_E4M3;
+}
+
+hipError_t launch_decode(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream) {
+  if (s.head_dim == 128) return launch_decode_128(s, a, stream);
+  if (s.head_dim == 64) return launch_decode_64(s, a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,219 @@
+// CPU block manager: free list, block tables and reference counts.
+//
+// "PagedAttention: Mathematical Foundations, ..." sec. 4 (allocation lifecycle: a prompt
+// of N tokens takes ceil(N/B) physical blocks from the free list; a finished sequence
+// drops one reference on each of its blocks and blocks at zero go back to the pool) and
+// sec. 5 (parallel sampling / system-prompt sharing: the prompt's blocks are stored once
+// with reference count K).  "Pytorch implementation of paper ..." sec. 3 fixes the order:
+// blocks leave from the front of the free list and return at its back.
+//
+// The free list is a ring buffer of capacity num_blocks (it can never hold more), so both
+// ends are O(1) and the list keeps its exact order.
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "paged_attn.h"
+
+void pa_set_error(const std::string& msg);  // defined in api.hip
+
+struct pa_block_manager {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ring;     // free ids, ring[(head + k) % num_blocks], k < free_count
+  int64_t head = 0;
+  int64_t free_count = 0;
+  std::vector<int32_t> refs;     // references per physical block
+  struct Seq {
+    std::vector<int32_t> blocks; // logical block j -> physical id
+    int32_t context_len = 0;
+    bool live = false;
+  };
+  std::vector<Seq> seqs;         // indexed by handle
+
+  int32_t pop_front() {
+    const int32_t id = ring[head];
+    head = (head + 1) % num_blocks;
+    --free_count;
+    return id;
+  }
+  void push_back(int32_t id) {
+    ring[(head + free_count) % num_blocks] = id;
+    ++free_count;
+  }
+};
+
+static int32_t blocks_for(int64_t tokens, int32_t bs) { return (int32_t)((tokens + bs - 1) / bs); }
+
+extern "C" {
+
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       pa_block_manager** out) {
+  if (!out || num_blocks < 1 || block_size < 1) {
+    pa_set_error("pa_bm_create: need out != NULL, num_blocks >= 1, block_size >= 1");
+    return PA_ERR_INVALID_ARG;
+  }
+  std::vector<int32_t> ring(num_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t k = 0; k < num_blocks; ++k) {
+      const int32_t id = free_order[k];
+      if (id < 0 || id >= num_blocks || seen[id]) {
+        pa_set_error("pa_bm_create: free_order is not a permutation of 0..num_blocks-1");
+        return PA_ERR_INVALID_ARG;
+      }
+      seen[id] = 1;
+      ring[k] = id;
+    }
+  } else {
+    for (int32_t k = 0; k < num_blocks; ++k) ring[k] = k;
+  }
+  auto* bm = new pa_block_manager();
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->ring = std::move(ring);
+  bm->free_count = num_blocks;
+  bm->refs.assign(num_blocks, 0);
+  *out = bm;
+  return PA_OK;
+}
+
+void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
+
+pa_status pa_alloc_tables(pa_block_manager* bm, int32_t num_seqs, const int32_t* context_lens,
+                          const int32_t* prefix_group, const int32_t* prefix_lens,
+                          int32_t num_groups, int32_t max_blocks_per_seq,
+                          int32_t* block_tables, int32_t* seq_handles) {
+  if (!bm || num_seqs < 0 || max_blocks_per_seq < 1 || num_groups < 0 ||
+      (num_seqs > 0 && (!context_lens || !block_tables || !seq_handles)) ||
+      (prefix_group && num_groups > 0 && !prefix_lens)) {
+    pa_set_error("pa_alloc_tables: invalid arguments");
+    return PA_ERR_INVALID_ARG;
+  }
+  const int32_t B = bm->block_size;
+  // Validate everything and count the blocks before touching any state.
+  std::vector<int32_t> group_shared(num_groups, -1);  // shared block count once met
+  int64_t need = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t n = context_lens[s];
+    if (n < 0) {
+      pa_set_error("pa_alloc_tables: negative context length");
+      return PA_ERR_INVALID_ARG;
+    }
+    const int32_t nb = blocks_for(n, B);
+    if (nb > max_blocks_per_seq) {
+      pa_set_error("pa_alloc_tables: sequence " + std::to_string(s) + " needs " +
+                   std::to_string(nb) + " blocks > max_blocks_per_seq " +
+                   std::to_string(max_blocks_per_seq));
+      return PA_ERR_TABLE_OVERFLOW;
+    }
+    int32_t shared = 0;
+    const int32_t g = prefix_group ? prefix_group[s] : -1;
+    if (g >= 0) {
+      if (g >= num_groups || prefix_lens[g] < 0 || prefix_lens[g] > n) {
+        pa_set_error("pa_alloc_tables: bad prefix group or prefix longer than the sequence");
+        return PA_ERR_INVALID_ARG;
+      }
+      shared = prefix_lens[g] / B;
+      if (group_shared[g] < 0) {
+        group_shared[g] = shared;
+        need += shared;
+      }
+    } else if (g < -1) {
+      pa_set_error("pa_alloc_tables: prefix group ids must be >= -1");
+      return PA_ERR_INVALID_ARG;
+    }
+    need += nb - shared;
+  }
+  if (need > bm->free_count) {
+    pa_set_error("pa_alloc_tables: need " + std::to_string(need) + " blocks, " +
+                 std::to_string(bm->free_count) + " free");
+    return PA_ERR_NO_BLOCKS;
+  }
+  // Commit.
+  std::vector<std::vector<int32_t>> group_blocks(num_groups);
+  std::vector<char> group_done(num_groups, 0);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t n = context_lens[s];
+    const int32_t nb = blocks_for(n, B);
+    pa_block_manager::Seq seq;
+    seq.context_len = n;
+    seq.live = true;
+    seq.blocks.reserve(nb);
+    const int32_t g = prefix_group ? prefix_group[s] : -1;
+    if (g >= 0) {
+      if (!group_done[g]) {
+        const int32_t shared = prefix_lens[g] / B;
+        for (int32_t k = 0; k < shared; ++k) group_blocks[g].push_back(bm->pop_front());
+        group_done[g] = 1;
+      }
+      for (int32_t id : group_blocks[g]) seq.blocks.push_back(id);
+    }
+    while ((int32_t)seq.blocks.size() < nb) seq.blocks.push_back(bm->pop_front());
+    int32_t* row = block_tables + (size_t)s * max_blocks_per_seq;
+    for (int32_t j = 0; j < max_blocks_per_seq; ++j)
+      row[j] = j < nb ? seq.blocks[j] : -1;
+    for (int32_t id : seq.blocks) bm->refs[id] += 1;
+    seq_handles[s] = (int32_t)bm->seqs.size();
+    bm->seqs.push_back(std::move(seq));
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_free(pa_block_manager* bm, int32_t n, const int32_t* seq_handles) {
+  if (!bm || n < 0 || (n > 0 && !seq_handles)) {
+    pa_set_error("pa_bm_free: invalid arguments");
+    return PA_ERR_INVALID_ARG;
+  }
+  std::vector<char> hit(bm->seqs.size(), 0);
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t h = seq_handles[k];
+    if (h < 0 || h >= (int32_t)bm->seqs.size() || !bm->seqs[h].live || hit[h]) {
+      pa_set_error("pa_bm_free: handle " + std::to_string(h) + " is not a live sequence");
+      return PA_ERR_INVALID_ARG;
+    }
+    hit[h] = 1;
+  }
+  for (int32_t k = 0; k < n; ++k) {
+    auto& seq = bm->seqs[seq_handles[k]];
+    for (int32_t id : seq.blocks)
+      if (--bm->refs[id] == 0) bm->push_back(id);
+    seq.blocks.clear();
+    seq.blocks.shrink_to_fit();
+    seq.live = false;
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_stats(const pa_block_manager* bm, int32_t* refcounts, int32_t* num_free,
+                      int64_t* waste_slots) {
+  if (!bm) {
+    pa_set_error("pa_bm_stats: NULL manager");
+    return PA_ERR_INVALID_ARG;
+  }
+  if (refcounts)
+    for (int32_t b = 0; b < bm->num_blocks; ++b) refcounts[b] = bm->refs[b];
+  if (num_free) *num_free = (int32_t)bm->free_count;
+  if (waste_slots) {
+    int64_t w = 0;
+    for (const auto& seq : bm->seqs)
+      if (seq.live) w += (int64_t)seq.blocks.size() * bm->block_size - seq.context_len;
+    *waste_slots = w;
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int32_t capacity,
+                          int32_t* count) {
+  if (!bm || !count || (capacity > 0 && !out) || capacity < 0) {
+    pa_set_error("pa_bm_free_list: invalid arguments");
+    return PA_ERR_INVALID_ARG;
+  }
+  *count = (int32_t)bm->free_count;
+  const int64_t k_end = bm->free_count < capacity ? bm->free_count : capacity;
+  for (int64_t k = 0; k < k_end; ++k) out[k] = bm->ring[(bm->head + k) % bm->num_blocks];
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,380 @@
+// Paged decode attention for gfx950: one wavefront per work unit (sequence, KV head,
+// context partition), single pass over K and V with online softmax.
+//
+// What is computed ([P1] = "PagedAttention: Mathematical Foundations, Virtual Memory Block
+// Allocation, and Zero-Waste KV Cache Serving"):
+//   sec. 3, eq. for a_ij / o_i and the block-wise forms S_ij, A_ij: the output is the
+//   softmax-weighted sum of the value rows over the sequence's first n tokens, scored by
+//   scale * q.k; the last block may be partial and its empty slots do not count;
+//   sec. 7 pseudocode: blocks are visited through the block table one at a time, the
+//   running maximum / denominator / output are rescaled by exp(old max - new max).
+// The partition split and its merge are this library's addition (the same rescaling
+// applied across partitions); see merge.hip.
+//
+// How it maps to CDNA4:
+//   * a (block, KV head) tile is B x D contiguous elements (cache layout
+//     [NB][Hkv][B][D]); one wave load instruction covers 1 KiB (16 B per lane, or 512 B at
+//     8 B per lane for tiles smaller than 1 KiB) of the tile, so every load is a fully
+//     coalesced run of consecutive bytes;
+//   * with that mapping LPT = D / (elements per lane) consecutive lanes hold one token row
+//     and a load covers TPL = 64 / LPT token rows; the q.k partial sums of a token are
+//     combined with DPP quad-permute / mirror moves inside the lane group, never through
+//     LDS;
+//   * each lane group (one "row" of the wave) keeps its own running max, denominator and
+//     output slice for the tokens it holds, so the per-block softmax update needs no
+//     cross-group traffic at all; the TPL group states are merged once per unit with
+//     the same rescaling rule;
+//   * the lane holds exactly the K/V elements its arithmetic needs, so tiles go straight
+//     from HBM into registers (no LDS round trip); the next block's K and V loads are
+//     issued before the current block is consumed (register double buffering), and a
+//     64-entry slice of the block table sits in one VGPR, read with v_readlane into
+//     scalar registers so the address of the next tile never waits on memory;
+//   * GQA (G query heads per KV head) reuses each loaded tile for all G heads;
+//   * e4m3 tiles are decoded in registers by the hardware fp8 converter; k_scale is
+//     folded into the logit scale and v_scale into the epilogue.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace pa {
+
+template <int D, int BS, int KVK>
+struct TileGeometry {
+  static constexpr int E = (KVK == KIND_E4M3) ? 1 : 2;   // bytes per element
+  static constexpr int TILE = BS * D * E;                // bytes of one (block, KV head) tile
+  static constexpr int LB = TILE >= 1024 ? 16 : 8;       // bytes per lane per load
+  static constexpr int W = LB / 4;                       // dwords per lane per load
+  static constexpr int EPL = LB / E;                     // elements per lane per load
+  static constexpr int LPT = D / EPL;                    // lanes sharing a token row
+  static constexpr int TPL = 64 / LPT;                   // token rows per load
+  static constexpr int NLD = BS / TPL;                   // loads per tile
+  static constexpr int SPAN = 64 * LB;                   // bytes per wave load
+  static_assert(NLD * SPAN == TILE, "tile must be covered by whole wave loads");
+  static_assert(LPT >= 2 && LPT <= 16, "token row must fit in a 16-lane DPP row");
+};
+
+template <int W> struct LoadVec;
+template <> struct LoadVec<4> { using T = u32x4; };
+template <> struct LoadVec<2> { using T = u32x2; };
+
+// Block-table slice kept in a VGPR: lane k holds entry base + k.  Entries outside
+// [0, num_blocks) are replaced by block 0 so a malformed table can never fault.
+struct TableWalk {
+  const int32_t* row;
+  int j1, nb, base, cur, nxt;
+
+  __device__ __forceinline__ void init(const int32_t* r, int j0, int j1_, int nb_, int lane) {
+    row = r; j1 = j1_; nb = nb_; base = j0;
+    cur = (j0 + lane < j1) ? row[j0 + lane] : 0;
+    nxt = (j0 + 64 + lane < j1) ? row[j0 + 64 + lane] : 0;
+  }
+  // j is wave-uniform and never decreases between calls.
+  __device__ __forceinline__ int get(int j, int lane) {
+    if (j - base >= 64) {
+      base += 64;
+      cur = nxt;
+      nxt = (base + 64 + lane < j1) ? row[base + 64 + lane] : 0;
+    }
+    const int p = __builtin_amdgcn_readlane(cur, j - base);
+    return ((unsigned)p < (unsigned)nb) ? p : 0;
+  }
+};
+
+template <int D, int BS, int QK, int KVK, int G>
+__global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeArgs a) {
+  using Geo = TileGeometry<D, BS, KVK>;
+  using LT = typename LoadVec<Geo::W>::T;
+  constexpr int W = Geo::W, EPL = Geo::EPL, LPT = Geo::LPT, TPL = Geo::TPL, NLD = Geo::NLD;
+  constexpr bool F8 = (KVK == KIND_E4M3);
+  static_assert(F8 || QK == KVK, "fp16/bf16 caches are read with a query of the same type");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * 4 + wave;
+  if (unit >= a.num_units) return;
+  const int kvh = unit % a.num_kv_heads;
+  const int rest = unit / a.num_kv_heads;
+  const int part = rest % a.num_parts;
+  const int s = rest / a.num_parts;
+  const int h0 = kvh * G;
+
+  int n = a.ctx[s];
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  const int nblk = (n + BS - 1) / BS;
+  const int j0 = part * a.blocks_per_part;
+  const int j1 = min(nblk, j0 + a.blocks_per_part);
+  const int r = lane / LPT;   // token row of this lane inside a load
+  const int c = lane % LPT;   // element slice [c*EPL, c*EPL + EPL) of the head dimension
+
+  if (j0 >= j1) {
+    // Nothing to read.  With a single partition this is the n == 0 row: write zeros.
+    if (a.num_parts == 1 && lane < LPT) {
+      for (int g = 0; g < G; ++g) {
+        uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + h0 + g) * D + c * EPL;
+        for (int e = 0; e < EPL; ++e) o[e] = 0;
+      }
+    }
+    return;
+  }
+
+  // ---- query slice, kept packed (fp16/bf16 caches) or widened to fp32 (e4m3 caches)
+  uint32_t qw[G][EPL / 2];
+  float qf[F8 ? G : 1][F8 ? EPL : 1];
+  for (int g = 0; g < G; ++g) {
+    const u32x4* qp = (const u32x4*)((const uint16_t*)a.q +
+                                     ((size_t)s * a.num_heads + h0 + g) * D + c * EPL);
+#pragma unroll
+    for (int k = 0; k < EPL / 8; ++k) {
+      u32x4 t = qp[k];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qw[g][4 * k + w] = t[w];
+    }
+    if constexpr (F8) {
+#pragma unroll
+      for (int w = 0; w < EPL / 2; ++w) {
+        if constexpr (QK == KIND_BF16) {
+          qf[g][2 * w] = bf16_lo(qw[g][w]);
+          qf[g][2 * w + 1] = bf16_hi(qw[g][w]);
+        } else {
+          qf[g][2 * w] = f16_lo(qw[g][w]);
+          qf[g][2 * w + 1] = f16_hi(qw[g][w]);
+        }
+      }
+    }
+  }
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+  }
+
+  const size_t blk_stride = (size_t)a.num_kv_heads * Geo::TILE;
+  const char* kbase = (const char*)a.k + (size_t)kvh * Geo::TILE;
+  const char* vbase = (const char*)a.v + (size_t)kvh * Geo::TILE;
+  const uint32_t loff = (uint32_t)lane * Geo::LB;
+  const float qk_scale = a.qk_scale;
+
+  auto issue = [&](int phys, LT (&kr)[NLD], LT (&vr)[NLD]) {
+    const char* kp = kbase + (size_t)phys * blk_stride;
+    const char* vp = vbase + (size_t)phys * blk_stride;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) kr[i] = *(const LT*)(kp + loff + i * Geo::SPAN);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) vr[i] = *(const LT*)(vp + loff + i * Geo::SPAN);
+  };
+
+  // Fold one block into the running state.  MASK: the block holds slots >= n.
+  auto consume = [&](auto mask_tag, int j, const LT (&kr)[NLD], const LT (&vr)[NLD]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float sc[G][NLD];
+    // q.k partial sums over this lane's slice
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (F8) {
+        float kf[EPL];
+#pragma unroll
+        for (int w = 0; w < W; ++w) e4m3x4_to_f32(kr[i][w], &kf[4 * w]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; e += 2) {
+            d0 = fmaf(qf[g][e], kf[e], d0);
+            d1 = fmaf(qf[g][e + 1], kf[e + 1], d1);
+          }
+          sc[g][i] = d0 + d1;
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = 0.f;
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            if constexpr (KVK == KIND_F16)
+              d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw[g][w]),
+                                         __builtin_bit_cast(f16x2, (uint32_t)kr[i][w]), d, false);
+            else
+              d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[g][w]),
+                                                  __builtin_bit_cast(bf16x2, (uint32_t)kr[i][w]),
+                                                  d, false);
+          }
+          sc[g][i] = d;
+        }
+      }
+    }
+    // finish the dot products inside each token's lane group; scale into log2 units
+    bool valid[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      valid[i] = !MASK || (j * BS + i * TPL + r < n);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float z = group_sum<LPT>(sc[g][i]) * qk_scale;
+        sc[g][i] = valid[i] ? z : -INFINITY;
+      }
+    }
+    // online softmax update per head
+    float p[G][NLD];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float bm = sc[g][0];
+#pragma unroll
+      for (int i = 1; i < NLD; ++i) bm = fmaxf(bm, sc[g][i]);
+      const float mn = fmaxf(m[g], bm);
+      const float ms = (mn == -INFINITY) ? 0.f : mn;  // row has seen no valid token yet
+      const float rs = fast_exp2(m[g] - ms);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        p[g][i] = fast_exp2(sc[g][i] - ms);
+        ps += p[g][i];
+      }
+      l[g] = l[g] * rs + ps;
+      m[g] = mn;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= rs;
+    }
+    // weighted value rows
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      float vf[EPL];
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const uint32_t x = vr[i][w];
+        if constexpr (F8) {
+          e4m3x4_to_f32(x, &vf[4 * w]);
+        } else if constexpr (KVK == KIND_BF16) {
+          vf[2 * w] = bf16_lo(x);
+          vf[2 * w + 1] = bf16_hi(x);
+        } else {
+          vf[2 * w] = f16_lo(x);
+          vf[2 * w + 1] = f16_hi(x);
+        }
+      }
+      if constexpr (MASK) {
+        // never let an unused slot's bytes (possibly NaN) reach the FMA: 0 * NaN = NaN
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = valid[i] ? vf[e] : 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g][i], vf[e], acc[g][e]);
+    }
+  };
+
+  auto process = [&](int j, const LT (&kr)[NLD], const LT (&vr)[NLD]) {
+    if ((j + 1) * BS <= n) consume(std::false_type{}, j, kr, vr);
+    else consume(std::true_type{}, j, kr, vr);
+  };
+
+  TableWalk tw;
+  tw.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
+  LT ka[NLD], va[NLD], kb[NLD], vb[NLD];
+  issue(tw.get(j0, lane), ka, va);
+  int j = j0;
+  while (true) {
+    if (j + 1 < j1) issue(tw.get(j + 1, lane), kb, vb);
+    process(j, ka, va);
+    if (++j >= j1) break;
+    if (j + 1 < j1) issue(tw.get(j + 1, lane), ka, va);
+    process(j, kb, vb);
+    if (++j >= j1) break;
+  }
+
+  // ---- merge the TPL lane-group states of the wave (same rescaling rule)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float M = m[g];
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float f = (m[g] == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
+    float L = l[g] * f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      L += __shfl_xor(L, off);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+    }
+    const int h = h0 + g;
+    if (a.num_parts == 1) {
+      if (lane < LPT) {
+        uint16_t ob[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float o = acc[g][e] / L;
+          if constexpr (F8) o = o * a.v_scale;
+          ob[e] = f32_to_store<QK>(o);
+        }
+        u32x4* op = (u32x4*)((uint16_t*)a.out + ((size_t)s * a.num_heads + h) * D + c * EPL);
+#pragma unroll
+        for (int k = 0; k < EPL / 8; ++k) {
+          u32x4 t;
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            t[w] = (uint32_t)ob[8 * k + 2 * w] | ((uint32_t)ob[8 * k + 2 * w + 1] << 16);
+          op[k] = t;
+        }
+      }
+    } else {
+      const size_t pi = ((size_t)s * a.num_heads + h) * a.num_parts + part;
+      if (lane < LPT) {
+        float* pa_ = a.part_acc + pi * D + c * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+          float4 t = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
+          *(float4*)(pa_ + e) = t;
+        }
+      }
+      if (lane == 0) {
+        a.part_ml[pi * 2] = M;
+        a.part_ml[pi * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+template <int D, int BS, int QK, int KVK, int G>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid((a.num_units + 3) / 4);
+  hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Instantiate every (block size, dtype pair, group) for one head_dim.
+template <int D>
+hipError_t launch_decode_d(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream) {
+#define PA_G(BS, QK, KVK)                                                  \
+  switch (s.group) {                                                       \
+    case 1: return launch_decode_t<D, BS, QK, KVK, 1>(a, stream);          \
+    case 2: return launch_decode_t<D, BS, QK, KVK, 2>(a, stream);          \
+    case 4: return launch_decode_t<D, BS, QK, KVK, 4>(a, stream);          \
+    case 8: return launch_decode_t<D, BS, QK, KVK, 8>(a, stream);          \
+    default: return hipErrorInvalidValue;                                  \
+  }
+#define PA_DT(BS)                                                                     \
+  if (s.q_kind == KIND_F16 && s.kv_kind == KIND_F16) { PA_G(BS, KIND_F16, KIND_F16) } \
+  if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_BF16) { PA_G(BS, KIND_BF16, KIND_BF16) } \
+  if (s.q_kind == KIND_F16 && s.kv_kind == KIND_E4M3) { PA_G(BS, KIND_F16, KIND_E4M3) } \
+  if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_E4M3) { PA_G(BS, KIND_BF16, KIND_E4M3) } \
+  return hipErrorInvalidValue;
+  switch (s.block_size) {
+    case 8: { PA_DT(8) }
+    case 16: { PA_DT(16) }
+    case 32: { PA_DT(32) }
+    default: return hipErrorInvalidValue;
+  }
+#undef PA_DT
+#undef PA_G
+}
+
+}  // namespace pa

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the gfx950 kernels of libpaged_attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ---- DPP cross-lane moves inside a 16-lane row -------------------------------------
+// Control words of the GFX9 DPP encoding.
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over groups of N consecutive lanes (N in {2,4,8,16}); every lane of a group gets
+// the group's total.  xor-1 and xor-2 are quad permutes; the 8- and 16-lane steps use
+// the half-row and row mirrors, which pair lane i with its reflection, i.e. the other
+// half of the group, after the smaller groups have been summed.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group size");
+  x += dpp_mov<DPP_QUAD_XOR1>(x);
+  if constexpr (N >= 4) x += dpp_mov<DPP_QUAD_XOR2>(x);
+  if constexpr (N >= 8) x += dpp_mov<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp_mov<DPP_ROW_MIRROR>(x);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- conversions ---------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[1];
+}
+
+// binary32 -> bfloat16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32 under the default round-to-nearest-even mode
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <int K>
+__device__ __forceinline__ uint16_t f32_to_store(float f) {
+  if constexpr (K == KIND_BF16) return f32_to_bf16_rne(f);
+  else return f32_to_f16_rne(f);
+}
+
+// Four e4m3 codes of a dword -> four floats (OCP E4M3 decode by the gfx950 converter).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* o) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
+}
+
+// binary32 -> OCP E4M3 code, round to nearest even, saturating at +-448, NaN -> NaN.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |x| >= 448 (and inf): largest finite
+  if (a >= 0x3C800000u) {                             // |x| >= 2^-6: normal E4M3 range
+    // keep 3 of the 23 fraction bits, ties to even; a carry bumps the exponent
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+    return sign | (r - (120u << 3));                  // rebias exponent 127 -> 7
+  }
+  // subnormal range: multiples of 2^-9; 8 * 2^-9 is the smallest normal (code 0x08)
+  const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
+  return sign | (uint32_t)m;
+}
+
+}  // namespace pa

@@ -1,0 +1,65 @@
+// Internal interface between the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Storage kinds used as template parameters.
+enum Kind : int { KIND_F16 = 0, KIND_BF16 = 1, KIND_E4M3 = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Decode over work units (sequence, KV head, partition).  A unit walks blocks
+// [part * blocks_per_part, min(ceil(n / B), (part + 1) * blocks_per_part)) of its
+// sequence for the num_heads / num_kv_heads query heads that share the KV head.
+struct DecodeArgs {
+  void* out;                 // [S, Hq, D] q dtype (written when num_parts == 1)
+  const void* q;             // [S, Hq, D]
+  const void* k;             // [NB, Hkv, B, D]
+  const void* v;
+  const int32_t* tables;     // [S, MB]
+  const int32_t* ctx;        // [S]
+  float* part_acc;           // [S, Hq, num_parts, D]   (num_parts > 1)
+  float* part_ml;            // [S, Hq, num_parts, 2]   running max (log2 units) and sum
+  int32_t num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks, max_ctx;
+  int32_t num_parts, blocks_per_part, num_units;
+  float qk_scale;            // scale * log2(e) * k_scale
+  float v_scale;
+};
+
+struct DecodeShape {
+  int head_dim, block_size, q_kind, kv_kind, group;
+};
+
+bool decode_supported(const DecodeShape& s);
+hipError_t launch_decode(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+
+struct MergeArgs {
+  void* out;
+  const float* part_acc;
+  const float* part_ml;
+  const int32_t* ctx;
+  int32_t num_seqs, num_heads, num_parts, partition_size, max_ctx;
+  float v_scale;
+};
+hipError_t launch_merge(int head_dim, int q_kind, const MergeArgs& a, hipStream_t stream);
+
+struct WriteArgs {
+  const void* k_src;
+  const void* v_src;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* tables;
+  const int32_t* seq_ids;
+  const int32_t* positions;
+  int32_t num_seqs, max_blocks, num_tokens, num_blocks, num_kv_heads;
+  float k_inv_scale, v_inv_scale;
+};
+bool write_supported(int head_dim, int block_size, int src_kind, int cache_kind);
+hipError_t launch_write_kv(int head_dim, int block_size, int src_kind, int cache_kind,
+                           const WriteArgs& a, hipStream_t stream);
+
+}  // namespace pa

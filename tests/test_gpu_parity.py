@@ -1,0 +1,283 @@
+"""GPU parity of libpaged_attn against the CPU oracle (needs an MI355X).
+
+Every case builds its inputs from a seeded generator, runs the HIP path through
+the C ABI (via the thin Python binding) and compares with the oracle:
+  * block tables and the KV write scatter: bit-exact;
+  * fp16/bf16 KV decode: max |gpu - oracle| <= 2e-3 and per-row
+    ||gpu - oracle||_inf / ||oracle||_inf <= 1e-2;
+  * e4m3 KV decode: max |gpu - oracle| <= 2e-2 against an oracle that dequantises
+    the same bytes with the same per-tensor scale.
+The oracle output is fp64 and unrounded; every unused cache slot and free block is
+NaN-poisoned, so a read past a sequence's end shows up as a NaN.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import paged_kv_cache_89_amd as pa
+from helpers import (DT, compare, dev_i32, oracle_caches, oracle_decode, oracle_tables, to_bits,
+                     to_dev, tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.lib()  # fail loudly when the library is not built
+    yield
+    torch.cuda.synchronize()
+
+
+def _gpu_decode(case, tables, k, v, partition_size=None, max_ctx=None):
+    sp = case.spec
+    q = to_dev(case.q, sp.q_dtype)
+    kd, vd = to_dev(k, sp.kv_dtype), to_dev(v, sp.kv_dtype)
+    P = sp.partition_size if partition_size is None else partition_size
+    mc = int(case.context_lens.max()) if max_ctx is None else max_ctx
+    out = pa.decode(q, kd, vd, dev_i32(tables), dev_i32(case.context_lens), mc, sp.scale,
+                    case.k_scale, case.v_scale, partition_size=P)
+    torch.cuda.synchronize()
+    return out
+
+
+def _f64(out):
+    return out.double().cpu().numpy()
+
+
+# ------------------------------------------------------------------ KV write scatter
+@pytest.mark.parametrize("name", list(workloads.SMALL))
+def test_write_kv_bit_exact(name):
+    case = workloads.generate(workloads.SMALL[name], 8900 + 20)
+    sp = case.spec
+    tables, _, _ = oracle_tables(case)
+    k_ref, v_ref = oracle_caches(case, tables)
+    kd = to_dev(workloads.empty_cache(sp), sp.kv_dtype)
+    vd = to_dev(workloads.empty_cache(sp), sp.kv_dtype)
+    pa.write_kv(to_dev(case.k_src, sp.src_dtype), to_dev(case.v_src, sp.src_dtype), kd, vd,
+                dev_i32(tables), dev_i32(case.seq_ids), dev_i32(case.positions),
+                case.k_inv_scale, case.v_inv_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kd), k_ref)
+    assert np.array_equal(to_bits(vd), v_ref)
+
+
+def test_write_kv_e4m3_every_code_path():
+    """Quantise values across the whole e4m3 range (subnormals, ties, saturation) and
+    compare every byte with the oracle's encoder."""
+    rng = np.random.default_rng(4)
+    sp = workloads.Spec("q", 1, 2, 2, 128, 16, 64, 64, 8, 4, "f16", "e4m3", 0.1)
+    T = 64
+    mags = np.concatenate([rng.uniform(0, 2 ** -6, T * 64), rng.uniform(2 ** -6, 600, T * 64),
+                           rng.standard_normal(T * 128) * 100])
+    x = (mags[: T * 2 * 128] * np.where(rng.random(T * 2 * 128) < 0.5, -1, 1)).astype(np.float32)
+    for src_dtype, qd in (("f16", "f16"), ("bf16", "bf16")):
+        src = workloads._round_bits(x.reshape(T, 2, 128), src_dtype)
+        case = workloads.Case(sp.replace(q_dtype=qd), np.array([T], np.int32),
+                              np.arange(8, dtype=np.int32), None, None,
+                              np.zeros((1, 2, 128), np.uint16), np.zeros(T, np.int32),
+                              np.arange(T, dtype=np.int32), src, src,
+                              np.arange(T, dtype=np.int32)[None], 1.0, 1.0, 0.75, 1.0)
+        tables, _, _ = oracle_tables(case)
+        k_ref, v_ref = oracle_caches(case, tables)
+        kd = to_dev(workloads.empty_cache(sp), "e4m3")
+        vd = to_dev(workloads.empty_cache(sp), "e4m3")
+        pa.write_kv(to_dev(src, src_dtype), to_dev(src, src_dtype), kd, vd, dev_i32(tables),
+                    dev_i32(case.seq_ids), dev_i32(case.positions), 0.75, 1.0)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(kd), k_ref) and np.array_equal(to_bits(vd), v_ref)
+
+
+def test_write_kv_skips_bad_rows():
+    """Tokens whose sequence, position or table entry is out of range are skipped."""
+    sp = workloads.Spec("w", 2, 4, 4, 64, 8, 8, 8, 6, 2, "f16", "f16", 0.1)
+    tables = np.array([[0, -1], [1, 99]], np.int32)
+    seq_ids = np.array([0, 0, 1, 5, -1, 1], np.int32)
+    pos = np.array([3, 9, 2, 0, 0, 12], np.int32)  # row 1: entry -1; row 5: entry 99
+    src = workloads._round_bits(np.random.default_rng(0).standard_normal((6, 4, 64),
+                                                                          dtype=np.float32), "f16")
+    kd = to_dev(workloads.empty_cache(sp), "f16")
+    vd = to_dev(workloads.empty_cache(sp), "f16")
+    pa.write_kv(to_dev(src, "f16"), to_dev(src, "f16"), kd, vd, dev_i32(tables),
+                dev_i32(seq_ids), dev_i32(pos))
+    torch.cuda.synchronize()
+    k = to_bits(kd)
+    expect = workloads.empty_cache(sp)
+    expect[0, :, 3, :] = src[0]
+    expect[1, :, 2, :] = src[2]
+    assert np.array_equal(k, expect)
+
+
+# ------------------------------------------------------------------ decode parity
+@pytest.mark.parametrize("name", list(workloads.SMALL))
+def test_decode_matches_oracle(name):
+    case = workloads.generate(workloads.SMALL[name], 8900 + 21)
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    ref = oracle_decode(case, tables, k, v)
+    out = _gpu_decode(case, tables, k, v)
+    atol, rrel = tolerance(case.spec)
+    compare(_f64(out), ref, atol, rrel, case.spec.q_dtype)
+
+
+@pytest.mark.parametrize("name", list(workloads.SMALL))
+def test_end_to_end_block_manager_write_decode(name):
+    """Tables from the library's block manager, cache filled by pa_write_kv, then
+    pa_decode: the whole path against the oracle's own tables/scatter/decode."""
+    case = workloads.generate(workloads.SMALL[name], 8900 + 22)
+    sp = case.spec
+    t_or, _, _ = oracle_tables(case)
+    k_ref, v_ref = oracle_caches(case, t_or)
+    ref = oracle_decode(case, t_or, k_ref, v_ref)
+    bm = pa.BlockManager(sp.num_blocks, sp.block_size, case.free_order)
+    tables, _ = bm.alloc_tables(case.context_lens, sp.max_blocks, case.prefix_group,
+                                case.prefix_lens)
+    assert np.array_equal(tables, t_or)
+    kd = to_dev(workloads.empty_cache(sp), sp.kv_dtype)
+    vd = to_dev(workloads.empty_cache(sp), sp.kv_dtype)
+    td = dev_i32(tables)
+    pa.write_kv(to_dev(case.k_src, sp.src_dtype), to_dev(case.v_src, sp.src_dtype), kd, vd, td,
+                dev_i32(case.seq_ids), dev_i32(case.positions), case.k_inv_scale,
+                case.v_inv_scale)
+    out = pa.decode(to_dev(case.q, sp.q_dtype), kd, vd, td, dev_i32(case.context_lens),
+                    int(case.context_lens.max()), sp.scale, case.k_scale, case.v_scale,
+                    partition_size=sp.partition_size)
+    torch.cuda.synchronize()
+    atol, rrel = tolerance(sp)
+    compare(_f64(out), ref, atol, rrel, case.spec.q_dtype)
+
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"),
+                                ("f16", "e4m3")])
+def test_decode_ragged_lengths_all_variants(B, d, dt):
+    """Every compiled (head_dim, block size, dtype) variant on lengths around block and
+    partition edges, including 0 and 1, with GQA groups 1 and 4."""
+    qd, kvd = dt
+    lens = [0, 1, B - 1, B, B + 1, 2 * B + 3, 97, 300, 513]
+    for G in (1, 4):
+        sp = workloads.Spec("rag", len(lens), 4 * G, 4, d, B, 1, 1,
+                            sum(math.ceil(n / B) for n in lens) + 7,
+                            math.ceil(max(lens) / B) + 2, qd, kvd, 1 / math.sqrt(d))
+        case = workloads.generate(sp, 1000 + B + d + G, context_lens=lens)
+        tables, _, _ = oracle_tables(case)
+        k, v = oracle_caches(case, tables)
+        ref = oracle_decode(case, tables, k, v)
+        atol, rrel = tolerance(sp)
+        for P in (0, B, 4 * B):
+            out = _f64(_gpu_decode(case, tables, k, v, partition_size=P))
+            assert (out[0] == 0).all(), "n = 0 must give a zero row"
+            compare(out, ref, atol, rrel, qd)
+
+
+def test_single_token_returns_v1_bit_exact():
+    for qd, kvd in (("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3")):
+        sp = workloads.Spec("n1", 6, 8, 2, 128, 16, 1, 1, 12, 2, qd, kvd, 0.0883883)
+        case = workloads.generate(sp, 31)
+        tables, _, _ = oracle_tables(case)
+        k, v = oracle_caches(case, tables)
+        out = to_bits(_gpu_decode(case, tables, k, v))
+        ref = oracle.round_to(oracle_decode(case, tables, k, v), DT[qd])
+        assert np.array_equal(out, ref), (qd, kvd)
+
+
+def test_e4m3_decoder_matches_ocp_definition():
+    """n = 1 with v_scale = 1 returns the decoded value of every e4m3 code (all of them
+    are exact in bf16): pins the in-register fp8 decode to the OCP E4M3 format."""
+    sp = workloads.Spec("codes", 2, 1, 1, 128, 16, 1, 1, 2, 1, "bf16", "e4m3", 0.1)
+    case = workloads.generate(sp, 3)
+    codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    k = np.zeros((2, 1, 16, 128), np.uint8)
+    v = np.zeros((2, 1, 16, 128), np.uint8)
+    v[0, 0, 0] = codes[0]
+    v[1, 0, 0] = codes[1]
+    tables = np.array([[0], [1]], np.int32)
+    case.v_scale = 1.0
+    out = _f64(_gpu_decode(case, tables, k, v))
+    ref = oracle.e4m3_to_f64(codes)
+    nan = np.isnan(ref)
+    assert (np.isnan(out[:, 0]) == nan).all() and (out[:, 0][~nan] == ref[~nan]).all()
+
+
+def test_physical_permutation_bit_identical():
+    case = workloads.generate(workloads.SMALL["opt13b_layer"], 8900 + 23)
+    sp = case.spec
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    out1 = to_bits(_gpu_decode(case, tables, k, v))
+    perm = np.random.default_rng(5).permutation(sp.num_blocks).astype(np.int32)
+    k2 = np.empty_like(k); k2[perm] = k
+    v2 = np.empty_like(v); v2[perm] = v
+    t2 = np.where(tables >= 0, perm[np.maximum(tables, 0)], -1).astype(np.int32)
+    out2 = to_bits(_gpu_decode(case, t2, k2, v2))
+    assert np.array_equal(out1, out2)
+
+
+def test_partition_size_invariance_and_determinism():
+    case = workloads.generate(workloads.SMALL["long_split"], 8900 + 24)
+    sp = case.spec
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    ref = oracle_decode(case, tables, k, v)
+    outs = {}
+    for P in (0, 32, 256, 512, 4096):
+        outs[P] = _f64(_gpu_decode(case, tables, k, v, partition_size=P))
+        compare(outs[P], ref, 2e-3, 1e-2, sp.q_dtype)
+    again = _f64(_gpu_decode(case, tables, k, v, partition_size=512))
+    assert np.array_equal(again, outs[512])
+
+
+def test_max_context_len_clamps_lengths():
+    """Lengths above max_context_len are treated as max_context_len."""
+    case = workloads.generate(workloads.SMALL["tiny_mha"], 8900 + 25)
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    cap = int(np.sort(case.context_lens)[1])
+    clipped = workloads.Case(**{**case.__dict__, "context_lens": np.minimum(case.context_lens, cap)})
+    ref = oracle_decode(clipped, tables, k, v)
+    out = _f64(_gpu_decode(case, tables, k, v, max_ctx=cap))
+    compare(out, ref, 2e-3, 1e-2, "f16")
+
+
+# ------------------------------------------------------------------ full-size workloads
+FULL_SAMPLE_ROWS = 64
+
+
+@pytest.mark.parametrize("name", list(workloads.SPECS))
+def test_full_size_sampled_rows(name):
+    """Each workload at its full size, launched as the benchmark launches it; the oracle
+    checks a sample of (sequence, head) rows computed one by one, every row is finite."""
+    sp = workloads.SPECS[name]
+    seed = 8900 + list(workloads.SPECS).index(name)
+    ctx, free = workloads.draw_lengths(sp, seed)
+    pg, pl = workloads.prefix_groups(sp)
+    st, tables, _, _ = oracle.build_tables(sp.num_blocks, sp.block_size, free, ctx,
+                                           sp.max_blocks, pg, pl)
+    assert st == 0
+    q, kd, vd, ks, vs = workloads.device_pool(sp, seed)
+    out = pa.decode(q, kd, vd, dev_i32(tables), dev_i32(ctx), int(ctx.max()), sp.scale, ks, vs,
+                    partition_size=sp.partition_size)
+    torch.cuda.synchronize()
+    got = _f64(out)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(seed)
+    S, H = sp.num_seqs, sp.num_heads
+    rows = set(zip(rng.integers(0, S, FULL_SAMPLE_ROWS).tolist(),
+                   rng.integers(0, H, FULL_SAMPLE_ROWS).tolist()))
+    longest = int(np.argmax(ctx))
+    rows |= {(longest, h) for h in range(0, H, max(1, H // 8))}
+    rows = np.array(sorted(rows), np.int32)
+    qb, kb, vb = to_bits(q), to_bits(kd), to_bits(vd)
+    del kd, vd
+    ref = oracle.decode(qb, DT[sp.q_dtype], kb, vb, DT[sp.kv_dtype], tables, ctx,
+                        sp.num_kv_heads, sp.block_size, sp.scale, ks, vs, rows=rows)
+    atol, rrel = tolerance(sp)
+    compare(got[rows[:, 0], rows[:, 1]], ref[rows[:, 0], rows[:, 1]], atol, rrel, sp.q_dtype)
