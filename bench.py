@@ -91,9 +91,11 @@ def main():
         pa.write_kv(k_new, v_new, kc, vc, tables_d, seq_ids, positions, k_inv, v_inv,
                     stream=stream)
 
+    flags = pa.DECODE_SHARED_KV if sp.group_size else 0  # shared prompt blocks
+
     def decode():
         pa.decode(q, kc, vc, tables_d, ctx_d, max_ctx, sp.scale, k_scale, v_scale,
-                  partition_size=P, out=out, workspace=ws, stream=stream)
+                  partition_size=P, flags=flags, out=out, workspace=ws, stream=stream)
 
     kv_bytes = workloads.kv_bytes(sp, ctx)  # algorithmic K+V bytes one decode pass reads
 
@@ -154,6 +156,7 @@ def main():
             + (f"+{sp.prompt_len}" if sp.prompt_len else ""), "num_blocks": sp.num_blocks,
             "q_dtype": sp.q_dtype, "kv_dtype": sp.kv_dtype, "partition_size": used_P,
             "num_partitions": nparts, "kv_bytes_per_step": kv_bytes, "seed": seed,
+            "decode_flags": flags,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -155,10 +155,17 @@ pa_status pa_write_kv(const void* k_src, const void* v_src, void* k_cache, void*
  *   k_scale, v_scale  dequantisation scales of an e4m3 cache (value = code * scale);
  *                 ignored for fp16/bf16 caches
  *   partition_size 0 = library choice, else a positive multiple of block_size
+ *   flags         0, or PA_DECODE_SHARED_KV when some physical blocks are referenced by
+ *                 several sequences of the batch (shared prompts, [P1] sec. 5): K/V loads
+ *                 then stay cacheable and sequences are visited together so that a shared
+ *                 block is fetched from HBM once; without it K/V loads are streamed with
+ *                 the non-temporal hint.  Results are identical either way.
  *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes
  *                 (may be NULL when that size is 0)
  * Supported: head_dim in {64, 128}; block_size in {8, 16, 32}; num_heads / num_kv_heads in
  * {1, 2, 4, 8}; (q, kv) in {(f16, f16), (bf16, bf16), (f16, e4m3), (bf16, e4m3)}. */
+#define PA_DECODE_SHARED_KV 1u
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                 int32_t partition_size);
@@ -176,8 +183,8 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                     int32_t num_blocks, int32_t max_context_len, float scale,
                     pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
-                    int32_t partition_size, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    int32_t partition_size, uint32_t flags, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Footprint: [P1] sec. 1 "KV Cache Memory Footprint" — a token stores one key and one

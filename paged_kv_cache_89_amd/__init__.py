@@ -18,12 +18,13 @@ import os
 import numpy as np
 
 __all__ = [
-    "F16", "BF16", "FP8_E4M3", "PagedAttnError", "LibraryNotBuilt", "lib", "library_path",
+    "F16", "BF16", "FP8_E4M3", "DECODE_SHARED_KV", "PagedAttnError", "LibraryNotBuilt", "lib", "library_path",
     "BlockManager", "write_kv", "decode", "decode_plan", "decode_workspace_size",
     "kv_bytes_per_token", "version",
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
+DECODE_SHARED_KV = 1  # pa_decode flag: blocks are shared between sequences of the batch
 _STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED",
            -3: "PA_ERR_NO_BLOCKS", -4: "PA_ERR_TABLE_OVERFLOW", -5: "PA_ERR_HIP"}
 
@@ -70,7 +71,7 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_workspace_size.restype = sz
     L.pa_decode_plan.argtypes = [i32] * 7 + [vp, vp]
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                            f32, c.c_int, c.c_int, f32, f32, i32, vp, sz, vp]
+                            f32, c.c_int, c.c_int, f32, f32, i32, c.c_uint32, vp, sz, vp]
     L.pa_kv_bytes_per_token.argtypes = [i32, i32, i32, c.c_int]
     L.pa_kv_bytes_per_token.restype = c.c_uint64
     for name in ("pa_bm_create", "pa_alloc_tables", "pa_bm_free", "pa_bm_stats",
@@ -219,7 +220,7 @@ def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_siz
 
 def decode(query, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
            scale: float, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
-           out=None, workspace=None, stream=None):
+           flags: int = 0, out=None, workspace=None, stream=None):
     """pa_decode.  query [S, Hq, D]; returns out [S, Hq, D] (query dtype)."""
     torch = _torch()
     S, Hq, D = query.shape
@@ -239,7 +240,8 @@ def decode(query, k_cache, v_cache, block_tables, context_lens, max_context_len:
                            _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B, MB, NB,
                            int(max_context_len), float(scale), _dtype_code(query),
                            _dtype_code(k_cache), float(k_scale), float(v_scale),
-                           int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+                           int(partition_size), int(flags), ws_ptr, ws_bytes,
+                           _stream(stream)))
     return out
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libpaged_attn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "block_manager.cpp", "write_kv.hip", "merge.hip",
-           "decode_d64.hip", "decode_d128.hip"]
+           "decode_d64_nt.hip", "decode_d64_t.hip", "decode_d128_nt.hip", "decode_d128_t.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",

@@ -49,14 +49,17 @@ struct Plan {
   int32_t num_parts;
 };
 
-// Library choice of the partition length.  A unit is one wavefront; short sequences run
-// unsplit, longer ones are cut into partitions so the grid holds many more, and more
-// uniform, units than the chip has wave slots (the length mix of a batch is ragged, and a
-// few long units would otherwise leave most CUs idle at the end of the launch).
-int32_t auto_partition(int32_t max_ctx) {
-  if (max_ctx <= 256) return 0;
-  if (max_ctx <= 4096) return 256;
-  return 512;
+// Library choice of the partition length.  A unit is one wavefront.  Partitions of 512
+// tokens keep units long enough to stream efficiently while cutting ragged batches into
+// near-uniform pieces; when that leaves too few units to fill the chip's wave slots
+// (256 CUs), the partition is halved, down to 64 tokens.
+int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
+  const int64_t want_units = 4096;
+  int32_t P = 512;
+  while (P > 64 &&
+         (int64_t)num_seqs * num_kv_heads * ((max_ctx + P - 1) / P) < want_units)
+    P /= 2;
+  return P;
 }
 
 pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -67,7 +70,8 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
     return fail(PA_ERR_INVALID_ARG, "decode plan: negative or zero size");
   if (partition_size % block_size != 0)
     return fail(PA_ERR_INVALID_ARG, "decode plan: partition_size must be a multiple of block_size");
-  int32_t P = partition_size > 0 ? partition_size : auto_partition(max_context_len);
+  int32_t P = partition_size > 0 ? partition_size
+                                  : auto_partition(num_seqs, num_kv_heads, max_context_len);
   if (P > 0 && P % block_size != 0) P = ((P + block_size - 1) / block_size) * block_size;
   if (P == 0 || P >= max_context_len) {
     plan->partition_size = 0;
@@ -162,8 +166,8 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                     int32_t num_blocks, int32_t max_context_len, float scale,
                     pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
-                    int32_t partition_size, void* workspace, size_t workspace_bytes_given,
-                    void* stream) {
+                    int32_t partition_size, uint32_t flags, void* workspace,
+                    size_t workspace_bytes_given, void* stream) {
   g_last_error.clear();
   int qk, kk;
   if (!dtype_kind(q_dtype, &qk) || !dtype_kind(kv_dtype, &kk))
@@ -177,7 +181,12 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
     return fail(PA_ERR_INVALID_ARG, "pa_decode: partition_size must be a multiple of block_size");
   if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PA_ERR_INVALID_ARG, "pa_decode: non-finite scale");
-  DecodeShape shape{head_dim, block_size, qk, kk, num_heads / num_kv_heads};
+  if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
+    return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown flag bits");
+  const bool shared = (flags & PA_DECODE_SHARED_KV) != 0;
+  // Read-once K/V streams with the non-temporal hint; blocks shared between sequences of
+  // the batch stay cacheable and the sharing sequences are visited together.
+  DecodeShape shape{head_dim, block_size, qk, kk, num_heads / num_kv_heads, !shared};
   if (!decode_supported(shape))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: unsupported head_dim/block_size/group/dtype pair");
   if (num_seqs == 0) return PA_OK;
@@ -187,9 +196,11 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   // Tokens beyond the table's reach can never be addressed.
   const int64_t reach = (int64_t)max_blocks_per_seq * block_size;
   const int32_t max_ctx = (int32_t)(max_context_len < reach ? max_context_len : reach);
+  // Plan from the caller's bound, exactly as pa_decode_workspace_size does; units beyond
+  // the table's reach find no blocks and exit.
   Plan plan;
-  pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
-                           partition_size, &plan);
+  pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, partition_size, &plan);
   if (st != PA_OK) return st;
   const size_t need = workspace_bytes(plan, num_seqs, num_heads, head_dim);
   if (need > 0 && (!workspace || workspace_bytes_given < need))
@@ -213,6 +224,8 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   const bool f8 = kk == KIND_E4M3;
   a.qk_scale = scale * kLog2e * (f8 ? k_scale : 1.0f);
   a.v_scale = f8 ? v_scale : 1.0f;
+  a.seq_fastest = shared ? 1 : 0;
+  a.xcd_remap = 1;
   if (log_enabled())
     std::fprintf(stderr, "[paged_attn] decode S=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d P=%d parts=%d units=%lld\n",
                  num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
@@ -231,8 +244,10 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
 
 namespace pa {
 
-hipError_t launch_decode_64(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_128(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_64_nt(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_64_t(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_128_nt(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_128_t(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
 
 bool decode_supported(const DecodeShape& s) {
   if (s.head_dim != 64 && s.head_dim != 128) return false;
@@ -243,8 +258,10 @@ bool decode_supported(const DecodeShape& s) {
 }
 
 hipError_t launch_decode(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream) {
-  if (s.head_dim == 128) return launch_decode_128(s, a, stream);
-  if (s.head_dim == 64) return launch_decode_64(s, a, stream);
+  if (s.head_dim == 128)
+    return s.nontemporal ? launch_decode_128_nt(s, a, stream) : launch_decode_128_t(s, a, stream);
+  if (s.head_dim == 64)
+    return s.nontemporal ? launch_decode_64_nt(s, a, stream) : launch_decode_64_t(s, a, stream);
   return hipErrorInvalidValue;
 }
 

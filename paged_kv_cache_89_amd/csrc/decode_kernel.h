@@ -39,6 +39,14 @@
 #include "device_common.h"
 #include "launch.h"
 
+// Compile-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4        // wavefronts (independent work units) per workgroup
+#endif
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 2        // K/V register buffers: blocks in flight = DEPTH - 1
+#endif
+
 namespace pa {
 
 template <int D, int BS, int KVK>
@@ -83,8 +91,9 @@ struct TableWalk {
   }
 };
 
-template <int D, int BS, int QK, int KVK, int G>
-__global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeArgs a) {
+// NT: K/V loads carry the non-temporal hint (data read once per step).
+template <int D, int BS, int QK, int KVK, int G, bool NT>
+__global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(const DecodeArgs a) {
   using Geo = TileGeometry<D, BS, KVK>;
   using LT = typename LoadVec<Geo::W>::T;
   constexpr int W = Geo::W, EPL = Geo::EPL, LPT = Geo::LPT, TPL = Geo::TPL, NLD = Geo::NLD;
@@ -93,12 +102,27 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * 4 + wave;
+  int wg = blockIdx.x;
+  if (a.xcd_remap) {
+    // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that XCD x runs a
+    // contiguous range of logical workgroups (a bijection for any grid size).
+    const int G8 = gridDim.x, x = wg % 8, loc = wg / 8, per = G8 / 8, rem = G8 % 8;
+    wg = (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
+  }
+  const int unit = wg * PA_DECODE_WAVES + wave;
   if (unit >= a.num_units) return;
-  const int kvh = unit % a.num_kv_heads;
-  const int rest = unit / a.num_kv_heads;
-  const int part = rest % a.num_parts;
-  const int s = rest / a.num_parts;
+  int s, kvh, part;
+  if (a.seq_fastest == 0) {  // (seq, part, kv head): neighbouring heads of the same blocks
+    kvh = unit % a.num_kv_heads;
+    const int rest = unit / a.num_kv_heads;
+    part = rest % a.num_parts;
+    s = rest / a.num_parts;
+  } else {                   // (part, kv head, seq): sequences that share blocks run together
+    s = unit % a.num_seqs;
+    const int rest = unit / a.num_seqs;
+    kvh = rest % a.num_kv_heads;
+    part = rest / a.num_kv_heads;
+  }
   const int h0 = kvh * G;
 
   int n = a.ctx[s];
@@ -165,9 +189,15 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeArgs a) {
     const char* kp = kbase + (size_t)phys * blk_stride;
     const char* vp = vbase + (size_t)phys * blk_stride;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) kr[i] = *(const LT*)(kp + loff + i * Geo::SPAN);
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (NT) kr[i] = __builtin_nontemporal_load((const LT*)(kp + loff + i * Geo::SPAN));
+      else kr[i] = *(const LT*)(kp + loff + i * Geo::SPAN);
+    }
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) vr[i] = *(const LT*)(vp + loff + i * Geo::SPAN);
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (NT) vr[i] = __builtin_nontemporal_load((const LT*)(vp + loff + i * Geo::SPAN));
+      else vr[i] = *(const LT*)(vp + loff + i * Geo::SPAN);
+    }
   };
 
   // Fold one block into the running state.  MASK: the block holds slots >= n.
@@ -275,18 +305,28 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeArgs a) {
     else consume(std::true_type{}, j, kr, vr);
   };
 
+  // Register ring of DEPTH K/V buffers: block j + DEPTH - 1 is requested before block j
+  // is consumed.  The ring is walked by a fully unrolled inner loop so every buffer index
+  // is a compile-time constant (no register indexing).
+  constexpr int DEPTH = PA_DECODE_DEPTH;
   TableWalk tw;
   tw.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
-  LT ka[NLD], va[NLD], kb[NLD], vb[NLD];
-  issue(tw.get(j0, lane), ka, va);
+  LT kq[DEPTH][NLD], vq[DEPTH][NLD];
+#pragma unroll
+  for (int b = 0; b < DEPTH - 1; ++b)
+    if (j0 + b < j1) issue(tw.get(j0 + b, lane), kq[b], vq[b]);
   int j = j0;
-  while (true) {
-    if (j + 1 < j1) issue(tw.get(j + 1, lane), kb, vb);
-    process(j, ka, va);
-    if (++j >= j1) break;
-    if (j + 1 < j1) issue(tw.get(j + 1, lane), ka, va);
-    process(j, kb, vb);
-    if (++j >= j1) break;
+  bool more = true;
+  while (more) {
+#pragma unroll
+    for (int b = 0; b < DEPTH; ++b) {
+      if (more) {
+        if (j + DEPTH - 1 < j1)
+          issue(tw.get(j + DEPTH - 1, lane), kq[(b + DEPTH - 1) % DEPTH], vq[(b + DEPTH - 1) % DEPTH]);
+        process(j, kq[b], vq[b]);
+        more = ++j < j1;
+      }
+    }
   }
 
   // ---- merge the TPL lane-group states of the wave (same rescaling rule)
@@ -343,22 +383,23 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(const DecodeArgs a) {
   }
 }
 
-template <int D, int BS, int QK, int KVK, int G>
+template <int D, int BS, int QK, int KVK, int G, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid((a.num_units + 3) / 4);
-  hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G>), grid, dim3(256), 0, stream, a);
+  const dim3 grid((a.num_units + PA_DECODE_WAVES - 1) / PA_DECODE_WAVES);
+  hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT>), grid, dim3(64 * PA_DECODE_WAVES),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-// Instantiate every (block size, dtype pair, group) for one head_dim.
-template <int D>
+// Instantiate every (block size, dtype pair, group) for one head_dim and load policy.
+template <int D, bool NT>
 hipError_t launch_decode_d(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream) {
 #define PA_G(BS, QK, KVK)                                                  \
   switch (s.group) {                                                       \
-    case 1: return launch_decode_t<D, BS, QK, KVK, 1>(a, stream);          \
-    case 2: return launch_decode_t<D, BS, QK, KVK, 2>(a, stream);          \
-    case 4: return launch_decode_t<D, BS, QK, KVK, 4>(a, stream);          \
-    case 8: return launch_decode_t<D, BS, QK, KVK, 8>(a, stream);          \
+    case 1: return launch_decode_t<D, BS, QK, KVK, 1, NT>(a, stream);      \
+    case 2: return launch_decode_t<D, BS, QK, KVK, 2, NT>(a, stream);      \
+    case 4: return launch_decode_t<D, BS, QK, KVK, 4, NT>(a, stream);      \
+    case 8: return launch_decode_t<D, BS, QK, KVK, 8, NT>(a, stream);      \
     default: return hipErrorInvalidValue;                                  \
   }
 #define PA_DT(BS)                                                                     \

@@ -28,10 +28,13 @@ struct DecodeArgs {
   int32_t num_parts, blocks_per_part, num_units;
   float qk_scale;            // scale * log2(e) * k_scale
   float v_scale;
+  int32_t seq_fastest;       // unit order: 0 = (seq, part, kv head), 1 = (part, kv head, seq)
+  int32_t xcd_remap;         // 1 = each XCD runs a contiguous range of workgroups
 };
 
 struct DecodeShape {
   int head_dim, block_size, q_kind, kv_kind, group;
+  bool nontemporal;          // K/V loads with the non-temporal hint
 };
 
 bool decode_supported(const DecodeShape& s);

@@ -36,14 +36,20 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _gpu_decode(case, tables, k, v, partition_size=None, max_ctx=None):
+def _flags(spec):
+    """The decode flags a caller would pass: shared prompt blocks -> PA_DECODE_SHARED_KV."""
+    return pa.DECODE_SHARED_KV if spec.group_size else 0
+
+
+def _gpu_decode(case, tables, k, v, partition_size=None, max_ctx=None, flags=None):
     sp = case.spec
     q = to_dev(case.q, sp.q_dtype)
     kd, vd = to_dev(k, sp.kv_dtype), to_dev(v, sp.kv_dtype)
     P = sp.partition_size if partition_size is None else partition_size
     mc = int(case.context_lens.max()) if max_ctx is None else max_ctx
     out = pa.decode(q, kd, vd, dev_i32(tables), dev_i32(case.context_lens), mc, sp.scale,
-                    case.k_scale, case.v_scale, partition_size=P)
+                    case.k_scale, case.v_scale, partition_size=P,
+                    flags=_flags(sp) if flags is None else flags)
     torch.cuda.synchronize()
     return out
 
@@ -148,7 +154,7 @@ def test_end_to_end_block_manager_write_decode(name):
                 case.v_inv_scale)
     out = pa.decode(to_dev(case.q, sp.q_dtype), kd, vd, td, dev_i32(case.context_lens),
                     int(case.context_lens.max()), sp.scale, case.k_scale, case.v_scale,
-                    partition_size=sp.partition_size)
+                    partition_size=sp.partition_size, flags=_flags(sp))
     torch.cuda.synchronize()
     atol, rrel = tolerance(sp)
     compare(_f64(out), ref, atol, rrel, case.spec.q_dtype)
@@ -173,9 +179,10 @@ def test_decode_ragged_lengths_all_variants(B, d, dt):
         ref = oracle_decode(case, tables, k, v)
         atol, rrel = tolerance(sp)
         for P in (0, B, 4 * B):
-            out = _f64(_gpu_decode(case, tables, k, v, partition_size=P))
-            assert (out[0] == 0).all(), "n = 0 must give a zero row"
-            compare(out, ref, atol, rrel, qd)
+            for flags in (0, pa.DECODE_SHARED_KV):  # streaming and cacheable K/V loads
+                out = _f64(_gpu_decode(case, tables, k, v, partition_size=P, flags=flags))
+                assert (out[0] == 0).all(), "n = 0 must give a zero row"
+                compare(out, ref, atol, rrel, qd)
 
 
 def test_single_token_returns_v1_bit_exact():
@@ -221,6 +228,18 @@ def test_physical_permutation_bit_identical():
     assert np.array_equal(out1, out2)
 
 
+@pytest.mark.parametrize("name", ["opt13b_layer", "fp8_prefix"])
+def test_load_policy_flag_gives_identical_results(name):
+    """PA_DECODE_SHARED_KV only changes cache hints and the order units are visited:
+    every unit computes the same thing, so the output is bit-identical."""
+    case = workloads.generate(workloads.SMALL[name], 8900 + 26)
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    a = to_bits(_gpu_decode(case, tables, k, v, flags=0))
+    b = to_bits(_gpu_decode(case, tables, k, v, flags=pa.DECODE_SHARED_KV))
+    assert np.array_equal(a, b)
+
+
 def test_partition_size_invariance_and_determinism():
     case = workloads.generate(workloads.SMALL["long_split"], 8900 + 24)
     sp = case.spec
@@ -264,7 +283,7 @@ def test_full_size_sampled_rows(name):
     assert st == 0
     q, kd, vd, ks, vs = workloads.device_pool(sp, seed)
     out = pa.decode(q, kd, vd, dev_i32(tables), dev_i32(ctx), int(ctx.max()), sp.scale, ks, vs,
-                    partition_size=sp.partition_size)
+                    partition_size=sp.partition_size, flags=_flags(sp))
     torch.cuda.synchronize()
     got = _f64(out)
     assert np.isfinite(got).all()

@@ -133,8 +133,13 @@ def test_decode_plan_and_workspace():
     P, n = pa.decode_plan(8, 32, 32, 128, 32, 32768, 512)
     assert (P, n) == (512, 64)
     assert pa.decode_workspace_size(8, 32, 32, 128, 32, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (0, 1)
-    assert pa.decode_workspace_size(4, 8, 8, 64, 16, 256, 0) == 0
+    # library choice: 512-token partitions, halved while the grid has < 4096 units
+    assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0) == (512, 4)
+    assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (512, 64)
+    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (64, 4)
+    assert pa.decode_plan(1, 8, 8, 64, 16, 48, 0) == (0, 1)      # fits one partition
+    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 4096) == (0, 1)  # explicit P >= context
+    assert pa.decode_workspace_size(4, 8, 8, 64, 16, 256, 4096) == 0
     with pytest.raises(pa.PagedAttnError):
         pa.decode_plan(4, 8, 8, 64, 16, 256, 24)  # not a multiple of B
 
@@ -143,14 +148,17 @@ def test_decode_argument_errors_without_gpu():
     L = pa.lib()
     # unsupported head_dim is reported before any pointer is touched
     st = L.pa_decode(None, None, None, None, None, None, 1, 8, 8, 96, 16, 4, 4, 64, 0.1,
-                     0, 0, 1.0, 1.0, 0, None, 0, None)
+                     0, 0, 1.0, 1.0, 0, 0, None, 0, None)
     assert st == -2 and b"unsupported" in L.pa_last_error()
     st = L.pa_decode(None, None, None, None, None, None, 1, 6, 4, 128, 16, 4, 4, 64, 0.1,
-                     0, 0, 1.0, 1.0, 0, None, 0, None)
+                     0, 0, 1.0, 1.0, 0, 0, None, 0, None)
     assert st == -1
     st = L.pa_decode(None, None, None, None, None, None, 1, 8, 8, 128, 16, 4, 4, 64, 0.1,
-                     0, 0, 1.0, 1.0, 0, None, 0, None)
+                     0, 0, 1.0, 1.0, 0, 0, None, 0, None)
     assert st == -1 and b"NULL" in L.pa_last_error()
+    st = L.pa_decode(None, None, None, None, None, None, 1, 8, 8, 128, 16, 4, 4, 64, 0.1,
+                     0, 0, 1.0, 1.0, 0, 6, None, 0, None)
+    assert st == -1 and b"flag" in L.pa_last_error()
     st = L.pa_write_kv(None, None, None, None, None, 1, 4, None, None, 1, 4, 8, 128, 12,
                        0, 0, 1.0, 1.0, None)
     assert st == -2
