@@ -26,6 +26,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+COUNTER_SOURCES = os.path.join(ROOT, "paged_kv_cache_89_amd", "csrc")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per pa_decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this workload, or None when there is none or the kernel sources changed
+    since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"decode_counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["kernel_sources"]:
+        h.update(open(os.path.join(COUNTER_SOURCES, f), "rb").read())
+    if h.hexdigest()[:16] != rec["kernel_sources_sha256_16"]:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -160,7 +179,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(sp.name),
             "kernel": "paged_decode_kernel" + (" + merge_partitions_kernel" if nparts > 1 else ""),
             "mean_launch_ms": round(dec_ms_mean, 5),
             "median_launch_ms": round(float(np.median(dec_ms)), 5),

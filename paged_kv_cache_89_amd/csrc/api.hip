@@ -49,14 +49,16 @@ struct Plan {
   int32_t num_parts;
 };
 
-// Library choice of the partition length.  A unit is one wavefront.  Partitions of 512
-// tokens keep units long enough to stream efficiently while cutting ragged batches into
-// near-uniform pieces; when that leaves too few units to fill the chip's wave slots
-// (256 CUs), the partition is halved, down to 64 tokens.
+// Library choice of the partition length.  A unit is one wavefront.  Contexts of at most
+// 256 tokens run unsplit (the merge launch would cost more than it balances).  Otherwise
+// partitions of 512 tokens keep units long enough to stream efficiently while cutting
+// ragged batches into near-uniform pieces; when that leaves too few units to fill the
+// chip's wave slots (256 CUs), the partition is halved, down to 128 tokens.
 int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
+  if (max_ctx <= 256) return 0;
   const int64_t want_units = 4096;
   int32_t P = 512;
-  while (P > 64 &&
+  while (P > 128 &&
          (int64_t)num_seqs * num_kv_heads * ((max_ctx + P - 1) / P) < want_units)
     P /= 2;
   return P;

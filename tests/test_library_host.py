@@ -133,11 +133,13 @@ def test_decode_plan_and_workspace():
     P, n = pa.decode_plan(8, 32, 32, 128, 32, 32768, 512)
     assert (P, n) == (512, 64)
     assert pa.decode_workspace_size(8, 32, 32, 128, 32, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    # library choice: 512-token partitions, halved while the grid has < 4096 units
+    # library choice: contexts <= 256 unsplit; else 512-token partitions, halved (down to
+    # 128) while the grid has < 4096 units
     assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0) == (512, 4)
     assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (512, 64)
-    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (64, 4)
-    assert pa.decode_plan(1, 8, 8, 64, 16, 48, 0) == (0, 1)      # fits one partition
+    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (0, 1)
+    assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0) == (128, 16)
+    assert pa.decode_plan(1, 8, 8, 64, 16, 48, 0) == (0, 1)
     assert pa.decode_plan(4, 8, 8, 64, 16, 256, 4096) == (0, 1)  # explicit P >= context
     assert pa.decode_workspace_size(4, 8, 8, 64, 16, 256, 4096) == 0
     with pytest.raises(pa.PagedAttnError):
