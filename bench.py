@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--workload", default="opt13b_layer")
     ap.add_argument("--partition-size", type=int, default=-1,
                     help="-1: the workload's setting (0 = library choice)")
+    ap.add_argument("--decode-flags", type=int, default=-1,
+                    help="-1: the workload's setting (PA_DECODE_SHARED_KV for shared prompts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -111,6 +113,8 @@ def main():
                     stream=stream)
 
     flags = pa.DECODE_SHARED_KV if sp.group_size else 0  # shared prompt blocks
+    if args.decode_flags >= 0:
+        flags = args.decode_flags
 
     def decode():
         pa.decode(q, kc, vc, tables_d, ctx_d, max_ctx, sp.scale, k_scale, v_scale,

@@ -154,7 +154,9 @@ pa_status pa_write_kv(const void* k_src, const void* v_src, void* k_cache, void*
  *                 context_lens are clamped to it and to max_blocks_per_seq * block_size)
  *   k_scale, v_scale  dequantisation scales of an e4m3 cache (value = code * scale);
  *                 ignored for fp16/bf16 caches
- *   partition_size 0 = library choice, else a positive multiple of block_size
+ *   partition_size 0 = library choice, else a positive multiple of block_size; a
+ *                 partition never spans more than 64 blocks (larger values, and unsplit
+ *                 contexts longer than 64 blocks, are cut into 64-block partitions)
  *   flags         0, or PA_DECODE_SHARED_KV when some physical blocks are referenced by
  *                 several sequences of the batch (shared prompts, [P1] sec. 5): K/V loads
  *                 then stay cacheable and sequences are visited together so that a shared

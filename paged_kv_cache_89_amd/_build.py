@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libpaged_attn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "block_manager.cpp", "write_kv.hip", "merge.hip",
-           "decode_d64_nt.hip", "decode_d64_t.hip", "decode_d128_nt.hip", "decode_d128_t.hip"]
+           "decode_d64_nt.hip", "decode_d64_t.hip", "decode_d128_nt.hip", "decode_d128_t.hip", "decode_gqa.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",
@@ -30,9 +30,14 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",
          "-Wno-unused-command-line-argument"]
 
 
+# Per-source extra flags.  The matrix-core kernels keep their MFMA accumulators in
+# ordinary VGPRs (no AGPR round trips around the loop's rarely taken rescale branch).
+EXTRA = {"decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -75,6 +75,10 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
   int32_t P = partition_size > 0 ? partition_size
                                   : auto_partition(num_seqs, num_kv_heads, max_context_len);
   if (P > 0 && P % block_size != 0) P = ((P + block_size - 1) / block_size) * block_size;
+  // A work unit walks at most kMaxUnitBlocks blocks (its table slice lives in one VGPR).
+  const int64_t cap = (int64_t)kMaxUnitBlocks * block_size;
+  if (P == 0 && max_context_len > cap) P = (int32_t)cap;
+  if (P > cap) P = (int32_t)cap;
   if (P == 0 || P >= max_context_len) {
     plan->partition_size = 0;
     plan->num_parts = 1;
@@ -259,7 +263,14 @@ bool decode_supported(const DecodeShape& s) {
   return s.kv_kind == s.q_kind || s.kv_kind == KIND_E4M3;
 }
 
+bool gqa_mfma_supported(const DecodeShape& s);
+hipError_t launch_decode_gqa_mfma(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+
+// Grouped-query shapes with 16-token blocks and fp16/bf16 caches run the matrix-core
+// kernel; every other shape runs the vector kernel (which also covers e4m3 caches).
 hipError_t launch_decode(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream) {
+  if (gqa_mfma_supported(s))
+    return launch_decode_gqa_mfma(s, a, stream);
   if (s.head_dim == 128)
     return s.nontemporal ? launch_decode_128_nt(s, a, stream) : launch_decode_128_t(s, a, stream);
   if (s.head_dim == 64)

@@ -26,9 +26,10 @@
 //     the same rescaling rule;
 //   * the lane holds exactly the K/V elements its arithmetic needs, so tiles go straight
 //     from HBM into registers (no LDS round trip); the next block's K and V loads are
-//     issued before the current block is consumed (register double buffering), and a
-//     64-entry slice of the block table sits in one VGPR, read with v_readlane into
-//     scalar registers so the address of the next tile never waits on memory;
+//     issued before the current block is consumed (register double buffering), and the
+//     unit's slice of the block table (at most 64 entries) sits in one VGPR, read with
+//     v_readlane into scalar registers so the address of the next tile never waits on
+//     memory;
 //   * GQA (G query heads per KV head) reuses each loaded tile for all G heads;
 //   * e4m3 tiles are decoded in registers by the hardware fp8 converter; k_scale is
 //     folded into the logit scale and v_scale into the epilogue.
@@ -42,9 +43,6 @@
 // Compile-time tuning knobs (defaults are the measured best on MI355X).
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 4        // wavefronts (independent work units) per workgroup
-#endif
-#ifndef PA_DECODE_DEPTH
-#define PA_DECODE_DEPTH 2        // K/V register buffers: blocks in flight = DEPTH - 1
 #endif
 
 namespace pa {
@@ -68,28 +66,6 @@ template <int W> struct LoadVec;
 template <> struct LoadVec<4> { using T = u32x4; };
 template <> struct LoadVec<2> { using T = u32x2; };
 
-// Block-table slice kept in a VGPR: lane k holds entry base + k.  Entries outside
-// [0, num_blocks) are replaced by block 0 so a malformed table can never fault.
-struct TableWalk {
-  const int32_t* row;
-  int j1, nb, base, cur, nxt;
-
-  __device__ __forceinline__ void init(const int32_t* r, int j0, int j1_, int nb_, int lane) {
-    row = r; j1 = j1_; nb = nb_; base = j0;
-    cur = (j0 + lane < j1) ? row[j0 + lane] : 0;
-    nxt = (j0 + 64 + lane < j1) ? row[j0 + 64 + lane] : 0;
-  }
-  // j is wave-uniform and never decreases between calls.
-  __device__ __forceinline__ int get(int j, int lane) {
-    if (j - base >= 64) {
-      base += 64;
-      cur = nxt;
-      nxt = (base + 64 + lane < j1) ? row[base + 64 + lane] : 0;
-    }
-    const int p = __builtin_amdgcn_readlane(cur, j - base);
-    return ((unsigned)p < (unsigned)nb) ? p : 0;
-  }
-};
 
 // NT: K/V loads carry the non-temporal hint (data read once per step).
 template <int D, int BS, int QK, int KVK, int G, bool NT>
@@ -305,28 +281,28 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
     else consume(std::true_type{}, j, kr, vr);
   };
 
-  // Register ring of DEPTH K/V buffers: block j + DEPTH - 1 is requested before block j
-  // is consumed.  The ring is walked by a fully unrolled inner loop so every buffer index
-  // is a compile-time constant (no register indexing).
-  constexpr int DEPTH = PA_DECODE_DEPTH;
-  TableWalk tw;
-  tw.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
-  LT kq[DEPTH][NLD], vq[DEPTH][NLD];
-#pragma unroll
-  for (int b = 0; b < DEPTH - 1; ++b)
-    if (j0 + b < j1) issue(tw.get(j0 + b, lane), kq[b], vq[b]);
+  // Software pipeline: the K/V loads of block j+1 are issued before block j is consumed
+  // (two register sets).  The steady-state loop always has a next block to request, so every
+  // load in it is unconditional and the compiler's in-order load counter waits for exactly
+  // the block being consumed; the last one or two blocks are peeled off the loop.
+  TableSlice ts;
+  ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
+  LT ka[NLD], va[NLD], kb[NLD], vb[NLD];
+  issue(ts.get(j0), ka, va);
   int j = j0;
-  bool more = true;
-  while (more) {
-#pragma unroll
-    for (int b = 0; b < DEPTH; ++b) {
-      if (more) {
-        if (j + DEPTH - 1 < j1)
-          issue(tw.get(j + DEPTH - 1, lane), kq[(b + DEPTH - 1) % DEPTH], vq[(b + DEPTH - 1) % DEPTH]);
-        process(j, kq[b], vq[b]);
-        more = ++j < j1;
-      }
-    }
+  while (j + 2 < j1) {
+    issue(ts.get(j + 1), kb, vb);
+    process(j, ka, va);
+    issue(ts.get(j + 2), ka, va);
+    process(j + 1, kb, vb);
+    j += 2;
+  }
+  if (j + 1 < j1) {
+    issue(ts.get(j + 1), kb, vb);
+    process(j, ka, va);
+    process(j + 1, kb, vb);
+  } else {
+    process(j, ka, va);
   }
 
   // ---- merge the TPL lane-group states of the wave (same rescaling rule)

@@ -95,4 +95,26 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
   return sign | (uint32_t)m;
 }
 
+// A work unit walks at most 64 blocks, so its slice of the block table fits one VGPR:
+// lane k holds entry j0 + k (loaded once, unconditionally, with the index clamped into the
+// unit's range), and the physical id of block j is read with v_readlane into a scalar
+// register.  Entries outside [0, num_blocks) are replaced by block 0 so a malformed table
+// can never fault.  Keeping every load of the block loop unconditional also lets the
+// compiler's in-order load counters wait for exactly the block being consumed.
+struct TableSlice {
+  int j0, nb, ids;
+
+  __device__ __forceinline__ void init(const int32_t* row, int j0_, int j1, int nb_, int lane) {
+    j0 = j0_;
+    nb = nb_;
+    const int jj = j0 + lane < j1 ? j0 + lane : j1 - 1;
+    ids = row[jj];
+  }
+  // j is wave-uniform, j0 <= j < j0 + 64
+  __device__ __forceinline__ int get(int j) const {
+    const int p = __builtin_amdgcn_readlane(ids, j - j0);
+    return ((unsigned)p < (unsigned)nb) ? p : 0;
+  }
+};
+
 }  // namespace pa

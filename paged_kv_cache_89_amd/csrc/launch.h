@@ -11,6 +11,7 @@ namespace pa {
 enum Kind : int { KIND_F16 = 0, KIND_BF16 = 1, KIND_E4M3 = 2 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxUnitBlocks = 64;  // blocks one work unit (wavefront) walks at most
 
 // Decode over work units (sequence, KV head, partition).  A unit walks blocks
 // [part * blocks_per_part, min(ceil(n / B), (part + 1) * blocks_per_part)) of its

@@ -166,10 +166,11 @@ def test_end_to_end_block_manager_write_decode(name):
                                 ("f16", "e4m3")])
 def test_decode_ragged_lengths_all_variants(B, d, dt):
     """Every compiled (head_dim, block size, dtype) variant on lengths around block and
-    partition edges, including 0 and 1, with GQA groups 1 and 4."""
+    partition edges, including 0 and 1, with GQA groups 1, 2, 4 and 8 (16-token fp16/bf16
+    blocks with G >= 2 run on the matrix-core kernel, the rest on the vector kernel)."""
     qd, kvd = dt
     lens = [0, 1, B - 1, B, B + 1, 2 * B + 3, 97, 300, 513]
-    for G in (1, 4):
+    for G in (1, 2, 4, 8):
         sp = workloads.Spec("rag", len(lens), 4 * G, 4, d, B, 1, 1,
                             sum(math.ceil(n / B) for n in lens) + 7,
                             math.ceil(max(lens) / B) + 2, qd, kvd, 1 / math.sqrt(d))

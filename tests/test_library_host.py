@@ -141,6 +141,9 @@ def test_decode_plan_and_workspace():
     assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0) == (128, 16)
     assert pa.decode_plan(1, 8, 8, 64, 16, 48, 0) == (0, 1)
     assert pa.decode_plan(4, 8, 8, 64, 16, 256, 4096) == (0, 1)  # explicit P >= context
+    # a unit walks at most 64 blocks: longer partitions / unsplit contexts are cut
+    assert pa.decode_plan(2, 8, 8, 64, 16, 4000, 4096) == (1024, 4)
+    assert pa.decode_plan(2, 8, 8, 64, 8, 2000, 1024) == (512, 4)
     assert pa.decode_workspace_size(4, 8, 8, 64, 16, 256, 4096) == 0
     with pytest.raises(pa.PagedAttnError):
         pa.decode_plan(4, 8, 8, 64, 16, 256, 24)  # not a multiple of B
