@@ -11,14 +11,16 @@
 //            (D/16 x v_mfma 16x16x16, one per 16-wide slice of the head dimension)
 //
 // Operand placement (lane l, r = l / 16, c = l % 16):
-//   * K comes straight from HBM: lane l loads the 16 bytes of token c at dims
-//     32kk + 8r .. +8 for k-step kk (each instruction reads 16 runs of 64 bytes);
+//   * K and V are read from HBM in fully coalesced 1 KiB wave loads and written row-major
+//     into this wavefront's two LDS tiles (bank-swizzled 16-byte chunks).  K's A operand
+//     (token c, dims 32kk + 8r .. +8) comes back with one ds_read_b128 per k-step.
+//     Reading K straight into that operand layout from HBM would touch 16 rows x 64 bytes
+//     per load instruction; measured, the coalesced route is 13 % faster;
 //   * Q^T is loaded once: lane l holds head c's dims 32kk + 8r .. +8 (zero for c >= G);
 //   * the logit result leaves in lane l the scores of head c for tokens 4r .. 4r+3, which
 //     is exactly the A-operand layout of the P . V contraction, so softmax weights never
 //     move between lanes;
-//   * V is read from HBM in fully coalesced 1 KiB wave loads, written row-major into this
-//     wavefront's LDS tile, and read back with ds_read_b64_tr_b16, which hands each lane the
+//   * V is read back from its LDS tile with ds_read_b64_tr_b16, which hands each lane the
 //     four tokens of one head-dimension column that the P . V B-operand needs.
 // Softmax statistics use a lazily moved reference maximum: weights are 2^(z - m_ref) and
 // m_ref (and with it acc and the denominator) is only moved when a block's maximum exceeds
@@ -96,6 +98,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   static_assert(G >= 2 && G <= 16, "group size");
   using Ops = MfmaOps<QK>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[4][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ktiles[4][TILE];
 
   // 16-byte chunk x of LDS row `row` holds chunk x ^ swz(row) of the V row: the two
   // chunks every ds_read_b64_tr_b16 takes from each of 16 rows then fall on distinct
@@ -162,10 +165,9 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   const size_t blk_stride = (size_t)a.num_kv_heads * TILE;
   const char* kbase = (const char*)a.k + (size_t)kvh * TILE;
   const char* vbase = (const char*)a.v + (size_t)kvh * TILE;
-  // K operand: token c, dims 32kk + 8r .. +8  ->  byte c*2D + 64kk + 16r
-  const uint32_t koff = (uint32_t)c * (2 * D) + 16 * r;
-  const uint32_t voff = (uint32_t)lane * 16;  // natural 1 KiB wave loads
+  const uint32_t voff = (uint32_t)lane * 16;  // natural 1 KiB wave loads (K and V)
   uint8_t* vt = lds_tiles[wave];
+  uint8_t* kt = lds_ktiles[wave];
   const float qk_scale = a.qk_scale;
   // LDS byte offsets: where this lane's V chunk of wave load i goes, and where its
   // ds_read_b64_tr_b16 of output slice t reads (row 4r + c/4, dims 16t + 4(c%4) .. +4)
@@ -177,13 +179,25 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   }
   const int trow = 4 * r + c / 4;
 
-  auto load_k = [&](int phys, u32x4 (&kr)[KSTEPS]) {
+  auto load_k = [&](int phys, u32x4 (&kr)[NLDV]) {
     const char* kp = kbase + (size_t)phys * blk_stride;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      if constexpr (NT) kr[kk] = __builtin_nontemporal_load((const u32x4*)(kp + koff + 64 * kk));
-      else kr[kk] = *(const u32x4*)(kp + koff + 64 * kk);
+    for (int i = 0; i < NLDV; ++i) {
+      if constexpr (NT) kr[i] = __builtin_nontemporal_load((const u32x4*)(kp + voff + 1024 * i));
+      else kr[i] = *(const u32x4*)(kp + voff + 1024 * i);
     }
+  };
+  // K rows into their LDS tile: 16-byte chunk x of row t sits at chunk x ^ (t mod LPT), so
+  // the A-operand reads (row c, chunk 4kk + r) of 16 lanes hit 16 different bank groups
+  uint32_t kw_off[NLDV];
+#pragma unroll
+  for (int i = 0; i < NLDV; ++i) {
+    const int row = i * TPL + lane / LPT;
+    kw_off[i] = row * PITCH + (((lane % LPT) ^ (row % LPT)) * 16);
+  }
+  auto stage_k = [&](const u32x4 (&kr)[NLDV]) {
+#pragma unroll
+    for (int i = 0; i < NLDV; ++i) *(u32x4*)(kt + kw_off[i]) = kr[i];
   };
   auto load_v = [&](int phys, u32x4 (&vr)[NLDV]) {
     const char* vp = vbase + (size_t)phys * blk_stride;
@@ -205,10 +219,14 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   };
 
   // logits of block j: C[token 4r+i][head c]
-  auto logits = [&](const u32x4 (&kr)[KSTEPS]) {
+  auto logits = [&]() {
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) sc = Ops::qk(kr[kk], qop[kk], sc);
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int chunk = (4 * kk + r) ^ (c % LPT);
+      const u32x4 kop = *(const u32x4*)(kt + c * PITCH + chunk * 16);
+      sc = Ops::qk(kop, qop[kk], sc);
+    }
     return sc;
   };
 
@@ -257,19 +275,20 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   // register sets each, as in the vector kernel); consuming block j moves V(j) into the
   // LDS tile, runs the logit contraction on K(j), the softmax update and P . V.  The mask
   // of slots >= n is applied branch-free (it only bites in a unit's last block).
-  auto process = [&](int j, const u32x4 (&kr)[KSTEPS], const u32x4 (&vr)[NLDV]) {
+  auto process = [&](int j, const u32x4 (&kr)[NLDV], const u32x4 (&vr)[NLDV]) {
+    stage_k(kr);
     stage_v(true, j, vr);
-    finish(j, logits(kr));
+    finish(j, logits());
   };
   TableSlice ts;
   ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
-  u32x4 ka[KSTEPS], va[NLDV], kb[KSTEPS], vb[NLDV];
+  u32x4 ka[NLDV], va[NLDV], kb[NLDV], vb[NLDV];
   {
     const int p0 = ts.get(j0);
     load_k(p0, ka);
     load_v(p0, va);
   }
-  auto fetch = [&](int jj, u32x4 (&kr)[KSTEPS], u32x4 (&vr)[NLDV]) {
+  auto fetch = [&](int jj, u32x4 (&kr)[NLDV], u32x4 (&vr)[NLDV]) {
     const int p = ts.get(jj);
     load_k(p, kr);
     load_v(p, vr);
