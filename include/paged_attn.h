@@ -11,7 +11,7 @@
  *        Language Model Serving with PagedAttention (2023)" (aishastr.live)
  *   [P3] the 10100.com article on the retirement of vLLM's PagedAttention kernel
  *
- * Conventions for the device calls (pa_write_kv, pa_decode):
+ * Conventions for the device calls (pa_write_kv, pa_copy_blocks, pa_decode):
  *   - every pointer is device memory owned by the caller, every tensor is contiguous
  *     row-major with the shape written beside it;
  *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream);
@@ -112,6 +112,34 @@ pa_status pa_bm_stats(const pa_block_manager* bm, int32_t* refcounts, int32_t* n
 pa_status pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int32_t capacity,
                           int32_t* count);
 
+/* Fork ([P1] sec. 5 "Parallel Sampling"): create n sequences that share every block of the
+ * live sequence `parent` (each shared block gains n references) and have its length.
+ * child_handles: host out [n]. */
+pa_status pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t n, int32_t* child_handles);
+
+/* Reserve the slot of the next token of each sequence, in the order given ([P1] sec. 4
+ * "Decoding Step" / "Block Overflow"; sec. 5 copy-on-write).  For a sequence of length L:
+ *   - L % B == 0: the token opens a new block, taken from the front of the free list;
+ *   - otherwise, if the last block is shared (reference count > 1): copy-on-write -- a new
+ *     block is taken, the pair (shared id, new id) is recorded for pa_copy_blocks, the
+ *     shared block loses one reference and the sequence's table points at the new block;
+ *   - the length becomes L + 1.
+ * slot_blocks / slot_offsets: host out [n], where the token goes (the block id and slot to
+ * hand to pa_write_kv via the updated table and position L).  copies: host out
+ * [max_copies][2]; *num_copies receives the number of pairs.  All-or-nothing: if the free
+ * list is too short (PA_ERR_NO_BLOCKS), max_copies too small or a handle not live
+ * (PA_ERR_INVALID_ARG), nothing changes.  The copies must run (pa_copy_blocks) before the
+ * new tokens are written. */
+pa_status pa_bm_append(pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
+                       int32_t* slot_blocks, int32_t* slot_offsets, int32_t* copies,
+                       int32_t max_copies, int32_t* num_copies);
+
+/* Current table rows and lengths of live sequences: block_tables host out
+ * [n, max_blocks_per_seq] (-1 padded), context_lens host out [n] (may be NULL).
+ * PA_ERR_TABLE_OVERFLOW if a row does not fit. */
+pa_status pa_bm_table(const pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
+                      int32_t max_blocks_per_seq, int32_t* block_tables, int32_t* context_lens);
+
 /* ------------------------------------------------------------------------------------
  * KV write: [P1] sec. 7 "Fused Reshape and Block Write" and sec. 4 "Decoding Step".
  * Token t (sequence seq_ids[t], position positions[t]) is stored in block
@@ -133,6 +161,18 @@ pa_status pa_write_kv(const void* k_src, const void* v_src, void* k_cache, void*
                       int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, pa_dtype src_dtype, pa_dtype cache_dtype,
                       float k_inv_scale, float v_inv_scale, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Batched block copy: [P1] sec. 7 "Batched Block Copy-on-Write" -- all copy-on-write
+ * duplications of a step in one launch.  block_pairs: device [num_pairs][2] int32 of
+ * (src, dst) physical ids (as produced by pa_bm_append); block dst of both pools receives
+ * block src, all KV heads.  Pairs naming an id outside [0, num_blocks) are skipped; a dst
+ * that is also a src of the same call races.  Any head_dim/block_size whose block is a
+ * multiple of 16 bytes. */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t block_size, int32_t head_dim, pa_dtype cache_dtype,
+                         void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Decode attention.

@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = [
     "F16", "BF16", "FP8_E4M3", "DECODE_SHARED_KV", "PagedAttnError", "LibraryNotBuilt", "lib", "library_path",
-    "BlockManager", "write_kv", "decode", "decode_plan", "decode_workspace_size",
+    "BlockManager", "write_kv", "copy_blocks", "decode", "decode_plan", "decode_workspace_size",
     "kv_bytes_per_token", "version",
 ]
 
@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
     L.pa_bm_free.argtypes = [vp, i32, vp]
     L.pa_bm_stats.argtypes = [vp, vp, vp, vp]
     L.pa_bm_free_list.argtypes = [vp, vp, i32, vp]
+    L.pa_bm_fork.argtypes = [vp, i32, i32, vp]
+    L.pa_bm_append.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp]
+    L.pa_bm_table.argtypes = [vp, i32, vp, i32, vp, vp]
+    L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, c.c_int, vp]
     L.pa_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32,
                               c.c_int, c.c_int, f32, f32, vp]
     L.pa_decode_workspace_size.argtypes = [i32] * 7
@@ -75,7 +79,8 @@ def lib() -> ctypes.CDLL:
     L.pa_kv_bytes_per_token.argtypes = [i32, i32, i32, c.c_int]
     L.pa_kv_bytes_per_token.restype = c.c_uint64
     for name in ("pa_bm_create", "pa_alloc_tables", "pa_bm_free", "pa_bm_stats",
-                 "pa_bm_free_list", "pa_write_kv", "pa_decode_plan", "pa_decode"):
+                 "pa_bm_free_list", "pa_bm_fork", "pa_bm_append", "pa_bm_table",
+                 "pa_copy_blocks", "pa_write_kv", "pa_decode_plan", "pa_decode"):
         getattr(L, name).restype = c.c_int
     _lib = L
     return L
@@ -152,6 +157,33 @@ class BlockManager:
         _check(lib().pa_bm_free_list(self._h, _ptr(out), self.num_blocks, _ptr(cnt)))
         return out[: cnt[0]].copy()
 
+    def fork(self, parent: int, n: int) -> np.ndarray:
+        """n new sequences sharing every block of `parent`; returns their handles."""
+        out = np.empty(int(n), np.int32)
+        _check(lib().pa_bm_fork(self._h, int(parent), int(n), _ptr(out)))
+        return out
+
+    def append(self, seq_handles):
+        """Reserve each sequence's next slot.  Returns (slot_blocks, slot_offsets,
+        copies [k, 2]) where copies are the copy-on-write pairs for copy_blocks()."""
+        h = _np(seq_handles)
+        blocks = np.empty(h.size, np.int32)
+        offs = np.empty(h.size, np.int32)
+        copies = np.empty((max(h.size, 1), 2), np.int32)
+        nc = np.zeros(1, np.int32)
+        _check(lib().pa_bm_append(self._h, h.size, _ptr(h), _ptr(blocks), _ptr(offs),
+                                  _ptr(copies), copies.shape[0], _ptr(nc)))
+        return blocks, offs, copies[: nc[0]].copy()
+
+    def table(self, seq_handles, max_blocks_per_seq: int):
+        """(block_tables [n, MB], context_lens [n]) of live sequences."""
+        h = _np(seq_handles)
+        t = np.empty((h.size, int(max_blocks_per_seq)), np.int32)
+        lens = np.empty(h.size, np.int32)
+        _check(lib().pa_bm_table(self._h, h.size, _ptr(h), int(max_blocks_per_seq), _ptr(t),
+                                 _ptr(lens)))
+        return t, lens
+
 
 # ------------------------------------------------------------------ device ops
 def _torch():
@@ -199,6 +231,19 @@ def write_kv(k_src, v_src, k_cache, v_cache, block_tables, seq_ids, positions,
                              _dev(seq_ids, "seq_ids"), _dev(positions, "positions"), T, NB,
                              Hkv, D, B, _dtype_code(k_src), _dtype_code(k_cache),
                              float(k_inv_scale), float(v_inv_scale), _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """pa_copy_blocks: block_pairs is a device int32 tensor [k, 2] of (src, dst) ids."""
+    NB, Hkv, B, D = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("copy_blocks: shape mismatch")
+    n = block_pairs.shape[0]
+    if n == 0:
+        return
+    _check(lib().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                _dev(block_pairs, "block_pairs"), n, NB, Hkv, B, D,
+                                _dtype_code(k_cache), _stream(stream)))
 
 
 def decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpaged_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "block_manager.cpp", "write_kv.hip", "merge.hip",
+SOURCES = ["api.hip", "block_manager.cpp", "write_kv.hip", "merge.hip", "copy_blocks.hip",
            "decode_d64_nt.hip", "decode_d64_t.hip", "decode_d128_nt.hip", "decode_d128_t.hip", "decode_gqa.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

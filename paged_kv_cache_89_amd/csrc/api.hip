@@ -142,6 +142,24 @@ pa_status pa_write_kv(const void* k_src, const void* v_src, void* k_cache, void*
                     "pa_write_kv launch");
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t block_size, int32_t head_dim, pa_dtype cache_dtype,
+                         void* stream) {
+  g_last_error.clear();
+  int ck;
+  if (!dtype_kind(cache_dtype, &ck)) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: unknown dtype");
+  if (num_pairs < 0 || num_blocks < 1 || num_kv_heads < 1 || block_size < 1 || head_dim < 1)
+    return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: bad size");
+  const int64_t bytes = (int64_t)num_kv_heads * block_size * head_dim * (ck == KIND_E4M3 ? 1 : 2);
+  if (bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block size in bytes must be a multiple of 16");
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: NULL pointer");
+  CopyArgs a{k_cache, v_cache, block_pairs, num_pairs, num_blocks, bytes};
+  return hip_status(launch_copy_blocks(a, (hipStream_t)stream), "pa_copy_blocks launch");
+}
+
 pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t max_context_len,
                          int32_t partition_size, int32_t* used_partition_size,

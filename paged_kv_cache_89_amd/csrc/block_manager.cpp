@@ -216,4 +216,136 @@ pa_status pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int32_t capa
   return PA_OK;
 }
 
+pa_status pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t n, int32_t* child_handles) {
+  if (!bm || n < 0 || (n > 0 && !child_handles) || parent < 0 ||
+      parent >= (int32_t)bm->seqs.size() || !bm->seqs[parent].live) {
+    pa_set_error("pa_bm_fork: invalid arguments or parent is not a live sequence");
+    return PA_ERR_INVALID_ARG;
+  }
+  for (int32_t k = 0; k < n; ++k) {
+    pa_block_manager::Seq child;
+    child.blocks = bm->seqs[parent].blocks;  // copied before push_back may reallocate
+    child.context_len = bm->seqs[parent].context_len;
+    child.live = true;
+    for (int32_t id : child.blocks) bm->refs[id] += 1;
+    child_handles[k] = (int32_t)bm->seqs.size();
+    bm->seqs.push_back(std::move(child));
+  }
+  return PA_OK;
+}
+
+pa_status pa_bm_append(pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
+                       int32_t* slot_blocks, int32_t* slot_offsets, int32_t* copies,
+                       int32_t max_copies, int32_t* num_copies) {
+  if (!bm || n < 0 || max_copies < 0 || !num_copies ||
+      (n > 0 && (!seq_handles || !slot_blocks || !slot_offsets)) || (max_copies > 0 && !copies)) {
+    pa_set_error("pa_bm_append: invalid arguments");
+    return PA_ERR_INVALID_ARG;
+  }
+  const int32_t B = bm->block_size;
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t h = seq_handles[k];
+    if (h < 0 || h >= (int32_t)bm->seqs.size() || !bm->seqs[h].live) {
+      pa_set_error("pa_bm_append: handle " + std::to_string(h) + " is not a live sequence");
+      return PA_ERR_INVALID_ARG;
+    }
+  }
+  // Dry run: count new blocks and copies without touching the manager.  Appends are
+  // applied in order, so a block shared by two sequences of the same call is copied only
+  // for the first of them (the second then holds the last reference).
+  std::vector<int32_t> ref_delta;   // sparse: block ids whose count dropped in the dry run
+  std::vector<int32_t> len(n), fresh_tail(n, 0);
+  auto dry_ref = [&](int32_t id) {
+    int32_t r = bm->refs[id];
+    for (int32_t x : ref_delta) r -= (x == id);
+    return r;
+  };
+  int64_t need = 0, ncopy = 0;
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t h = seq_handles[k];
+    int32_t cur = bm->seqs[h].context_len;
+    bool tail_private = false;  // this call already gave the sequence a private tail block
+    for (int32_t q = 0; q < k; ++q)
+      if (seq_handles[q] == h) {
+        cur += 1;
+        tail_private = tail_private || fresh_tail[q];
+      }
+    if (cur % B == 0) {
+      need += 1;
+      fresh_tail[k] = 1;
+    } else if (!tail_private) {
+      const int32_t last = bm->seqs[h].blocks[cur / B];
+      if (dry_ref(last) > 1) {
+        need += 1;
+        ncopy += 1;
+        ref_delta.push_back(last);
+        fresh_tail[k] = 1;
+      }
+    } else {
+      fresh_tail[k] = 1;
+    }
+  }
+  if (need > bm->free_count) {
+    pa_set_error("pa_bm_append: need " + std::to_string(need) + " blocks, " +
+                 std::to_string(bm->free_count) + " free");
+    return PA_ERR_NO_BLOCKS;
+  }
+  if (ncopy > max_copies) {
+    pa_set_error("pa_bm_append: " + std::to_string(ncopy) + " block copies exceed max_copies");
+    return PA_ERR_INVALID_ARG;
+  }
+  // Commit.
+  int32_t nc = 0;
+  for (int32_t k = 0; k < n; ++k) {
+    auto& seq = bm->seqs[seq_handles[k]];
+    const int32_t j = seq.context_len / B, off = seq.context_len % B;
+    if (off == 0) {  // overflow: the token opens a new block
+      const int32_t id = bm->pop_front();
+      bm->refs[id] = 1;
+      seq.blocks.push_back(id);
+    } else if (bm->refs[seq.blocks[j]] > 1) {  // copy-on-write of a shared partial block
+      const int32_t src = seq.blocks[j];
+      const int32_t id = bm->pop_front();
+      bm->refs[src] -= 1;
+      bm->refs[id] = 1;
+      seq.blocks[j] = id;
+      copies[2 * nc] = src;
+      copies[2 * nc + 1] = id;
+      ++nc;
+    }
+    slot_blocks[k] = seq.blocks[j];
+    slot_offsets[k] = off;
+    seq.context_len += 1;
+  }
+  *num_copies = nc;
+  return PA_OK;
+}
+
+pa_status pa_bm_table(const pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
+                      int32_t max_blocks_per_seq, int32_t* block_tables, int32_t* context_lens) {
+  if (!bm || n < 0 || max_blocks_per_seq < 1 || (n > 0 && (!seq_handles || !block_tables))) {
+    pa_set_error("pa_bm_table: invalid arguments");
+    return PA_ERR_INVALID_ARG;
+  }
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t h = seq_handles[k];
+    if (h < 0 || h >= (int32_t)bm->seqs.size() || !bm->seqs[h].live) {
+      pa_set_error("pa_bm_table: handle " + std::to_string(h) + " is not a live sequence");
+      return PA_ERR_INVALID_ARG;
+    }
+    if ((int32_t)bm->seqs[h].blocks.size() > max_blocks_per_seq) {
+      pa_set_error("pa_bm_table: sequence needs more than max_blocks_per_seq entries");
+      return PA_ERR_TABLE_OVERFLOW;
+    }
+  }
+  for (int32_t k = 0; k < n; ++k) {
+    const auto& seq = bm->seqs[seq_handles[k]];
+    int32_t* row = block_tables + (size_t)k * max_blocks_per_seq;
+    for (int32_t j = 0; j < max_blocks_per_seq; ++j)
+      row[j] = j < (int32_t)seq.blocks.size() ? seq.blocks[j] : -1;
+    if (context_lens) context_lens[k] = seq.context_len;
+  }
+  return PA_OK;
+}
+
 }  // extern "C"

@@ -66,4 +66,13 @@ bool write_supported(int head_dim, int block_size, int src_kind, int cache_kind)
 hipError_t launch_write_kv(int head_dim, int block_size, int src_kind, int cache_kind,
                            const WriteArgs& a, hipStream_t stream);
 
+struct CopyArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* pairs;      // [num_pairs][2]: (src, dst) physical block ids
+  int32_t num_pairs, num_blocks;
+  int64_t block_bytes;       // Hkv * B * d * e, a multiple of 16
+};
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+
 }  // namespace pa
