@@ -82,19 +82,47 @@ template <> struct MfmaOps<KIND_F16> {
 
 constexpr float kLazyRescaleLog2 = 8.0f;  // weights stay <= 2^8 between reference moves
 
-// Supported: D in {64, 128}, B = 16 (one MFMA token tile per block), fp16 or bf16 Q/K/V,
+// e4m3 codes -> values of the query's 16-bit type (exact: every e4m3 value is
+// representable in bf16 and in fp16); 16 codes in, 16 values (two 16-byte chunks) out.
+template <int QK>
+__device__ __forceinline__ void e4m3x16_widen(const u32x4 src, u32x4 (&dst)[2]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float f[4];
+    e4m3x4_to_f32(src[w], f);
+    uint32_t lo, hi;
+    if constexpr (QK == KIND_BF16) {
+      lo = __builtin_bit_cast(uint16_t, (__bf16)f[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f[1]) << 16);
+      hi = __builtin_bit_cast(uint16_t, (__bf16)f[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f[3]) << 16);
+    } else {
+      lo = __builtin_bit_cast(uint16_t, (_Float16)f[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[1]) << 16);
+      hi = __builtin_bit_cast(uint16_t, (_Float16)f[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[3]) << 16);
+    }
+    dst[(2 * w) / 4][(2 * w) % 4] = lo;
+    dst[(2 * w + 1) / 4][(2 * w + 1) % 4] = hi;
+  }
+}
+
+// Supported: D in {64, 128}, B = 16 (one MFMA token tile per block), fp16 or bf16 Q with a
+// cache of the same type or e4m3 (widened to Q's type while it is staged into LDS),
 // 2 <= G <= 16.
-template <int D, int QK, int G, bool NT>
+template <int D, int QK, int KVK, int G, bool NT>
 __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
   constexpr int KSTEPS = D / 32;             // 16x16x32 steps over the head dimension
   constexpr int NTILES = D / 16;             // 16-wide output slices
-  constexpr int LPT = D / 8;                 // lanes per token row in a 16-byte-per-lane load
-  constexpr int TPL = 64 / LPT;              // token rows per 1 KiB wave load
-  constexpr int NLDV = BS / TPL;             // wave loads per V tile
-  constexpr int PITCH = D * 2;               // LDS row pitch (bytes)
+  constexpr int E = (KVK == KIND_E4M3) ? 1 : 2;  // cache bytes per element
+  constexpr int EPLS = 16 / E;               // cache elements per lane per 16-byte load
+  constexpr int LPTS = D / EPLS;             // lanes per token row of a 1 KiB wave load
+  constexpr int TPLS = 64 / LPTS;            // token rows per 1 KiB wave load
+  constexpr int STILE = BS * D * E;          // cache bytes of one (block, KV head) tile
+  constexpr int NLDS = STILE / 1024;         // wave loads per cache tile
+  constexpr int CPL = EPLS / 8;              // 16-byte LDS chunks one lane's load becomes
+  constexpr int CPR = D / 8;                 // 16-byte chunks per LDS row
+  constexpr int PITCH = D * 2;               // LDS row pitch (bytes, Q's 16-bit type)
   constexpr int RPB = 256 / PITCH;           // rows per 256-byte bank period
-  constexpr int TILE = BS * D * 2;           // bytes of one (block, KV head) tile
+  constexpr int TILE = BS * D * 2;           // LDS bytes of one tile
+  static_assert(NLDS * 1024 == STILE, "tile must be covered by whole wave loads");
   static_assert(G >= 2 && G <= 16, "group size");
   using Ops = MfmaOps<QK>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[4][TILE];
@@ -162,59 +190,56 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   float m_ref = -INFINITY;  // reference maximum of head c (log2 units), same in its 4 lanes
   float l_part = 0.f;       // this lane's share of head c's denominator
 
-  const size_t blk_stride = (size_t)a.num_kv_heads * TILE;
-  const char* kbase = (const char*)a.k + (size_t)kvh * TILE;
-  const char* vbase = (const char*)a.v + (size_t)kvh * TILE;
+  const size_t blk_stride = (size_t)a.num_kv_heads * STILE;
+  const char* kbase = (const char*)a.k + (size_t)kvh * STILE;
+  const char* vbase = (const char*)a.v + (size_t)kvh * STILE;
   const uint32_t voff = (uint32_t)lane * 16;  // natural 1 KiB wave loads (K and V)
   uint8_t* vt = lds_tiles[wave];
   uint8_t* kt = lds_ktiles[wave];
   const float qk_scale = a.qk_scale;
-  // LDS byte offsets: where this lane's V chunk of wave load i goes, and where its
-  // ds_read_b64_tr_b16 of output slice t reads (row 4r + c/4, dims 16t + 4(c%4) .. +4)
-  uint32_t vw_off[NLDV];
+  // This lane's share of a tile: wave load i, token row i*TPLS + lane/LPTS, elements
+  // (lane % LPTS) * EPLS .. +EPLS, i.e. LDS chunks (lane % LPTS) * CPL .. +CPL of that row.
+  // K's chunk x of row t sits at x ^ (t mod CPR): the A-operand reads (row c, chunk
+  // 4kk + r) of 16 lanes hit 16 different bank groups.  V's chunk x sits at x ^ swz(t).
+  uint32_t kw_off[NLDS][CPL], vw_off[NLDS][CPL];
 #pragma unroll
-  for (int i = 0; i < NLDV; ++i) {
-    const int row = i * TPL + lane / LPT;
-    vw_off[i] = row * PITCH + (((lane % LPT) ^ swz(row)) * 16);
+  for (int i = 0; i < NLDS; ++i) {
+    const int row = i * TPLS + lane / LPTS;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int chunk = (lane % LPTS) * CPL + q;
+      kw_off[i][q] = row * PITCH + ((chunk ^ (row % CPR)) * 16);
+      vw_off[i][q] = row * PITCH + ((chunk ^ swz(row)) * 16);
+    }
   }
   const int trow = 4 * r + c / 4;
 
-  auto load_k = [&](int phys, u32x4 (&kr)[NLDV]) {
-    const char* kp = kbase + (size_t)phys * blk_stride;
+  auto load_tile = [&](const char* base, int phys, u32x4 (&t)[NLDS]) {
+    const char* p = base + (size_t)phys * blk_stride;
 #pragma unroll
-    for (int i = 0; i < NLDV; ++i) {
-      if constexpr (NT) kr[i] = __builtin_nontemporal_load((const u32x4*)(kp + voff + 1024 * i));
-      else kr[i] = *(const u32x4*)(kp + voff + 1024 * i);
+    for (int i = 0; i < NLDS; ++i) {
+      if constexpr (NT) t[i] = __builtin_nontemporal_load((const u32x4*)(p + voff + 1024 * i));
+      else t[i] = *(const u32x4*)(p + voff + 1024 * i);
     }
   };
-  // K rows into their LDS tile: 16-byte chunk x of row t sits at chunk x ^ (t mod LPT), so
-  // the A-operand reads (row c, chunk 4kk + r) of 16 lanes hit 16 different bank groups
-  uint32_t kw_off[NLDV];
+  // widen (e4m3) and write one tile into LDS; rows at or beyond n become zeros when
+  // `mask` (their bytes may be NaN and the matrix core would turn 0 * NaN into NaN)
+  auto stage = [&](uint8_t* dst, const uint32_t (&off)[NLDS][CPL], bool mask, int j,
+                   const u32x4 (&t)[NLDS]) {
 #pragma unroll
-  for (int i = 0; i < NLDV; ++i) {
-    const int row = i * TPL + lane / LPT;
-    kw_off[i] = row * PITCH + (((lane % LPT) ^ (row % LPT)) * 16);
-  }
-  auto stage_k = [&](const u32x4 (&kr)[NLDV]) {
+    for (int i = 0; i < NLDS; ++i) {
+      u32x4 w[CPL];
+      if constexpr (KVK == KIND_E4M3) {
+        u32x4 two[2];
+        e4m3x16_widen<QK>(t[i], two);
+        w[0] = two[0];
+        w[CPL - 1] = two[1];
+      } else {
+        w[0] = t[i];
+      }
+      const bool dead = mask && j * BS + i * TPLS + lane / LPTS >= n;
 #pragma unroll
-    for (int i = 0; i < NLDV; ++i) *(u32x4*)(kt + kw_off[i]) = kr[i];
-  };
-  auto load_v = [&](int phys, u32x4 (&vr)[NLDV]) {
-    const char* vp = vbase + (size_t)phys * blk_stride;
-#pragma unroll
-    for (int i = 0; i < NLDV; ++i) {
-      if constexpr (NT) vr[i] = __builtin_nontemporal_load((const u32x4*)(vp + voff + 1024 * i));
-      else vr[i] = *(const u32x4*)(vp + voff + 1024 * i);
-    }
-  };
-  // V rows into LDS; slots at or beyond n become zeros (their bytes may be NaN and the
-  // matrix core would turn 0 * NaN into NaN)
-  auto stage_v = [&](bool mask, int j, const u32x4 (&vr)[NLDV]) {
-#pragma unroll
-    for (int i = 0; i < NLDV; ++i) {
-      u32x4 v = vr[i];
-      if (mask && j * BS + i * TPL + lane / LPT >= n) v = u32x4{0, 0, 0, 0};
-      *(u32x4*)(vt + vw_off[i]) = v;
+      for (int q = 0; q < CPL; ++q) *(u32x4*)(dst + off[i][q]) = dead ? u32x4{0, 0, 0, 0} : w[q];
     }
   };
 
@@ -223,7 +248,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int chunk = (4 * kk + r) ^ (c % LPT);
+      const int chunk = (4 * kk + r) ^ (c % CPR);
       const u32x4 kop = *(const u32x4*)(kt + c * PITCH + chunk * 16);
       sc = Ops::qk(kop, qop[kk], sc);
     }
@@ -275,24 +300,20 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   // register sets each, as in the vector kernel); consuming block j moves V(j) into the
   // LDS tile, runs the logit contraction on K(j), the softmax update and P . V.  The mask
   // of slots >= n is applied branch-free (it only bites in a unit's last block).
-  auto process = [&](int j, const u32x4 (&kr)[NLDV], const u32x4 (&vr)[NLDV]) {
-    stage_k(kr);
-    stage_v(true, j, vr);
+  auto process = [&](int j, const u32x4 (&kr)[NLDS], const u32x4 (&vr)[NLDS]) {
+    stage(kt, kw_off, false, j, kr);
+    stage(vt, vw_off, true, j, vr);
     finish(j, logits());
   };
   TableSlice ts;
   ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
-  u32x4 ka[NLDV], va[NLDV], kb[NLDV], vb[NLDV];
-  {
-    const int p0 = ts.get(j0);
-    load_k(p0, ka);
-    load_v(p0, va);
-  }
-  auto fetch = [&](int jj, u32x4 (&kr)[NLDV], u32x4 (&vr)[NLDV]) {
+  u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
+  auto fetch = [&](int jj, u32x4 (&kr)[NLDS], u32x4 (&vr)[NLDS]) {
     const int p = ts.get(jj);
-    load_k(p, kr);
-    load_v(p, vr);
+    load_tile(kbase, p, kr);
+    load_tile(vbase, p, vr);
   };
+  fetch(j0, ka, va);
   // steady state: every load in the loop is unconditional (see the vector kernel)
   int j = j0;
   while (j + 2 < j1) {
@@ -325,7 +346,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
         uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + h) * D + c;
 #pragma unroll
         for (int t = 0; t < NTILES; ++t)
-          o[16 * t] = f32_to_store<QK>(cacc[t][i] / Li);
+          o[16 * t] = f32_to_store<QK>(cacc[t][i] / Li * a.v_scale);
       } else {
         const size_t pi = ((size_t)s * a.num_heads + h) * a.num_parts + part;
         float* pa_ = a.part_acc + pi * D + c;
@@ -340,24 +361,26 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   }
 }
 
-template <int D, int QK, int G, bool NT>
+template <int D, int QK, int KVK, int G, bool NT>
 hipError_t launch_gqa_mfma_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((a.num_units + 3) / 4);
-  hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, G, NT>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, bool NT>
 hipError_t launch_gqa_mfma_d(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream) {
-#define PA_GQ(QK)                                                     \
-  switch (s.group) {                                                  \
-    case 2: return launch_gqa_mfma_t<D, QK, 2, NT>(a, stream);        \
-    case 4: return launch_gqa_mfma_t<D, QK, 4, NT>(a, stream);        \
-    case 8: return launch_gqa_mfma_t<D, QK, 8, NT>(a, stream);        \
-    default: return hipErrorInvalidValue;                             \
+#define PA_GQ(QK, KVK)                                                     \
+  switch (s.group) {                                                       \
+    case 2: return launch_gqa_mfma_t<D, QK, KVK, 2, NT>(a, stream);        \
+    case 4: return launch_gqa_mfma_t<D, QK, KVK, 4, NT>(a, stream);        \
+    case 8: return launch_gqa_mfma_t<D, QK, KVK, 8, NT>(a, stream);        \
+    default: return hipErrorInvalidValue;                                  \
   }
-  if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_BF16) { PA_GQ(KIND_BF16) }
-  if (s.q_kind == KIND_F16 && s.kv_kind == KIND_F16) { PA_GQ(KIND_F16) }
+  if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_BF16) { PA_GQ(KIND_BF16, KIND_BF16) }
+  if (s.q_kind == KIND_F16 && s.kv_kind == KIND_F16) { PA_GQ(KIND_F16, KIND_F16) }
+  if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_E4M3) { PA_GQ(KIND_BF16, KIND_E4M3) }
+  if (s.q_kind == KIND_F16 && s.kv_kind == KIND_E4M3) { PA_GQ(KIND_F16, KIND_E4M3) }
   return hipErrorInvalidValue;
 #undef PA_GQ
 }
