@@ -29,16 +29,18 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 COUNTER_SOURCES = os.path.join(ROOT, "paged_kv_cache_89_amd", "csrc")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per pa_decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary of this workload, or None when there is none or the kernel sources changed
-    since the counters were taken."""
+def measured_traffic(workload: str, decode_path: str):
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this workload, or None when there is none, it was taken on the other decode
+    path, or the kernel sources changed since the counters were taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"decode_counters_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if rec.get("decode_path", "plain") != decode_path:
+        return None
     h = hashlib.sha256()
     for f in rec["kernel_sources"]:
         h.update(open(os.path.join(COUNTER_SOURCES, f), "rb").read())
@@ -57,6 +59,9 @@ def parse():
                     help="-1: the workload's setting (0 = library choice)")
     ap.add_argument("--decode-flags", type=int, default=-1,
                     help="-1: the workload's setting (PA_DECODE_SHARED_KV for shared prompts)")
+    ap.add_argument("--decode-path", choices=["auto", "plain", "shared_prefix"], default="auto",
+                    help="auto: the shared-prefix (cascade) decode for workloads whose "
+                         "sequences share prompt blocks, else the plain decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -112,15 +117,40 @@ def main():
         pa.write_kv(k_new, v_new, kc, vc, tables_d, seq_ids, positions, k_inv, v_inv,
                     stream=stream)
 
-    flags = pa.DECODE_SHARED_KV if sp.group_size else 0  # shared prompt blocks
+    path = args.decode_path
+    if path == "auto":
+        path = "shared_prefix" if sp.group_size else "plain"
+    # the plain decode over shared prompt blocks keeps them cacheable; the shared-prefix
+    # decode reads each of them once and streams everything
+    flags = pa.DECODE_SHARED_KV if sp.group_size and path == "plain" else 0
     if args.decode_flags >= 0:
         flags = args.decode_flags
+    kv_bytes = workloads.kv_bytes(sp, ctx)  # K+V bytes of every sequence's own context
+    unique_bytes = kv_bytes                 # K+V bytes one decode pass must read
+    kernels = "paged_decode_kernel" + (" + merge_partitions_kernel" if nparts > 1 else "")
+    if path == "shared_prefix":
+        if not sp.group_size:
+            raise SystemExit("--decode-path shared_prefix needs a workload with shared prompts")
+        prefix_blocks = (pl // B).astype(np.int32)
+        max_pb = int(prefix_blocks.max())
+        pb_d = torch.from_numpy(prefix_blocks).cuda()
+        ws_bytes = pa.decode_shared_prefix_workspace_size(S, Hq, Hkv, D, B, max_ctx, max_pb, P)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        # a group's shared tokens are read once, every sequence's remaining tokens once
+        shared_tok = np.minimum(prefix_blocks * B, ctx.reshape(-1, sp.group_size).max(axis=1))
+        own = ctx - np.minimum(np.repeat(prefix_blocks * B, sp.group_size), ctx)
+        unique_bytes = workloads.kv_bytes(sp, np.concatenate([shared_tok, own]))
+        kernels = ("paged_decode_gqa_mfma_kernel (group prefixes) + paged_decode_kernel "
+                   "(own tokens) + merge_partitions_kernel")
 
-    def decode():
-        pa.decode(q, kc, vc, tables_d, ctx_d, max_ctx, sp.scale, k_scale, v_scale,
-                  partition_size=P, flags=flags, out=out, workspace=ws, stream=stream)
-
-    kv_bytes = workloads.kv_bytes(sp, ctx)  # algorithmic K+V bytes one decode pass reads
+        def decode():
+            pa.decode_shared_prefix(q, kc, vc, tables_d, ctx_d, pb_d, sp.group_size, max_ctx,
+                                    max_pb, sp.scale, k_scale, v_scale, partition_size=P,
+                                    flags=flags, out=out, workspace=ws, stream=stream)
+    else:
+        def decode():
+            pa.decode(q, kc, vc, tables_d, ctx_d, max_ctx, sp.scale, k_scale, v_scale,
+                      partition_size=P, flags=flags, out=out, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         write()
@@ -143,7 +173,7 @@ def main():
     dec_ms = [a.elapsed_time(b) for a, b in ev]
     dec_ms_mean = float(np.mean(dec_ms))
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = kv_bytes / (dec_ms_mean * 1e-3) / 1e9
+    achieved = unique_bytes / (dec_ms_mean * 1e-3) / 1e9
 
     if args.copy_calibration:
         # A plain device copy of known size: the hardware-counter runs scale FETCH_SIZE /
@@ -178,13 +208,15 @@ def main():
             "head_dim": D, "block_size": B, "context_lens": f"U[{sp.ctx_lo},{sp.ctx_hi}]"
             + (f"+{sp.prompt_len}" if sp.prompt_len else ""), "num_blocks": sp.num_blocks,
             "q_dtype": sp.q_dtype, "kv_dtype": sp.kv_dtype, "partition_size": used_P,
-            "num_partitions": nparts, "kv_bytes_per_step": kv_bytes, "seed": seed,
-            "decode_flags": flags,
+            "num_partitions": nparts, "kv_bytes_per_step": kv_bytes,
+            "unique_kv_bytes_per_step": unique_bytes, "seed": seed,
+            "decode_flags": flags, "decode_path": path,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(sp.name),
-            "kernel": "paged_decode_kernel" + (" + merge_partitions_kernel" if nparts > 1 else ""),
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(sp.name, path),
+            "kernel": kernels,
             "mean_launch_ms": round(dec_ms_mean, 5),
             "median_launch_ms": round(float(np.median(dec_ms)), 5),
         },

@@ -11,7 +11,7 @@
  *        Language Model Serving with PagedAttention (2023)" (aishastr.live)
  *   [P3] the 10100.com article on the retirement of vLLM's PagedAttention kernel
  *
- * Conventions for the device calls (pa_write_kv, pa_copy_blocks, pa_decode):
+ * Conventions for the device calls (pa_write_kv, pa_copy_blocks, pa_decode*):
  *   - every pointer is device memory owned by the caller, every tensor is contiguous
  *     row-major with the shape written beside it;
  *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream);
@@ -227,6 +227,55 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
                     int32_t partition_size, uint32_t flags, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Shared-prefix (cascade) decode.  Same result as pa_decode (the attention definition of
+ * [P1] sec. 3) for batches in which groups of sequences share their leading blocks: the
+ * K samples of one prompt ([P1] sec. 5, parallel sampling) or the sessions behind one
+ * pinned system prompt ([P1] sec. 5, prefix sharing).  The shared blocks are read from HBM
+ * once per group: one launch attends the queries of all members to the group's prefix
+ * (the member queries become the columns of one matrix-core contraction per block), a
+ * second attends every sequence to its own remaining tokens, and the partial (max, sum,
+ * output) triples are combined by the log-sum-exp merge (the rescaling of [P1] sec. 7).
+ *   Arguments as for pa_decode, plus:
+ *   seq_group      sequences per group; the batch is num_seqs / seq_group groups of
+ *                  consecutive sequences (group g = sequences g*seq_group .. +seq_group-1)
+ *   prefix_blocks  device [num_seqs / seq_group] int32: blocks shared by the group's
+ *                  members.  Precondition: the first prefix_blocks[g] entries of the
+ *                  members' table rows are the same physical ids; the prefix launch reads
+ *                  the first member's row only, so a violation gives that member's blocks
+ *                  to every member (wrong numbers, no fault).  Values are clamped to
+ *                  [0, max_prefix_blocks]; a member shorter than the prefix attends its
+ *                  own n tokens of it, so any value gives the pa_decode result when the
+ *                  precondition holds.
+ *   max_prefix_blocks  host upper bound of prefix_blocks (sizes the prefix grid)
+ *   flags          0, or PA_DECODE_SHARED_KV when blocks after the group prefixes are still
+ *                  shared (e.g. between beams): the per-sequence launch then keeps its K/V
+ *                  loads cacheable.  The prefix launch always streams (it reads each shared
+ *                  block once).  Results are identical either way.
+ *   workspace      at least pa_decode_shared_prefix_workspace_size(...) bytes (never 0
+ *                  for num_seqs > 0: the two launches always leave partials)
+ * Supported: what the matrix-core decode covers for the group's queries: block_size 16,
+ * head_dim in {64, 128}, (num_heads / num_kv_heads) * seq_group in {2, 4, 8, 16}, q in
+ * {f16, bf16} with a cache of the same type or e4m3; the per-sequence launch then follows
+ * pa_decode's support.  Other shapes return PA_ERR_UNSUPPORTED (use pa_decode). */
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t block_size, int32_t max_context_len,
+                                              int32_t max_prefix_blocks,
+                                              int32_t partition_size);
+
+pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* prefix_blocks,
+                                  int32_t num_seqs, int32_t seq_group, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int32_t num_blocks,
+                                  int32_t max_context_len, int32_t max_prefix_blocks,
+                                  float scale, pa_dtype q_dtype, pa_dtype kv_dtype,
+                                  float k_scale, float v_scale, int32_t partition_size,
+                                  uint32_t flags, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Footprint: [P1] sec. 1 "KV Cache Memory Footprint" — a token stores one key and one

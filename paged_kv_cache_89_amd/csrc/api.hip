@@ -1,6 +1,7 @@
 // C-ABI layer of libpaged_attn: argument checks, launch planning, error reporting.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -92,6 +93,43 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
 size_t workspace_bytes(const Plan& p, int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
   if (p.num_parts <= 1) return 0;
   const size_t rows = (size_t)num_seqs * num_heads * p.num_parts;
+  return rows * head_dim * sizeof(float) + rows * 2 * sizeof(float);
+}
+
+// Shared-prefix decode: one partition length P for both launches (pa_decode's choice,
+// or the whole context up to the 64-block cap when that choice is "no split"); the prefix
+// launch owns slots [0, pre_parts) of every row, the per-sequence launch the next
+// suf_parts.  Both counts come from host bounds, so some slots stay empty.
+struct CascadePlan {
+  int32_t partition_size, pre_parts, suf_parts;
+};
+
+pa_status make_cascade_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                            int32_t max_prefix_blocks, int32_t partition_size,
+                            CascadePlan* cp) {
+  if (max_prefix_blocks < 0) return fail(PA_ERR_INVALID_ARG, "shared-prefix plan: max_prefix_blocks < 0");
+  Plan p;
+  const pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                 max_context_len, partition_size, &p);
+  if (st != PA_OK) return st;
+  int64_t P = p.partition_size;
+  if (P == 0) {
+    const int64_t cap = (int64_t)kMaxUnitBlocks * block_size;
+    const int64_t whole = ((int64_t)(max_context_len > 0 ? max_context_len : 1) + block_size - 1) /
+                          block_size * block_size;
+    P = whole < cap ? whole : cap;
+  }
+  const int64_t pre_tokens = std::min<int64_t>((int64_t)max_prefix_blocks * block_size, max_context_len);
+  cp->partition_size = (int32_t)P;
+  cp->pre_parts = (int32_t)((pre_tokens + P - 1) / P);
+  cp->suf_parts = (int32_t)std::max<int64_t>(1, (max_context_len + P - 1) / P);
+  return PA_OK;
+}
+
+size_t cascade_workspace_bytes(const CascadePlan& cp, int32_t num_seqs, int32_t num_heads,
+                               int32_t head_dim) {
+  const size_t rows = (size_t)num_seqs * num_heads * (cp.pre_parts + cp.suf_parts);
   return rows * head_dim * sizeof(float) + rows * 2 * sizeof(float);
 }
 
@@ -250,6 +288,10 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   a.v_scale = f8 ? v_scale : 1.0f;
   a.seq_fastest = shared ? 1 : 0;
   a.xcd_remap = 1;
+  a.num_slots = plan.num_parts > 1 ? plan.num_parts : 0;
+  a.slot_base = 0;
+  a.mode = MODE_PLAIN;
+  a.seq_group = 1; a.num_groups = num_seqs; a.max_prefix_blocks = 0; a.prefix_blocks = nullptr;
   if (log_enabled())
     std::fprintf(stderr, "[paged_attn] decode S=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d P=%d parts=%d units=%lld\n",
                  num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
@@ -260,8 +302,126 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
   m.num_seqs = num_seqs; m.num_heads = num_heads; m.num_parts = plan.num_parts;
   m.partition_size = plan.partition_size; m.max_ctx = max_ctx;
-  m.v_scale = a.v_scale;
+  m.v_scale = a.v_scale; m.all_slots = 0;
   return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream), "pa_decode merge launch");
+}
+
+size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t block_size, int32_t max_context_len,
+                                              int32_t max_prefix_blocks,
+                                              int32_t partition_size) {
+  CascadePlan cp;
+  if (make_cascade_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_context_len, max_prefix_blocks, partition_size, &cp) != PA_OK)
+    return 0;
+  return cascade_workspace_bytes(cp, num_seqs, num_heads, head_dim);
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* prefix_blocks,
+                                  int32_t num_seqs, int32_t seq_group, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int32_t num_blocks,
+                                  int32_t max_context_len, int32_t max_prefix_blocks,
+                                  float scale, pa_dtype q_dtype, pa_dtype kv_dtype,
+                                  float k_scale, float v_scale, int32_t partition_size,
+                                  uint32_t flags, void* workspace,
+                                  size_t workspace_bytes_given, void* stream) {
+  g_last_error.clear();
+  const char* who = "pa_decode_shared_prefix";
+  int qk, kk;
+  if (!dtype_kind(q_dtype, &qk) || !dtype_kind(kv_dtype, &kk))
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": unknown dtype");
+  if (num_seqs < 0 || seq_group < 1 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      block_size < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0 ||
+      max_prefix_blocks < 0 || partition_size < 0)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": bad size");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": num_heads must be a multiple of num_kv_heads");
+  if (num_seqs % seq_group != 0)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": num_seqs must be a multiple of seq_group");
+  if (partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": partition_size must be a multiple of block_size");
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": non-finite scale");
+  if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": unknown flag bits");
+  const bool shared = (flags & PA_DECODE_SHARED_KV) != 0;
+  const int32_t G = num_heads / num_kv_heads;
+  const int64_t vgroup = (int64_t)G * seq_group;
+  // The prefix launch: one matrix-core unit holds every member's G heads.
+  DecodeShape pre_shape{head_dim, block_size, qk, kk, (int)std::min<int64_t>(vgroup, 1 << 20), true};
+  DecodeShape suf_shape{head_dim, block_size, qk, kk, G, !shared};
+  if (!gqa_mfma_supported(pre_shape) || !decode_supported(suf_shape))
+    return fail(PA_ERR_UNSUPPORTED, std::string(who) +
+                ": needs block_size 16, head_dim 64/128, fp16/bf16 queries and "
+                "(num_heads/num_kv_heads)*seq_group in {2,4,8,16}");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens ||
+      (max_prefix_blocks > 0 && !prefix_blocks))
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": NULL pointer");
+
+  const int64_t reach = (int64_t)max_blocks_per_seq * block_size;
+  const int32_t max_ctx = (int32_t)(max_context_len < reach ? max_context_len : reach);
+  CascadePlan cp;
+  pa_status st = make_cascade_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                   max_context_len, max_prefix_blocks, partition_size, &cp);
+  if (st != PA_OK) return st;
+  const size_t need = cascade_workspace_bytes(cp, num_seqs, num_heads, head_dim);
+  if (!workspace || workspace_bytes_given < need)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": workspace needs " + std::to_string(need) +
+                                        " bytes, got " + std::to_string(workspace_bytes_given));
+  const int32_t slots = cp.pre_parts + cp.suf_parts;
+  const int32_t groups = num_seqs / seq_group;
+  const int64_t pre_units = (int64_t)groups * num_kv_heads * cp.pre_parts;
+  const int64_t suf_units = (int64_t)num_seqs * num_kv_heads * cp.suf_parts;
+  if (pre_units > (int64_t)1 << 30 || suf_units > (int64_t)1 << 30)
+    return fail(PA_ERR_UNSUPPORTED, std::string(who) + ": grid too large");
+
+  DecodeArgs a;
+  a.out = out; a.q = query; a.k = k_cache; a.v = v_cache;
+  a.tables = block_tables; a.ctx = context_lens;
+  a.part_acc = (float*)workspace;
+  a.part_ml = (float*)workspace + (size_t)num_seqs * num_heads * slots * head_dim;
+  a.num_seqs = num_seqs; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks; a.max_ctx = max_ctx;
+  a.blocks_per_part = cp.partition_size / block_size;
+  a.num_slots = slots;
+  const bool f8 = kk == KIND_E4M3;
+  a.qk_scale = scale * kLog2e * (f8 ? k_scale : 1.0f);
+  a.v_scale = f8 ? v_scale : 1.0f;
+  a.xcd_remap = 1;
+  a.seq_group = seq_group; a.num_groups = groups;
+  a.max_prefix_blocks = max_prefix_blocks;
+  a.prefix_blocks = prefix_blocks;
+  if (log_enabled())
+    std::fprintf(stderr, "[paged_attn] shared-prefix decode S=%d K=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d "
+                 "max_prefix_blocks=%d P=%d prefix_parts=%d suffix_parts=%d\n",
+                 num_seqs, seq_group, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
+                 max_prefix_blocks, cp.partition_size, cp.pre_parts, cp.suf_parts);
+  if (cp.pre_parts > 0) {
+    a.mode = MODE_PREFIX; a.slot_base = 0; a.num_parts = cp.pre_parts;
+    a.num_units = (int32_t)pre_units; a.seq_fastest = 0;
+    st = hip_status(launch_decode_gqa_mfma(pre_shape, a, (hipStream_t)stream),
+                    "pa_decode_shared_prefix prefix launch");
+    if (st != PA_OK) return st;
+  }
+  // The remaining tokens are mostly private: neighbouring units take neighbouring heads of
+  // the same blocks (contiguous lines); PA_DECODE_SHARED_KV only keeps the loads cacheable.
+  a.mode = MODE_SUFFIX; a.slot_base = cp.pre_parts; a.num_parts = cp.suf_parts;
+  a.num_units = (int32_t)suf_units; a.seq_fastest = 0;
+  st = hip_status(launch_decode(suf_shape, a, (hipStream_t)stream),
+                  "pa_decode_shared_prefix suffix launch");
+  if (st != PA_OK) return st;
+  MergeArgs m;
+  m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
+  m.num_seqs = num_seqs; m.num_heads = num_heads; m.num_parts = slots;
+  m.partition_size = cp.partition_size; m.max_ctx = max_ctx;
+  m.v_scale = a.v_scale; m.all_slots = 1;
+  return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream),
+                    "pa_decode_shared_prefix merge launch");
 }
 
 }  // extern "C"
@@ -281,8 +441,6 @@ bool decode_supported(const DecodeShape& s) {
   return s.kv_kind == s.q_kind || s.kv_kind == KIND_E4M3;
 }
 
-bool gqa_mfma_supported(const DecodeShape& s);
-hipError_t launch_decode_gqa_mfma(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
 
 // Grouped-query shapes with 16-token blocks and fp16/bf16 caches run the matrix-core
 // kernel; every other shape runs the vector kernel (which also covers e4m3 caches).

@@ -142,31 +142,57 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   }
   const int unit = wg * 4 + wave;
   if (unit >= a.num_units) return;
-  int s, kvh, part;
+  const bool prefix = a.mode == MODE_PREFIX;
+  const int rows = prefix ? a.num_groups : a.num_seqs;
+  int s, kvh, part;  // s: the sequence, or in prefix mode the group
   if (a.seq_fastest == 0) {
     kvh = unit % a.num_kv_heads;
     const int rest = unit / a.num_kv_heads;
     part = rest % a.num_parts;
     s = rest / a.num_parts;
   } else {
-    s = unit % a.num_seqs;
-    const int rest = unit / a.num_seqs;
+    s = unit % rows;
+    const int rest = unit / rows;
     kvh = rest % a.num_kv_heads;
     part = rest / a.num_kv_heads;
   }
-  const int h0 = kvh * G;
-  int n = a.ctx[s];
-  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  const int nblk = (n + BS - 1) / BS;
-  const int j0 = part * a.blocks_per_part;
-  const int j1 = min(nblk, j0 + a.blocks_per_part);
   const int r = lane >> 4;
   const int c = lane & 15;
+  // Query head c of the unit (c < G) is head hc of sequence sc.  Plain and suffix units:
+  // the G heads of sequence s that share KV head kvh.  Prefix units: head c % Gr of member
+  // c / Gr of group s (Gr = real query heads per KV head, G = seq_group * Gr).
+  const int Gr = a.num_heads / a.num_kv_heads;
+  const int sc = prefix ? s * a.seq_group + c / Gr : s;
+  const int hc = prefix ? kvh * Gr + c % Gr : kvh * G + c;
+  auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > a.max_ctx ? a.max_ctx : v); };
+  // n: tokens the unit's block range covers; nc: tokens head c attends (slot t is
+  // visible to head c iff t < nc); jb: first block of the walk.
+  int n, nc, jb = 0;
+  const int32_t* table_row;
+  if (prefix) {
+    n = 0;
+    for (int k = 0; k < a.seq_group; ++k)
+      n = max(n, prefix_tokens(a, s, BS, clamp_len(a.ctx[s * a.seq_group + k])));
+    nc = (c < G) ? prefix_tokens(a, s, BS, clamp_len(a.ctx[sc])) : 0;
+    table_row = a.tables + (size_t)s * a.seq_group * a.max_blocks;  // the group's first member
+  } else {
+    n = clamp_len(a.ctx[s]);
+    nc = (c < G) ? n : 0;
+    if (a.mode == MODE_SUFFIX) jb = (prefix_tokens(a, s / a.seq_group, BS, n) + BS - 1) / BS;
+    table_row = a.tables + (size_t)s * a.max_blocks;
+  }
+  const int nblk = (n + BS - 1) / BS;
+  const int j0 = jb + part * a.blocks_per_part;
+  const int j1 = min(nblk, j0 + a.blocks_per_part);
 
   if (j0 >= j1) {
-    if (a.num_parts == 1) {  // n == 0: zero rows
-      uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + h0) * D;
+    if (a.num_slots == 0) {  // direct output of an n == 0 sequence: zero rows
+      uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + kvh * G) * D;
       for (int e = lane; e < G * D; e += 64) o[e] = 0;
+    } else if (a.mode != MODE_PLAIN && r == 0 && c < G) {  // empty cascade slot
+      const size_t pi = ((size_t)sc * a.num_heads + hc) * a.num_slots + a.slot_base + part;
+      a.part_ml[pi * 2] = -INFINITY;
+      a.part_ml[pi * 2 + 1] = 0.f;
     }
     return;
   }
@@ -176,7 +202,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
     if (c < G)
-      qop[kk] = *(const u32x4*)((const uint16_t*)a.q + ((size_t)s * a.num_heads + h0 + c) * D +
+      qop[kk] = *(const u32x4*)((const uint16_t*)a.q + ((size_t)sc * a.num_heads + hc) * D +
                                 32 * kk + 8 * r);
     else
       qop[kk] = u32x4{0, 0, 0, 0};
@@ -256,13 +282,10 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   };
 
   // online-softmax weights and P . V for block j (MASK: the block holds slots >= n)
-  auto finish = [&](int j, f32x4 sc) {
+  auto finish = [&](int j, f32x4 sv) {
     float z[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = (c < G) && (j * BS + 4 * r + i < n);
-      z[i] = ok ? sc[i] * qk_scale : -INFINITY;
-    }
+    for (int i = 0; i < 4; ++i) z[i] = (j * BS + 4 * r + i < nc) ? sv[i] * qk_scale : -INFINITY;
     float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
@@ -306,7 +329,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
     finish(j, logits());
   };
   TableSlice ts;
-  ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
+  ts.init(table_row, j0, j1, a.num_blocks, lane);
   u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
   auto fetch = [&](int jj, u32x4 (&kr)[NLDS], u32x4 (&vr)[NLDS]) {
     const int p = ts.get(jj);
@@ -340,15 +363,15 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
     const int hh = 4 * r + i;
     const float Li = __shfl(L, hh);
     const float Mi = __shfl(m_ref, hh);
+    const int sh = __shfl(sc, hh), h = __shfl(hc, hh);  // row of query head hh
     if (hh < G) {
-      const int h = h0 + hh;
-      if (a.num_parts == 1) {
-        uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + h) * D + c;
+      if (a.num_slots == 0) {
+        uint16_t* o = (uint16_t*)a.out + ((size_t)sh * a.num_heads + h) * D + c;
 #pragma unroll
         for (int t = 0; t < NTILES; ++t)
           o[16 * t] = f32_to_store<QK>(cacc[t][i] / Li * a.v_scale);
       } else {
-        const size_t pi = ((size_t)s * a.num_heads + h) * a.num_parts + part;
+        const size_t pi = ((size_t)sh * a.num_heads + h) * a.num_slots + a.slot_base + part;
         float* pa_ = a.part_acc + pi * D + c;
 #pragma unroll
         for (int t = 0; t < NTILES; ++t) pa_[16 * t] = cacc[t][i];
@@ -375,6 +398,7 @@ hipError_t launch_gqa_mfma_d(const DecodeShape& s, const DecodeArgs& a, hipStrea
     case 2: return launch_gqa_mfma_t<D, QK, KVK, 2, NT>(a, stream);        \
     case 4: return launch_gqa_mfma_t<D, QK, KVK, 4, NT>(a, stream);        \
     case 8: return launch_gqa_mfma_t<D, QK, KVK, 8, NT>(a, stream);        \
+    case 16: return launch_gqa_mfma_t<D, QK, KVK, 16, NT>(a, stream);      \
     default: return hipErrorInvalidValue;                                  \
   }
   if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_BF16) { PA_GQ(KIND_BF16, KIND_BF16) }

@@ -104,18 +104,26 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
   int n = a.ctx[s];
   n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
   const int nblk = (n + BS - 1) / BS;
-  const int j0 = part * a.blocks_per_part;
+  // suffix of a shared-prefix group: start after the blocks the prefix units cover
+  const int jb = (a.mode == MODE_SUFFIX)
+                     ? (prefix_tokens(a, s / a.seq_group, BS, n) + BS - 1) / BS : 0;
+  const int j0 = jb + part * a.blocks_per_part;
   const int j1 = min(nblk, j0 + a.blocks_per_part);
   const int r = lane / LPT;   // token row of this lane inside a load
   const int c = lane % LPT;   // element slice [c*EPL, c*EPL + EPL) of the head dimension
 
   if (j0 >= j1) {
-    // Nothing to read.  With a single partition this is the n == 0 row: write zeros.
-    if (a.num_parts == 1 && lane < LPT) {
+    // Nothing to read.  Direct output: this is the n == 0 row, write zeros.  Cascade
+    // partials: mark the slot empty (the merge skips it).
+    if (a.num_slots == 0 && lane < LPT) {
       for (int g = 0; g < G; ++g) {
         uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + h0 + g) * D + c * EPL;
         for (int e = 0; e < EPL; ++e) o[e] = 0;
       }
+    } else if (a.mode != MODE_PLAIN && lane < G) {
+      const size_t pi = ((size_t)s * a.num_heads + h0 + lane) * a.num_slots + a.slot_base + part;
+      a.part_ml[pi * 2] = -INFINITY;
+      a.part_ml[pi * 2 + 1] = 0.f;
     }
     return;
   }
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
       for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
     }
     const int h = h0 + g;
-    if (a.num_parts == 1) {
+    if (a.num_slots == 0) {
       if (lane < LPT) {
         uint16_t ob[EPL];
 #pragma unroll
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
         }
       }
     } else {
-      const size_t pi = ((size_t)s * a.num_heads + h) * a.num_parts + part;
+      const size_t pi = ((size_t)s * a.num_heads + h) * a.num_slots + a.slot_base + part;
       if (lane < LPT) {
         float* pa_ = a.part_acc + pi * D + c * EPL;
 #pragma unroll

@@ -117,4 +117,13 @@ struct TableSlice {
   }
 };
 
+// Tokens of its group's shared prefix that a sequence of length n attends (cascade modes):
+// the group's shared blocks, clamped to [0, max_prefix_blocks], in tokens, capped at n.
+__device__ __forceinline__ int prefix_tokens(const DecodeArgs& a, int group, int block_size, int n) {
+  int pb = a.prefix_blocks[group];
+  pb = pb < 0 ? 0 : (pb > a.max_prefix_blocks ? a.max_prefix_blocks : pb);
+  const int t = pb * block_size;
+  return t < n ? t : n;
+}
+
 }  // namespace pa

@@ -16,21 +16,37 @@ constexpr int kMaxUnitBlocks = 64;  // blocks one work unit (wavefront) walks at
 // Decode over work units (sequence, KV head, partition).  A unit walks blocks
 // [part * blocks_per_part, min(ceil(n / B), (part + 1) * blocks_per_part)) of its
 // sequence for the num_heads / num_kv_heads query heads that share the KV head.
+//
+// Shared-prefix (cascade) modes: the batch is cut into groups of seq_group consecutive
+// sequences whose first prefix_blocks[g] table entries are the same physical blocks.
+//   MODE_PREFIX: units are (group, KV head, partition) over the group's shared prefix; the
+//     unit's query heads are the G heads of every member (seq_group * G of them), and head
+//     c of member k sees min(prefix tokens, n_k) of those tokens.
+//   MODE_SUFFIX: units are (sequence, KV head, partition) over the tokens after the
+//     sequence's shared prefix; the walk starts at block ceil(min(prefix tokens, n) / B).
+// In both modes every unit writes its (m, l, acc) partial, empty or not, into slot
+// slot_base + part of the num_slots slots of each of its rows.
+enum DecodeMode : int32_t { MODE_PLAIN = 0, MODE_PREFIX = 1, MODE_SUFFIX = 2 };
+
 struct DecodeArgs {
-  void* out;                 // [S, Hq, D] q dtype (written when num_parts == 1)
+  void* out;                 // [S, Hq, D] q dtype (written when num_slots == 0)
   const void* q;             // [S, Hq, D]
   const void* k;             // [NB, Hkv, B, D]
   const void* v;
   const int32_t* tables;     // [S, MB]
   const int32_t* ctx;        // [S]
-  float* part_acc;           // [S, Hq, num_parts, D]   (num_parts > 1)
-  float* part_ml;            // [S, Hq, num_parts, 2]   running max (log2 units) and sum
+  float* part_acc;           // [S, Hq, num_slots, D]   (num_slots > 0)
+  float* part_ml;            // [S, Hq, num_slots, 2]   running max (log2 units) and sum
   int32_t num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks, max_ctx;
   int32_t num_parts, blocks_per_part, num_units;
+  int32_t num_slots, slot_base;  // partial slots per row (0: write the output directly)
   float qk_scale;            // scale * log2(e) * k_scale
   float v_scale;
   int32_t seq_fastest;       // unit order: 0 = (seq, part, kv head), 1 = (part, kv head, seq)
   int32_t xcd_remap;         // 1 = each XCD runs a contiguous range of workgroups
+  int32_t mode;              // DecodeMode
+  int32_t seq_group, num_groups, max_prefix_blocks;
+  const int32_t* prefix_blocks;  // [num_groups] shared leading blocks of each group
 };
 
 struct DecodeShape {
@@ -40,6 +56,9 @@ struct DecodeShape {
 
 bool decode_supported(const DecodeShape& s);
 hipError_t launch_decode(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+// The matrix-core kernel alone (the only one that runs shared-prefix units).
+bool gqa_mfma_supported(const DecodeShape& s);
+hipError_t launch_decode_gqa_mfma(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
 
 struct MergeArgs {
   void* out;
@@ -48,6 +67,7 @@ struct MergeArgs {
   const int32_t* ctx;
   int32_t num_seqs, num_heads, num_parts, partition_size, max_ctx;
   float v_scale;
+  int32_t all_slots;         // 1: merge every slot, skipping empty ones (cascade partials)
 };
 hipError_t launch_merge(int head_dim, int q_kind, const MergeArgs& a, hipStream_t stream);
 

@@ -6,6 +6,8 @@
 // between blocks ("PagedAttention: Mathematical Foundations, ..." sec. 7 pseudocode):
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  o = sum_p acc_p 2^(m_p - M) / L.
 // One wavefront per (sequence, query head); lane k owns D/64 consecutive output elements.
+// Cascade partials (shared prefix + own suffix) fill every slot of a row, some of them
+// empty (m = -inf, l = 0, acc not written): those are skipped.
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,23 +23,25 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a
   const int s = row / a.num_heads;
   int n = a.ctx[s];
   n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  const int np = (n + a.partition_size - 1) / a.partition_size;
+  const int np = a.all_slots ? (n > 0 ? a.num_parts : 0) : (n + a.partition_size - 1) / a.partition_size;
   uint16_t* o = (uint16_t*)a.out + (size_t)row * D + lane * EPL;
-  if (np == 0) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = 0;
-    return;
-  }
   const float* ml = a.part_ml + (size_t)row * a.num_parts * 2;
   const float* pacc = a.part_acc + (size_t)row * a.num_parts * D + lane * EPL;
   float M = -INFINITY;
   for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  if (M == -INFINITY) {  // n == 0: no token, zero row
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0;
+    return;
+  }
   float L = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 #pragma unroll 4
   for (int p = 0; p < np; ++p) {
-    const float w = fast_exp2(ml[2 * p] - M);
+    const float mp = ml[2 * p];
+    if (a.all_slots && mp == -INFINITY) continue;  // empty slot (wave-uniform)
+    const float w = fast_exp2(mp - M);
     L = fmaf(w, ml[2 * p + 1], L);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, pacc[(size_t)p * D + e], acc[e]);

@@ -1,0 +1,152 @@
+"""GPU parity of the shared-prefix (cascade) decode, pa_decode_shared_prefix.
+
+The operation is the plain decode ("PagedAttention: Mathematical Foundations, ..." sec. 3)
+over tables whose groups share their leading blocks (same page, sec. 5): the expected
+values are the oracle's plain decode on the same tables and caches; the cascade split
+(group prefix once, own suffix, log-sum-exp merge) must not be visible beyond rounding.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_89_amd as pa
+import workloads
+from helpers import DT, compare, dev_i32, oracle_caches, oracle_decode, oracle_tables, \
+    to_bits, to_dev, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _f64(t):
+    return t.double().cpu().numpy()
+
+
+def _shared_case(G, K, d, B, qd, kvd, lens, prompt, seed, decode_lens=None):
+    """Groups of K consecutive sequences sharing floor(prompt / B) prompt blocks (every
+    member holds the prompt).  `decode_lens` then shortens members for the decode: a
+    member shorter than its group's shared blocks attends only its first n tokens."""
+    S = len(lens)
+    assert S % K == 0
+    shared = prompt // B
+    need = (S // K) * shared + sum(max(0, math.ceil(n / B) - shared) for n in lens) + 5
+    sp = workloads.Spec("casc", S, 2 * G, 2, d, B, 0, 0, need, max(math.ceil(max(lens) / B), shared) + 2,
+                        qd, kvd, 1 / math.sqrt(d), group_size=K, prompt_len=prompt)
+    case = workloads.generate(sp, seed, context_lens=lens)
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    if decode_lens is not None:
+        case.context_lens = np.asarray(decode_lens, np.int32)
+    return case, tables, k, v
+
+
+def _cascade(case, tables, k, v, prefix_blocks, max_prefix_blocks, **kw):
+    sp = case.spec
+    out = pa.decode_shared_prefix(
+        to_dev(case.q, sp.q_dtype), to_dev(k, sp.kv_dtype), to_dev(v, sp.kv_dtype),
+        dev_i32(tables), dev_i32(case.context_lens), dev_i32(prefix_blocks), sp.group_size,
+        int(case.context_lens.max()), max_prefix_blocks, sp.scale, case.k_scale, case.v_scale,
+        **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", [("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"),
+                                ("f16", "e4m3")])
+def test_shared_prefix_matches_oracle_all_variants(d, dt):
+    """Every compiled variant and member-head count (G query heads per KV head x K members
+    in {2, 4, 8, 16}); members shorter than the prompt, of length 0 and 1, ending on and
+    around block and partition edges; groups using all, part or none of their shared blocks;
+    library, one-block and four-block partitions; both load policies."""
+    qd, kvd = dt
+    B, prompt = 16, 53                      # 3 shared blocks, partial prompt block private
+    pool = [53, 54, 63, 64, 65, 97, 300, 513]
+    short = [0, 1, 17, 47, 48, 49]
+    for G, K in ((1, 2), (1, 4), (2, 2), (1, 16), (2, 4), (4, 4), (8, 2)):
+        lens = [pool[(3 * i + G + K) % len(pool)] for i in range(3 * K)]
+        dec = list(lens)
+        for k in range(0, K, 2):            # group 0: every other member ends inside the prompt
+            dec[k] = short[(k // 2 + G) % len(short)]
+        case, tables, k, v = _shared_case(G, K, d, B, qd, kvd, lens, prompt, 77 + G * K + d,
+                                          decode_lens=dec)
+        lens = dec
+        ref = oracle_decode(case, tables, k, v)
+        atol, rrel = tolerance(case.spec)
+        # group 0: all 3 shared blocks; group 1: 1 of them; group 2: none
+        pbs = np.array([3, 1, 0], np.int32)
+        for P in (0, B, 4 * B):
+            for flags in (0, pa.DECODE_SHARED_KV):
+                out = _f64(_cascade(case, tables, k, v, pbs, 3, partition_size=P, flags=flags))
+                for s, n in enumerate(lens):
+                    if n == 0:
+                        assert (out[s] == 0).all(), "n = 0 must give a zero row"
+                compare(out, ref, atol, rrel, qd)
+
+
+def test_prefix_bound_clamps_and_equals_plain_decode():
+    """prefix_blocks above max_prefix_blocks are clamped to it; any valid split gives the
+    plain decode's result up to rounding, and the cascade output is deterministic."""
+    B, K, G = 16, 4, 1
+    lens = [200, 80, 96, 112, 190, 81, 100, 129]
+    case, tables, k, v = _shared_case(G, K, 128, B, "bf16", "e4m3", lens, 80, 5,
+                                      decode_lens=[200, 33, 48, 64, 190, 20, 100, 129])
+    ref = oracle_decode(case, tables, k, v)
+    atol, rrel = tolerance(case.spec)
+    a = _f64(_cascade(case, tables, k, v, np.array([9, 9], np.int32), 5))
+    b = _f64(_cascade(case, tables, k, v, np.array([5, 5], np.int32), 5))
+    c = _f64(_cascade(case, tables, k, v, np.array([2, 7], np.int32), 2))
+    assert np.array_equal(a, b)
+    for x in (a, c):
+        compare(x, ref, atol, rrel, "bf16")
+    again = _f64(_cascade(case, tables, k, v, np.array([5, 5], np.int32), 5))
+    assert np.array_equal(a, again)
+
+
+def test_full_size_fp8_shared_prompts_sampled_rows():
+    """The fp8 shared-prompt workload at full size (256 sequences in groups of 4 behind
+    1024-token prompts, 32 heads, d 128, e4m3 K/V) launched as the benchmark launches it:
+    the oracle checks sampled (sequence, head) rows one by one; every row is finite and
+    within rounding of the plain library decode."""
+    sp = workloads.SPECS["fp8_prefix"]
+    seed = 8900 + list(workloads.SPECS).index("fp8_prefix")
+    ctx, free = workloads.draw_lengths(sp, seed)
+    pg, pl = workloads.prefix_groups(sp)
+    st, tables, _, _ = oracle.build_tables(sp.num_blocks, sp.block_size, free, ctx,
+                                           sp.max_blocks, pg, pl)
+    assert st == 0
+    q, kd, vd, ks, vs = workloads.device_pool(sp, seed)
+    pb = (pl // sp.block_size).astype(np.int32)
+    td, cd = dev_i32(tables), dev_i32(ctx)
+    out = pa.decode_shared_prefix(q, kd, vd, td, cd, dev_i32(pb), sp.group_size, int(ctx.max()),
+                                  int(pb.max()), sp.scale, ks, vs, flags=pa.DECODE_SHARED_KV)
+    plain = pa.decode(q, kd, vd, td, cd, int(ctx.max()), sp.scale, ks, vs,
+                      flags=pa.DECODE_SHARED_KV)
+    torch.cuda.synchronize()
+    got = _f64(out)
+    assert np.isfinite(got).all()
+    atol, rrel = tolerance(sp)
+    compare(got, _f64(plain), atol, None, None)
+    rng = np.random.default_rng(seed)
+    S, H = sp.num_seqs, sp.num_heads
+    rows = set(zip(rng.integers(0, S, 64).tolist(), rng.integers(0, H, 64).tolist()))
+    rows |= {(s, 0) for s in range(4)}      # one whole group
+    rows = np.array(sorted(rows), np.int32)
+    qb, kb, vb = to_bits(q), to_bits(kd), to_bits(vd)
+    del kd, vd
+    ref = oracle.decode(qb, DT[sp.q_dtype], kb, vb, DT[sp.kv_dtype], tables, ctx,
+                        sp.num_kv_heads, sp.block_size, sp.scale, ks, vs, rows=rows)
+    compare(got[rows[:, 0], rows[:, 1]], ref[rows[:, 0], rows[:, 1]], atol, rrel, sp.q_dtype)

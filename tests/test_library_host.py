@@ -170,3 +170,30 @@ def test_decode_argument_errors_without_gpu():
     st = L.pa_write_kv(None, None, None, None, None, 1, 4, None, None, 1, 4, 8, 128, 16,
                        0, 1, 1.0, 1.0, None)  # f16 source into a bf16 cache
     assert st == -2
+
+
+def test_shared_prefix_workspace_and_errors_without_gpu():
+    # fp8 shared-prompt shape: 256 seqs, 32 heads, d 128, B 16, max context 1536, prompts
+    # of 64 blocks.  P = 512 (pa_decode's choice); 2 prefix slots + 3 per-sequence slots.
+    assert pa.decode_plan(256, 32, 32, 128, 16, 1536, 0) == (512, 3)
+    ws = pa.decode_shared_prefix_workspace_size(256, 32, 32, 128, 16, 1536, 64)
+    assert ws == 256 * 32 * (2 + 3) * 130 * 4
+    # unsplit choice: the whole context (rounded to B) is one slot on each side
+    assert pa.decode_shared_prefix_workspace_size(4, 8, 8, 64, 16, 100, 2) == 4 * 8 * 2 * 66 * 4
+    # no prefix bound: per-sequence slots only
+    assert pa.decode_shared_prefix_workspace_size(4, 8, 8, 64, 16, 100, 0) == 4 * 8 * 1 * 66 * 4
+    assert pa.decode_shared_prefix_workspace_size(4, 8, 8, 64, 16, 100, -1) == 0  # bad bound
+    L = pa.lib()
+
+    def call(S=8, K=4, Hq=8, Hkv=8, d=128, B=16, q=1, kv=2, flags=0):
+        return L.pa_decode_shared_prefix(None, None, None, None, None, None, None, S, K, Hq, Hkv,
+                                         d, B, 8, 64, 128, 4, 0.1, q, kv, 1.0, 1.0, 0, flags,
+                                         None, 0, None)
+    assert call(B=8) == -2 and b"block_size 16" in L.pa_last_error()
+    assert call(K=1) == -2                      # one query head per unit: no matrix-core tile
+    assert call(K=4, Hq=16, Hkv=2) == -2        # 8 heads x 4 members = 32 > 16
+    assert call(q=0, kv=1) == -2                # fp16 queries over a bf16 cache
+    assert call(S=6, K=4) == -1 and b"multiple of seq_group" in L.pa_last_error()
+    assert call(flags=4) == -1 and b"flag" in L.pa_last_error()
+    assert call() == -1 and b"NULL" in L.pa_last_error()
+    assert call(S=0) == 0                       # empty batch: nothing to do
