@@ -106,7 +106,9 @@ __device__ __forceinline__ void e4m3x16_widen(const u32x4 src, u32x4 (&dst)[2]) 
 // Supported: D in {64, 128}, B = 16 (one MFMA token tile per block), fp16 or bf16 Q with a
 // cache of the same type or e4m3 (widened to Q's type while it is staged into LDS),
 // 2 <= G <= 16.
-template <int D, int QK, int KVK, int G, bool NT>
+// PREFIX: the kernel runs the prefix units of the shared-prefix decode (a.mode ==
+// MODE_PREFIX), whose per-column token counts need a per-lane mask.
+template <int D, int QK, int KVK, int G, bool NT, bool PREFIX>
 __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
   constexpr int KSTEPS = D / 32;             // 16x16x32 steps over the head dimension
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   }
   const int unit = wg * 4 + wave;
   if (unit >= a.num_units) return;
-  const bool prefix = a.mode == MODE_PREFIX;
+  constexpr bool prefix = PREFIX;
   const int rows = prefix ? a.num_groups : a.num_seqs;
   int s, kvh, part;  // s: the sequence, or in prefix mode the group
   if (a.seq_fastest == 0) {
@@ -162,8 +164,9 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   // the G heads of sequence s that share KV head kvh.  Prefix units: head c % Gr of member
   // c / Gr of group s (Gr = real query heads per KV head, G = seq_group * Gr).
   const int Gr = a.num_heads / a.num_kv_heads;
-  const int sc = prefix ? s * a.seq_group + c / Gr : s;
-  const int hc = prefix ? kvh * Gr + c % Gr : kvh * G + c;
+  auto seq_of = [&](int cc) { return prefix ? s * a.seq_group + cc / Gr : s; };
+  auto head_of = [&](int cc) { return prefix ? kvh * Gr + cc % Gr : kvh * G + cc; };
+  const int sc = seq_of(c);
   auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > a.max_ctx ? a.max_ctx : v); };
   // n: tokens the unit's block range covers; nc: tokens head c attends (slot t is
   // visible to head c iff t < nc); jb: first block of the walk.
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
       uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + kvh * G) * D;
       for (int e = lane; e < G * D; e += 64) o[e] = 0;
     } else if (a.mode != MODE_PLAIN && r == 0 && c < G) {  // empty cascade slot
-      const size_t pi = ((size_t)sc * a.num_heads + hc) * a.num_slots + a.slot_base + part;
+      const size_t pi = ((size_t)sc * a.num_heads + head_of(c)) * a.num_slots + a.slot_base + part;
       a.part_ml[pi * 2] = -INFINITY;
       a.part_ml[pi * 2 + 1] = 0.f;
     }
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
     if (c < G)
-      qop[kk] = *(const u32x4*)((const uint16_t*)a.q + ((size_t)sc * a.num_heads + hc) * D +
+      qop[kk] = *(const u32x4*)((const uint16_t*)a.q + ((size_t)sc * a.num_heads + head_of(c)) * D +
                                 32 * kk + 8 * r);
     else
       qop[kk] = u32x4{0, 0, 0, 0};
@@ -285,7 +288,11 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   auto finish = [&](int j, f32x4 sv) {
     float z[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = (j * BS + 4 * r + i < nc) ? sv[i] * qk_scale : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const int t = j * BS + 4 * r + i;
+      const bool ok = PREFIX ? (t < nc) : (c < G && t < n);
+      z[i] = ok ? sv[i] * qk_scale : -INFINITY;
+    }
     float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
@@ -363,7 +370,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
     const int hh = 4 * r + i;
     const float Li = __shfl(L, hh);
     const float Mi = __shfl(m_ref, hh);
-    const int sh = __shfl(sc, hh), h = __shfl(hc, hh);  // row of query head hh
+    const int sh = seq_of(hh), h = head_of(hh);  // row of query head hh
     if (hh < G) {
       if (a.num_slots == 0) {
         uint16_t* o = (uint16_t*)a.out + ((size_t)sh * a.num_heads + h) * D + c;
@@ -387,7 +394,12 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 template <int D, int QK, int KVK, int G, bool NT>
 hipError_t launch_gqa_mfma_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((a.num_units + 3) / 4);
-  hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT>), grid, dim3(256), 0, stream, a);
+  if (a.mode == MODE_PREFIX)
+    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true>), grid, dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, false>), grid, dim3(256), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
