@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.or_decode.argtypes = dec + [vp, c.c_int32, c.c_int32, vp, vp]
         L.or_decode_online.argtypes = dec + [vp, vp]
         L.or_decode_partitioned.argtypes = dec + [c.c_int32, vp]
+        L.or_decode_multi.argtypes = dec + [c.c_int32, vp, c.c_int32, vp]
         L.or_kv_bytes_per_token.argtypes = [c.c_int32] * 4
         L.or_kv_bytes_per_token.restype = c.c_uint64
         _lib = L
@@ -221,6 +222,23 @@ def decode_partitioned(q, q_dtype, k_cache, v_cache, kv_dtype, tables, context_l
     S, Hq, d = keep[0].shape
     out = np.zeros((S, Hq, d))
     lib().or_decode_partitioned(*args, int(partition_size), _p(out))
+    return out
+
+
+def decode_multi(q, q_dtype, k_cache, v_cache, kv_dtype, tables, context_lens, num_kv_heads,
+                 block_size, scale, k_scale=1.0, v_scale=1.0, tree_masks=None, threads=None):
+    """Multi-token queries q [S, T, Hq, d] (the last T positions of each sequence);
+    tree_masks [S, T] uint32 or None (causal).  Returns out [S, T, Hq, d] fp64."""
+    q = np.ascontiguousarray(q)
+    S, T, Hq, d = q.shape
+    keep, args = _dec_args(q.reshape(S, T * Hq, d), q_dtype, k_cache, v_cache, kv_dtype,
+                           k_scale, v_scale, tables, context_lens, num_kv_heads, block_size,
+                           scale)
+    args[10] = Hq  # _dec_args read Hq from the flattened shape
+    tm = None if tree_masks is None else _c(tree_masks, np.uint32).reshape(S, T)
+    out = np.zeros((S, T, Hq, d))
+    nthreads = threads if threads is not None else (os.cpu_count() or 1)
+    lib().or_decode_multi(*args, int(T), _p(tm), nthreads, _p(out))
     return out
 
 

@@ -306,6 +306,45 @@ void decode_row_partitioned(const DecodeArgs& a, int s, int h, int P, double* ou
   }
 }
 
+// Several query tokens per sequence (speculative / tree verification, [P1] sec. 9 names
+// speculative decoding trees among the uses of the shared block store).  Reading: the T
+// query tokens of sequence s are its last T positions n-T .. n-1, already stored in the
+// cache; query t sees every position before n-T and the draft position n-T+u iff bit u
+// of its mask is set (causal mask: bits 0..t).  The output is the same softmax-weighted
+// sum of [P1] sec. 3 over the visible positions; no visible position gives a zero row.
+void decode_row_multi(const DecodeArgs& a, int T, const uint32_t* masks, int s, int t, int h,
+                      double* out) {
+  const int n = a.ctx[s];
+  const int g = h / (a.Hq / a.Hkv);
+  const size_t row = ((size_t)s * T + t) * a.Hq + h;
+  double* o = out + row * a.d;
+  for (int i = 0; i < a.d; ++i) o[i] = 0.0;
+  const uint32_t mask = masks ? masks[(size_t)s * T + t] : (uint32_t)((2ull << t) - 1);
+  const int first_draft = n - T;
+  std::vector<int> vis;
+  for (int p = 0; p < n; ++p) {
+    if (p < first_draft) { vis.push_back(p); continue; }
+    const int u = p - first_draft;
+    if (u < 32 && ((mask >> u) & 1u)) vis.push_back(p);
+  }
+  if (vis.empty()) return;
+  std::vector<double> z(vis.size());
+  for (size_t k = 0; k < vis.size(); ++k) {
+    double dot = 0.0;
+    for (int i = 0; i < a.d; ++i)
+      dot += load_elem(a.q, row * a.d + i, a.q_dtype) *
+             dequant(a.k, cache_index(a, s, vis[k], g, i), a.kv_dtype, a.k_scale);
+    z[k] = a.scale * dot;
+  }
+  double m = -std::numeric_limits<double>::infinity();
+  for (double x : z) m = std::max(m, x);
+  double Z = 0.0;
+  for (double& x : z) { x = std::exp(x - m); Z += x; }
+  for (size_t k = 0; k < vis.size(); ++k)
+    for (int i = 0; i < a.d; ++i)
+      o[i] += z[k] / Z * dequant(a.v, cache_index(a, s, vis[k], g, i), a.kv_dtype, a.v_scale);
+}
+
 template <class F>
 void parallel_rows(int nrows, int threads, F&& f) {
   if (threads <= 1 || nrows <= 1) {
@@ -500,6 +539,19 @@ void or_decode_partitioned(const void* q, int q_dtype, const void* k_cache, cons
                S, Hq, Hkv, d, B, MB, (double)scale};
   for (int s = 0; s < S; ++s)
     for (int h = 0; h < Hq; ++h) decode_row_partitioned(a, s, h, P, out);
+}
+
+// Multi-token queries: q and out are [S, T, Hq, d]; tree_masks is [S, T] or null (causal).
+void or_decode_multi(const void* q, int q_dtype, const void* k_cache, const void* v_cache,
+                     int kv_dtype, float k_scale, float v_scale, const int32_t* tables,
+                     const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t d,
+                     int32_t B, int32_t MB, float scale, int32_t T, const uint32_t* tree_masks,
+                     int32_t threads, double* out) {
+  DecodeArgs a{q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, tables, context_lens,
+               S, Hq, Hkv, d, B, MB, (double)scale};
+  parallel_rows(S * T * Hq, threads, [&](int r) {
+    decode_row_multi(a, T, tree_masks, r / (T * Hq), (r / Hq) % T, r % Hq, out);
+  });
 }
 
 // ---- O6: footprint ----

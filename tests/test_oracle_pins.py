@@ -437,3 +437,74 @@ def test_shared_prefix_equals_private_copies(orc):
     k2, v2 = oracle_caches(priv, t2)
     out2 = oracle_decode(priv, t2, k2, v2)
     assert np.array_equal(out, out2)
+
+
+# ------------------------------------------------------------------ multi-token queries
+def _multi_case(T, kv="f16", q="f16", seed=3, lens=(1, 2, 5, 16, 17, 40, 64)):
+    sp = workloads.Spec("multi", len(lens), 8, 4, 64, 16, 1, 1,
+                        sum(math.ceil(n / 16) for n in lens) + 4, math.ceil(max(lens) / 16) + 1,
+                        q, kv, 0.125)
+    case = workloads.generate(sp, seed, context_lens=list(lens))
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    rng = np.random.default_rng(seed)
+    qm = workloads._round_bits(rng.standard_normal((len(lens), T, 8, 64), dtype=np.float32), q)
+    return case, tables, k, v, qm
+
+
+def _multi(case, tables, k, v, qm, masks=None):
+    sp = case.spec
+    return oracle.decode_multi(qm, DT[sp.q_dtype], k, v, DT[sp.kv_dtype], tables,
+                               case.context_lens, sp.num_kv_heads, sp.block_size, sp.scale,
+                               case.k_scale, case.v_scale, tree_masks=masks)
+
+
+def test_multi_single_token_equals_decode(orc):
+    """T = 1 with the causal mask is the plain decode (a different oracle routine)."""
+    case, tables, k, v, qm = _multi_case(1)
+    sp = case.spec
+    out = _multi(case, tables, k, v, qm)
+    ref = oracle.decode(qm[:, 0], DT[sp.q_dtype], k, v, DT[sp.kv_dtype], tables,
+                        case.context_lens, sp.num_kv_heads, sp.block_size, sp.scale)
+    assert np.abs(out[:, 0] - ref).max() <= 1e-13
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_multi_causal_equals_truncated_decode(orc, T):
+    """Causal query t of a sequence of n tokens sees exactly its first n - T + 1 + t
+    positions: the plain decode with that length."""
+    case, tables, k, v, qm = _multi_case(T, seed=5 + T)
+    sp = case.spec
+    out = _multi(case, tables, k, v, qm)
+    for t in range(T):
+        lens = np.maximum(case.context_lens - T + 1 + t, 0).astype(np.int32)
+        ref = oracle.decode(qm[:, t], DT[sp.q_dtype], k, v, DT[sp.kv_dtype], tables, lens,
+                            sp.num_kv_heads, sp.block_size, sp.scale)
+        assert np.abs(out[:, t] - ref).max() <= 1e-13
+
+
+def test_multi_tree_mask_vs_dense_numpy(orc):
+    """Arbitrary tree masks: dense attention over the visible logical rows in numpy."""
+    T = 4
+    case, tables, k, v, qm = _multi_case(T, kv="bf16", q="bf16", seed=9)
+    sp = case.spec
+    rng = np.random.default_rng(1)
+    masks = rng.integers(0, 1 << T, (sp.num_seqs, T)).astype(np.uint32)
+    masks[0, :] = 0                       # n = 1: query 0..3 see nothing or the one token
+    out = _multi(case, tables, k, v, qm, masks)
+    G = sp.num_heads // sp.num_kv_heads
+    for s in range(sp.num_seqs):
+        n = int(case.context_lens[s])
+        K = workloads.bits_to_f32(case.logical(s, "k"), "bf16").astype(np.float64)
+        V = workloads.bits_to_f32(case.logical(s, "v"), "bf16").astype(np.float64)
+        for t in range(T):
+            vis = [p for p in range(n) if p < n - T or (masks[s, t] >> (p - (n - T))) & 1]
+            for h in range(sp.num_heads):
+                if not vis:
+                    assert (out[s, t, h] == 0).all()
+                    continue
+                qv = workloads.bits_to_f32(qm[s, t, h], "bf16").astype(np.float64)
+                z = np.float64(np.float32(sp.scale)) * (K[vis, h // G] @ qv)
+                w = np.exp(z - z.max())
+                ref = (w / w.sum()) @ V[vis, h // G]
+                assert np.abs(out[s, t, h] - ref).max() <= 1e-12
