@@ -278,6 +278,37 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
                                   void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Multi-token decode: query_len > 1 query tokens per sequence, as when a draft of several
+ * tokens (a chain or a tree, [P1] sec. 9 speculative decoding trees) is verified in one
+ * pass.  The query tokens of sequence s are its last query_len positions, whose K/V rows
+ * are already in the cache (n = context_lens[s] counts them).  Query token t attends
+ * every position before n - query_len and the draft position n - query_len + u when bit
+ * u of its mask is set; with tree_masks == NULL the mask is causal (bits 0..t).  Each
+ * (s, t, h) output row is the [P1] sec. 3 softmax-weighted sum over its visible
+ * positions; a row with no visible position is zero.
+ *   out, query     [num_seqs, query_len, num_heads, head_dim] in q_dtype
+ *   tree_masks     device [num_seqs, query_len] uint32, or NULL (causal)
+ *   Other arguments, planning, flags and the workspace as for pa_decode (the workspace
+ *   holds partials for num_seqs * query_len * num_heads rows).
+ * One matrix-core tile holds the query_len * (num_heads / num_kv_heads) query columns of
+ * a KV head, so each K/V tile is read once for all draft tokens.
+ * Supported: block_size 16, head_dim in {64, 128}, query_len * (num_heads / num_kv_heads)
+ * in {2, 4, 8, 16}, q in {f16, bf16} with a cache of the same type or e4m3. */
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t query_len, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t max_context_len, int32_t partition_size);
+
+pa_status pa_decode_multi(void* out, const void* query, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const uint32_t* tree_masks, int32_t num_seqs, int32_t query_len,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                          int32_t max_context_len, float scale, pa_dtype q_dtype,
+                          pa_dtype kv_dtype, float k_scale, float v_scale,
+                          int32_t partition_size, uint32_t flags, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Footprint: [P1] sec. 1 "KV Cache Memory Footprint" — a token stores one key and one
  * value vector per layer, so it costs 2 * num_layers * num_kv_heads * head_dim * e bytes
  * (e = 2 for fp16/bf16, 1 for e4m3); with fp16 and num_kv_heads * head_dim = d_model this

@@ -81,12 +81,17 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                           i32, i32, i32, i32, i32, f32, c.c_int, c.c_int, f32,
                                           f32, i32, c.c_uint32, vp, sz, vp]
+    L.pa_decode_multi_workspace_size.argtypes = [i32] * 8
+    L.pa_decode_multi_workspace_size.restype = sz
+    L.pa_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                  i32, i32, f32, c.c_int, c.c_int, f32, f32, i32, c.c_uint32, vp,
+                                  sz, vp]
     L.pa_kv_bytes_per_token.argtypes = [i32, i32, i32, c.c_int]
     L.pa_kv_bytes_per_token.restype = c.c_uint64
     for name in ("pa_bm_create", "pa_alloc_tables", "pa_bm_free", "pa_bm_stats",
                  "pa_bm_free_list", "pa_bm_fork", "pa_bm_append", "pa_bm_table",
                  "pa_copy_blocks", "pa_write_kv", "pa_decode_plan", "pa_decode",
-                 "pa_decode_shared_prefix"):
+                 "pa_decode_shared_prefix", "pa_decode_multi"):
         getattr(L, name).restype = c.c_int
     _lib = L
     return L
@@ -331,6 +336,44 @@ def decode_shared_prefix(query, k_cache, v_cache, block_tables, context_lens, pr
         _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
         _dev(context_lens, "context_lens"), pb, S, int(seq_group), Hq, Hkv, D, B, MB, NB,
         int(max_context_len), int(max_prefix_blocks), float(scale), _dtype_code(query),
+        _dtype_code(k_cache), float(k_scale), float(v_scale), int(partition_size), int(flags),
+        ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def decode_multi_workspace_size(num_seqs, query_len, num_heads, num_kv_heads, head_dim,
+                                block_size, max_context_len, partition_size=0) -> int:
+    return int(lib().pa_decode_multi_workspace_size(num_seqs, query_len, num_heads,
+                                                    num_kv_heads, head_dim, block_size,
+                                                    int(max_context_len), int(partition_size)))
+
+
+def decode_multi(query, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                 scale: float, k_scale: float = 1.0, v_scale: float = 1.0, tree_masks=None,
+                 partition_size: int = 0, flags: int = 0, out=None, workspace=None,
+                 stream=None):
+    """pa_decode_multi.  query [S, T, Hq, D]; tree_masks [S, T] int32/uint32 bits or None
+    (causal); returns out [S, T, Hq, D] (query dtype)."""
+    torch = _torch()
+    S, T, Hq, D = query.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("decode_multi: shape mismatch")
+    if tree_masks is not None and tuple(tree_masks.shape) != (S, T):
+        raise ValueError("decode_multi: tree_masks must be [S, T]")
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    need = decode_multi_workspace_size(S, T, Hq, Hkv, D, B, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    tm = _dev(tree_masks, "tree_masks") if tree_masks is not None else None
+    _check(lib().pa_decode_multi(
+        _dev(out, "out"), _dev(query, "query"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), tm, S, T, Hq,
+        Hkv, D, B, MB, NB, int(max_context_len), float(scale), _dtype_code(query),
         _dtype_code(k_cache), float(k_scale), float(v_scale), int(partition_size), int(flags),
         ws_ptr, ws_bytes, _stream(stream)))
     return out

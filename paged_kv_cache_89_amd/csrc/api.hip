@@ -292,6 +292,7 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   a.slot_base = 0;
   a.mode = MODE_PLAIN;
   a.seq_group = 1; a.num_groups = num_seqs; a.max_prefix_blocks = 0; a.prefix_blocks = nullptr;
+  a.query_len = 1; a.tree_masks = nullptr;
   if (log_enabled())
     std::fprintf(stderr, "[paged_attn] decode S=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d P=%d parts=%d units=%lld\n",
                  num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
@@ -396,6 +397,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
   a.seq_group = seq_group; a.num_groups = groups;
   a.max_prefix_blocks = max_prefix_blocks;
   a.prefix_blocks = prefix_blocks;
+  a.query_len = 1; a.tree_masks = nullptr;
   if (log_enabled())
     std::fprintf(stderr, "[paged_attn] shared-prefix decode S=%d K=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d "
                  "max_prefix_blocks=%d P=%d prefix_parts=%d suffix_parts=%d\n",
@@ -422,6 +424,97 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
   m.v_scale = a.v_scale; m.all_slots = 1;
   return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream),
                     "pa_decode_shared_prefix merge launch");
+}
+
+size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t query_len, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t max_context_len, int32_t partition_size) {
+  Plan p;
+  if (query_len < 1 || make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                 max_context_len, partition_size, &p) != PA_OK)
+    return 0;
+  return workspace_bytes(p, num_seqs * query_len, num_heads, head_dim);
+}
+
+pa_status pa_decode_multi(void* out, const void* query, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          const uint32_t* tree_masks, int32_t num_seqs, int32_t query_len,
+                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                          int32_t max_context_len, float scale, pa_dtype q_dtype,
+                          pa_dtype kv_dtype, float k_scale, float v_scale,
+                          int32_t partition_size, uint32_t flags, void* workspace,
+                          size_t workspace_bytes_given, void* stream) {
+  g_last_error.clear();
+  const std::string who = "pa_decode_multi";
+  int qk, kk;
+  if (!dtype_kind(q_dtype, &qk) || !dtype_kind(kv_dtype, &kk))
+    return fail(PA_ERR_INVALID_ARG, who + ": unknown dtype");
+  if (num_seqs < 0 || query_len < 1 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      block_size < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0 ||
+      partition_size < 0)
+    return fail(PA_ERR_INVALID_ARG, who + ": bad size");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, who + ": num_heads must be a multiple of num_kv_heads");
+  if (partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, who + ": partition_size must be a multiple of block_size");
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_INVALID_ARG, who + ": non-finite scale");
+  if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
+    return fail(PA_ERR_INVALID_ARG, who + ": unknown flag bits");
+  const bool shared = (flags & PA_DECODE_SHARED_KV) != 0;
+  const int64_t cols = (int64_t)query_len * (num_heads / num_kv_heads);
+  DecodeShape shape{head_dim, block_size, qk, kk, (int)std::min<int64_t>(cols, 1 << 20), !shared};
+  if (!gqa_mfma_supported(shape))
+    return fail(PA_ERR_UNSUPPORTED, who + ": needs block_size 16, head_dim 64/128, fp16/bf16 "
+                "queries and query_len*(num_heads/num_kv_heads) in {2,4,8,16}");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, who + ": NULL pointer");
+
+  const int64_t reach = (int64_t)max_blocks_per_seq * block_size;
+  const int32_t max_ctx = (int32_t)(max_context_len < reach ? max_context_len : reach);
+  Plan plan;
+  pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, partition_size, &plan);
+  if (st != PA_OK) return st;
+  const int32_t qrows = num_seqs * query_len;  // rows of [S, T] query tokens
+  const size_t need = workspace_bytes(plan, qrows, num_heads, head_dim);
+  if (need > 0 && (!workspace || workspace_bytes_given < need))
+    return fail(PA_ERR_INVALID_ARG, who + ": workspace needs " + std::to_string(need) +
+                                        " bytes, got " + std::to_string(workspace_bytes_given));
+  DecodeArgs a;
+  a.out = out; a.q = query; a.k = k_cache; a.v = v_cache;
+  a.tables = block_tables; a.ctx = context_lens;
+  a.part_acc = need ? (float*)workspace : nullptr;
+  a.part_ml = need ? (float*)workspace + (size_t)qrows * num_heads * plan.num_parts * head_dim
+                   : nullptr;
+  a.num_seqs = num_seqs; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks; a.max_ctx = max_ctx;
+  a.num_parts = plan.num_parts;
+  a.blocks_per_part = plan.num_parts > 1 ? plan.partition_size / block_size
+                                         : (int32_t)((reach + block_size - 1) / block_size);
+  const int64_t units = (int64_t)num_seqs * num_kv_heads * plan.num_parts;
+  if (units > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, who + ": grid too large");
+  a.num_units = (int32_t)units;
+  a.num_slots = plan.num_parts > 1 ? plan.num_parts : 0;
+  a.slot_base = 0;
+  const bool f8 = kk == KIND_E4M3;
+  a.qk_scale = scale * kLog2e * (f8 ? k_scale : 1.0f);
+  a.v_scale = f8 ? v_scale : 1.0f;
+  a.seq_fastest = shared ? 1 : 0;
+  a.xcd_remap = 1;
+  a.mode = MODE_MULTI;
+  a.seq_group = 1; a.num_groups = num_seqs; a.max_prefix_blocks = 0; a.prefix_blocks = nullptr;
+  a.query_len = query_len; a.tree_masks = tree_masks;
+  st = hip_status(launch_decode_gqa_mfma(shape, a, (hipStream_t)stream), "pa_decode_multi launch");
+  if (st != PA_OK || plan.num_parts <= 1) return st;
+  MergeArgs m;
+  m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
+  m.num_seqs = num_seqs; m.num_heads = query_len * num_heads; m.num_parts = plan.num_parts;
+  m.partition_size = plan.partition_size; m.max_ctx = max_ctx;
+  m.v_scale = a.v_scale; m.all_slots = 0;
+  return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream), "pa_decode_multi merge launch");
 }
 
 }  // extern "C"

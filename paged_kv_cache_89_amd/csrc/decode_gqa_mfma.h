@@ -106,9 +106,10 @@ __device__ __forceinline__ void e4m3x16_widen(const u32x4 src, u32x4 (&dst)[2]) 
 // Supported: D in {64, 128}, B = 16 (one MFMA token tile per block), fp16 or bf16 Q with a
 // cache of the same type or e4m3 (widened to Q's type while it is staged into LDS),
 // 2 <= G <= 16.
-// PREFIX: the kernel runs the prefix units of the shared-prefix decode (a.mode ==
-// MODE_PREFIX), whose per-column token counts need a per-lane mask.
-template <int D, int QK, int KVK, int G, bool NT, bool PREFIX>
+// LANE: per-column visibility (each query column has its own token range and draft
+// mask), needed by the prefix units of the shared-prefix decode and by multi-token
+// queries; plain and suffix units share one token count and use the cheaper mask.
+template <int D, int QK, int KVK, int G, bool NT, bool LANE>
 __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
   constexpr int KSTEPS = D / 32;             // 16x16x32 steps over the head dimension
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   }
   const int unit = wg * 4 + wave;
   if (unit >= a.num_units) return;
-  constexpr bool prefix = PREFIX;
+  const bool prefix = LANE && a.mode == MODE_PREFIX;
+  const bool multi = LANE && a.mode == MODE_MULTI;
   const int rows = prefix ? a.num_groups : a.num_seqs;
   int s, kvh, part;  // s: the sequence, or in prefix mode the group
   if (a.seq_fastest == 0) {
@@ -160,27 +162,42 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   }
   const int r = lane >> 4;
   const int c = lane & 15;
-  // Query head c of the unit (c < G) is head hc of sequence sc.  Plain and suffix units:
-  // the G heads of sequence s that share KV head kvh.  Prefix units: head c % Gr of member
-  // c / Gr of group s (Gr = real query heads per KV head, G = seq_group * Gr).
+  // Query column cc < G of the unit reads and writes row row_of(cc) of the [rows, D]
+  // query / output arrays.  Plain and suffix units: the G heads of sequence s that share
+  // KV head kvh.  Prefix units: head cc % Gr of member cc / Gr of group s; multi-token
+  // units: head cc % Gr of query token cc / Gr of sequence s (Gr = query heads per KV
+  // head; G = Gr * members or Gr * query tokens).
   const int Gr = a.num_heads / a.num_kv_heads;
-  auto seq_of = [&](int cc) { return prefix ? s * a.seq_group + cc / Gr : s; };
-  auto head_of = [&](int cc) { return prefix ? kvh * Gr + cc % Gr : kvh * G + cc; };
-  const int sc = seq_of(c);
+  const int outer_n = prefix ? a.seq_group : a.query_len;
+  auto row_of = [&](int cc) -> size_t {
+    if (LANE && (prefix || multi))
+      return ((size_t)s * outer_n + cc / Gr) * a.num_heads + kvh * Gr + cc % Gr;
+    return (size_t)s * a.num_heads + kvh * G + cc;
+  };
   auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > a.max_ctx ? a.max_ctx : v); };
-  // n: tokens the unit's block range covers; nc: tokens head c attends (slot t is
-  // visible to head c iff t < nc); jb: first block of the walk.
-  int n, nc, jb = 0;
+  // n: tokens the unit's block range covers; jb: first block of the walk.  Column c
+  // sees token t iff t < lo or (t < hi and bit t - lo of tm is set).
+  int n, jb = 0, lo = 0, hi = 0;
+  uint32_t tm = 0;
   const int32_t* table_row;
   if (prefix) {
     n = 0;
     for (int k = 0; k < a.seq_group; ++k)
       n = max(n, prefix_tokens(a, s, BS, clamp_len(a.ctx[s * a.seq_group + k])));
-    nc = (c < G) ? prefix_tokens(a, s, BS, clamp_len(a.ctx[sc])) : 0;
+    lo = hi = (c < G) ? prefix_tokens(a, s, BS, clamp_len(a.ctx[s * a.seq_group + c / Gr])) : 0;
     table_row = a.tables + (size_t)s * a.seq_group * a.max_blocks;  // the group's first member
   } else {
     n = clamp_len(a.ctx[s]);
-    nc = (c < G) ? n : 0;
+    if (multi) {
+      const int t = c / Gr;
+      lo = (c < G) ? n - a.query_len : 0;
+      hi = (c < G) ? n : 0;
+      tm = (c >= G) ? 0u
+           : a.tree_masks ? a.tree_masks[(size_t)s * a.query_len + t]
+                          : (uint32_t)((2ull << t) - 1);
+    } else {
+      lo = hi = (c < G) ? n : 0;
+    }
     if (a.mode == MODE_SUFFIX) jb = (prefix_tokens(a, s / a.seq_group, BS, n) + BS - 1) / BS;
     table_row = a.tables + (size_t)s * a.max_blocks;
   }
@@ -190,10 +207,12 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 
   if (j0 >= j1) {
     if (a.num_slots == 0) {  // direct output of an n == 0 sequence: zero rows
-      uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + kvh * G) * D;
-      for (int e = lane; e < G * D; e += 64) o[e] = 0;
-    } else if (a.mode != MODE_PLAIN && r == 0 && c < G) {  // empty cascade slot
-      const size_t pi = ((size_t)sc * a.num_heads + head_of(c)) * a.num_slots + a.slot_base + part;
+      for (int cc = 0; cc < G; ++cc) {
+        uint16_t* o = (uint16_t*)a.out + row_of(cc) * D;
+        for (int e = lane; e < D; e += 64) o[e] = 0;
+      }
+    } else if (a.mode != MODE_PLAIN && r == 0 && c < G) {  // empty slot of a cascade row
+      const size_t pi = row_of(c) * a.num_slots + a.slot_base + part;
       a.part_ml[pi * 2] = -INFINITY;
       a.part_ml[pi * 2 + 1] = 0.f;
     }
@@ -205,8 +224,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
     if (c < G)
-      qop[kk] = *(const u32x4*)((const uint16_t*)a.q + ((size_t)sc * a.num_heads + head_of(c)) * D +
-                                32 * kk + 8 * r);
+      qop[kk] = *(const u32x4*)((const uint16_t*)a.q + row_of(c) * D + 32 * kk + 8 * r);
     else
       qop[kk] = u32x4{0, 0, 0, 0};
   }
@@ -290,7 +308,8 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = j * BS + 4 * r + i;
-      const bool ok = PREFIX ? (t < nc) : (c < G && t < n);
+      const bool ok = LANE ? (t < lo || (t < hi && ((tm >> ((t - lo) & 31)) & 1u)))
+                           : (c < G && t < n);
       z[i] = ok ? sv[i] * qk_scale : -INFINITY;
     }
     float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -311,11 +330,27 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
       }
     }
     const float ms = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float rp[4];
-    const uint32_t p01 = Ops::pack2(fast_exp2(z[0] - ms), fast_exp2(z[1] - ms), &rp[0], &rp[1]);
-    const uint32_t p23 = Ops::pack2(fast_exp2(z[2] - ms), fast_exp2(z[3] - ms), &rp[2], &rp[3]);
-    l_part += (rp[0] + rp[1]) + (rp[2] + rp[3]);
+    float p[4], rp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - ms);
+    const uint32_t p01 = Ops::pack2(p[0], p[1], &rp[0], &rp[1]);
+    const uint32_t p23 = Ops::pack2(p[2], p[3], &rp[2], &rp[3]);
     const u32x2 pop = u32x2{p01, p23};
+    // bf16 keeps 8 significant bits: a weight rounded to it can be off by 2^-9 of itself,
+    // which a few dominant tokens with distant values turn into output errors above the
+    // fp16/bf16 bar.  So P goes in as hi + lo (the second MFMA takes the rounding
+    // residual) and the denominator sums the unrounded weights.  fp16 P keeps 11 bits
+    // and goes in once, with the denominator of the rounded weights.
+    constexpr bool SPLIT = QK == KIND_BF16;
+    u32x2 plo = u32x2{0u, 0u};
+    if constexpr (SPLIT) {
+      float unused[4];
+      plo = u32x2{Ops::pack2(p[0] - rp[0], p[1] - rp[1], &unused[0], &unused[1]),
+                  Ops::pack2(p[2] - rp[2], p[3] - rp[3], &unused[2], &unused[3])};
+      l_part += (p[0] + p[1]) + (p[2] + p[3]);
+    } else {
+      l_part += (rp[0] + rp[1]) + (rp[2] + rp[3]);
+    }
     // P . V over the 16 tokens, one 16-wide slice of the head dimension at a time
 #pragma unroll
     for (int t = 0; t < NTILES; ++t) {
@@ -323,6 +358,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
       const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(vt + trow * PITCH + chunk * 16 + 8 * (c % 2)));
       cacc[t] = Ops::pv(pop, vb, cacc[t]);
+      if constexpr (SPLIT) cacc[t] = Ops::pv(plo, vb, cacc[t]);
     }
   };
 
@@ -370,15 +406,15 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
     const int hh = 4 * r + i;
     const float Li = __shfl(L, hh);
     const float Mi = __shfl(m_ref, hh);
-    const int sh = seq_of(hh), h = head_of(hh);  // row of query head hh
     if (hh < G) {
       if (a.num_slots == 0) {
-        uint16_t* o = (uint16_t*)a.out + ((size_t)sh * a.num_heads + h) * D + c;
+        uint16_t* o = (uint16_t*)a.out + row_of(hh) * D + c;
+        // a column that sees no token (possible under a draft mask) gives a zero row
+        const float inv = (Li > 0.f) ? a.v_scale / Li : 0.f;
 #pragma unroll
-        for (int t = 0; t < NTILES; ++t)
-          o[16 * t] = f32_to_store<QK>(cacc[t][i] / Li * a.v_scale);
+        for (int t = 0; t < NTILES; ++t) o[16 * t] = f32_to_store<QK>(cacc[t][i] * inv);
       } else {
-        const size_t pi = ((size_t)sh * a.num_heads + h) * a.num_slots + a.slot_base + part;
+        const size_t pi = row_of(hh) * a.num_slots + a.slot_base + part;
         float* pa_ = a.part_acc + pi * D + c;
 #pragma unroll
         for (int t = 0; t < NTILES; ++t) pa_[16 * t] = cacc[t][i];
@@ -394,7 +430,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 template <int D, int QK, int KVK, int G, bool NT>
 hipError_t launch_gqa_mfma_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((a.num_units + 3) / 4);
-  if (a.mode == MODE_PREFIX)
+  if (a.mode == MODE_PREFIX || a.mode == MODE_MULTI)
     hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true>), grid, dim3(256), 0,
                        stream, a);
   else

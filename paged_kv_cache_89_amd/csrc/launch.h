@@ -26,7 +26,12 @@ constexpr int kMaxUnitBlocks = 64;  // blocks one work unit (wavefront) walks at
 //     sequence's shared prefix; the walk starts at block ceil(min(prefix tokens, n) / B).
 // In both modes every unit writes its (m, l, acc) partial, empty or not, into slot
 // slot_base + part of the num_slots slots of each of its rows.
-enum DecodeMode : int32_t { MODE_PLAIN = 0, MODE_PREFIX = 1, MODE_SUFFIX = 2 };
+//
+// MODE_MULTI: query_len tokens per sequence (q and out are [S, query_len, Hq, D]); a
+// unit's query heads are its KV head's G heads for every query token, and query token
+// t sees the positions before n - query_len plus the draft positions n - query_len + u
+// whose bit u is set in tree_masks[s][t] (causal, bits 0..t, when tree_masks is null).
+enum DecodeMode : int32_t { MODE_PLAIN = 0, MODE_PREFIX = 1, MODE_SUFFIX = 2, MODE_MULTI = 3 };
 
 struct DecodeArgs {
   void* out;                 // [S, Hq, D] q dtype (written when num_slots == 0)
@@ -47,6 +52,8 @@ struct DecodeArgs {
   int32_t mode;              // DecodeMode
   int32_t seq_group, num_groups, max_prefix_blocks;
   const int32_t* prefix_blocks;  // [num_groups] shared leading blocks of each group
+  int32_t query_len;             // MODE_MULTI: query tokens per sequence
+  const uint32_t* tree_masks;    // MODE_MULTI: [S, query_len] or null (causal)
 };
 
 struct DecodeShape {

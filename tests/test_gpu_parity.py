@@ -186,6 +186,25 @@ def test_decode_ragged_lengths_all_variants(B, d, dt):
                 compare(out, ref, atol, rrel, qd)
 
 
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+def test_few_dominant_tokens_with_distant_values(qd):
+    """A handful of tokens share the weight and their values are far apart (+-4): the
+    output then amplifies any rounding of the weights, which must stay within the bar on
+    the matrix-core path (bf16 has only 8 significant bits for P)."""
+    lens = [2, 3, 5, 7, 16, 19]
+    for G in (2, 4, 8):
+        sp = workloads.Spec("few", len(lens), 4 * G, 4, 128, 16, 1, 1, 40, 3, qd, qd,
+                            1 / math.sqrt(128))
+        case = workloads.generate(sp, 77 + G, context_lens=lens)
+        rng = np.random.default_rng(G)
+        signs = rng.choice([-4.0, 4.0], case.v_src.shape).astype(np.float32)
+        case.v_src = workloads._round_bits(signs, qd)
+        tables, _, _ = oracle_tables(case)
+        k, v = oracle_caches(case, tables)
+        ref = oracle_decode(case, tables, k, v)
+        compare(_f64(_gpu_decode(case, tables, k, v, partition_size=0)), ref, 2e-3, 1e-2, qd)
+
+
 def test_single_token_returns_v1_bit_exact():
     for qd, kvd in (("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3")):
         sp = workloads.Spec("n1", 6, 8, 2, 128, 16, 1, 1, 12, 2, qd, kvd, 0.0883883)

@@ -197,3 +197,21 @@ def test_shared_prefix_workspace_and_errors_without_gpu():
     assert call(flags=4) == -1 and b"flag" in L.pa_last_error()
     assert call() == -1 and b"NULL" in L.pa_last_error()
     assert call(S=0) == 0                       # empty batch: nothing to do
+
+
+def test_multi_token_workspace_and_errors_without_gpu():
+    # rows are (sequence, query token, head): 4 x 3 x 8 rows of 4 partitions
+    assert pa.decode_multi_workspace_size(4, 3, 8, 8, 64, 16, 2000, 512) == 4 * 3 * 8 * 4 * 66 * 4
+    assert pa.decode_multi_workspace_size(4, 3, 8, 8, 64, 16, 200, 0) == 0
+    assert pa.decode_multi_workspace_size(4, 0, 8, 8, 64, 16, 200, 0) == 0
+    L = pa.lib()
+
+    def call(S=2, T=4, Hq=8, Hkv=8, d=128, B=16, q=1, kv=1, flags=0):
+        return L.pa_decode_multi(None, None, None, None, None, None, None, S, T, Hq, Hkv, d, B,
+                                 8, 64, 128, 0.1, q, kv, 1.0, 1.0, 0, flags, None, 0, None)
+    assert call(B=32) == -2 and b"block_size 16" in L.pa_last_error()
+    assert call(T=1) == -2                      # one column: use pa_decode
+    assert call(T=8, Hq=16, Hkv=4) == -2        # 8 tokens x 4 heads = 32 columns > 16
+    assert call(T=8, Hq=8, Hkv=4) == -1         # 16 columns: supported, NULL pointers
+    assert call(T=0) == -1
+    assert call(S=0) == 0
