@@ -67,6 +67,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of 1 GiB (for hardware-counter scaling)")
+    ap.add_argument("--swap", type=int, default=0, metavar="N",
+                    help="also time pa_swap_blocks moving the blocks of the first N sequences "
+                         "to pinned host memory and back, beside a DMA copy of the same bytes")
     return ap.parse_args()
 
 
@@ -184,6 +187,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    swap = swap_leg(sp, kc, vc, tables, args.swap) if args.swap > 0 else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, args.cpu_seconds)
@@ -222,7 +227,56 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if swap is not None:
+        line["swap"] = swap
     print(json.dumps(line), flush=True)
+
+
+def swap_leg(sp, kc, vc, tables, nseq):
+    """Preemption by swapping: the distinct blocks of the first nseq sequences (K and V)
+    moved device -> pinned host and back with pa_swap_blocks (one launch each way, reading
+    or writing host memory directly over the host link), beside torch's DMA copy of the
+    same number of contiguous bytes each way.  GB/s = moved bytes / mean time."""
+    import torch
+
+    import paged_kv_cache_89_amd as pa
+
+    rows = tables[:nseq]
+    ids = np.unique(rows[rows >= 0]).astype(np.int32)
+    n = int(ids.size)
+    hk = torch.empty((n,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    out_pairs = torch.from_numpy(np.stack([ids, np.arange(n, dtype=np.int32)], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([np.arange(n, dtype=np.int32), ids], 1)).cuda()
+    nbytes = 2 * n * hk[0].numel() * hk.element_size()
+    dk = torch.empty(hk.shape, dtype=kc.dtype, device="cuda")
+    dv = torch.empty_like(dk)
+    hk2, hv2 = torch.empty_like(hk, pin_memory=True), torch.empty_like(hv, pin_memory=True)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_out = timed(lambda: pa.swap_blocks(kc, vc, hk, hv, out_pairs, stream=stream))
+    t_in = timed(lambda: pa.swap_blocks(hk, hv, kc, vc, in_pairs, stream=stream))
+    t_dma_out = timed(lambda: (hk2.copy_(dk, non_blocking=True), hv2.copy_(dv, non_blocking=True)))
+    t_dma_in = timed(lambda: (dk.copy_(hk2, non_blocking=True), dv.copy_(hv2, non_blocking=True)))
+
+    def gbs(ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 2)
+
+    return {"sequences": nseq, "blocks": n, "bytes_each_way": nbytes,
+            "out_GBps": gbs(t_out), "in_GBps": gbs(t_in),
+            "dma_out_GBps": gbs(t_dma_out), "dma_in_GBps": gbs(t_dma_in),
+            "out_ms": round(t_out, 4), "in_ms": round(t_in, 4)}
 
 
 def cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, target_s):

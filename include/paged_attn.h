@@ -134,7 +134,42 @@ pa_status pa_bm_append(pa_block_manager* bm, int32_t n, const int32_t* seq_handl
                        int32_t* slot_blocks, int32_t* slot_offsets, int32_t* copies,
                        int32_t max_copies, int32_t* num_copies);
 
-/* Current table rows and lengths of live sequences: block_tables host out
+/* ------------------------------------------------------------------------------------
+ * Swapping ([P1] sec. 6, preemption by swapping: a preempted request's blocks are evicted
+ * from HBM to host RAM and brought back when it resumes; the cost is bounded by the host
+ * link).  The manager keeps an optional pool of host slots with its own FIFO free list
+ * (ascending ids) and reference counts; the data moves with pa_swap_blocks.
+ *
+ * pa_bm_host_pool: (re)size the host pool to num_host_blocks slots; refused while any slot
+ * is referenced. */
+pa_status pa_bm_host_pool(pa_block_manager* bm, int32_t num_host_blocks);
+
+/* host_refcounts host out [num_host_blocks] (may be NULL), num_host_free (may be NULL). */
+pa_status pa_bm_host_stats(const pa_block_manager* bm, int32_t* host_refcounts,
+                           int32_t* num_host_free);
+
+/* Swap out a gang of live, resident sequences (e.g. all samples of one request): every
+ * distinct block they reference (first appearance in handle order, then table order)
+ * takes a host slot from the front of the host free list; the gang's tables then name host
+ * slots (sharing inside the gang is kept), each device block loses the gang's references
+ * and returns to the back of the device free list at zero.  block_pairs host out
+ * [max_pairs][2] receives (device block, host slot) for every move, *num_pairs their
+ * count: copy them (pa_swap_blocks, device pools -> host pools) before the released
+ * device blocks are written again.  Swapped-out sequences can only be swapped in or freed
+ * (pa_bm_free releases their host slots).  All-or-nothing: too few host slots
+ * (PA_ERR_NO_BLOCKS), max_pairs too small or a handle that is not a live resident
+ * sequence or is repeated (PA_ERR_INVALID_ARG) change nothing. */
+pa_status pa_bm_swap_out(pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
+                         int32_t* block_pairs, int32_t max_pairs, int32_t* num_pairs);
+
+/* Swap a gang of swapped-out sequences back in: every distinct host slot they reference
+ * takes a block from the front of the device free list; block_pairs receives (host slot,
+ * device block) per move (copy host pools -> device pools with pa_swap_blocks before the
+ * sequences are decoded).  Same rules and errors as pa_bm_swap_out, roles exchanged. */
+pa_status pa_bm_swap_in(pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
+                        int32_t* block_pairs, int32_t max_pairs, int32_t* num_pairs);
+
+/* Current table rows and lengths of live, resident sequences: block_tables host out
  * [n, max_blocks_per_seq] (-1 padded), context_lens host out [n] (may be NULL).
  * PA_ERR_TABLE_OVERFLOW if a row does not fit. */
 pa_status pa_bm_table(const pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
@@ -173,6 +208,21 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pair
                          int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
                          int32_t block_size, int32_t head_dim, pa_dtype cache_dtype,
                          void* stream);
+
+/* Batched move of blocks between two pools (swap-out: device -> host; swap-in: host ->
+ * device), [P1] sec. 6.  Pools are [blocks][num_kv_heads][block_size][head_dim] of
+ * cache_dtype, K and V each; src_blocks / dst_blocks give their sizes in blocks (the
+ * caller guarantees the allocations hold that many).  block_pairs: [num_pairs][2] int32 of
+ * (src block, dst block), e.g. from pa_bm_swap_out / pa_bm_swap_in.  Every pointer must be
+ * device memory or pinned host memory mapped for the device (hipHostMalloc, torch
+ * pin_memory); anything else is refused with PA_ERR_INVALID_ARG before any launch.  One
+ * launch moves all pairs; a work-item copies 16 bytes, so host memory is written or read
+ * directly over the host link (no staging copy).  Pairs naming an id outside its pool are
+ * skipped. */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const int32_t* block_pairs, int32_t num_pairs, int32_t src_blocks,
+                         int32_t dst_blocks, int32_t num_kv_heads, int32_t block_size,
+                         int32_t head_dim, pa_dtype cache_dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Decode attention.

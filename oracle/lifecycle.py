@@ -14,12 +14,17 @@ Plain Python, written from the pages:
 * same page, sec. 7, fusion 3: all copies of one step are done by one batched copy.
 * "Pytorch implementation of paper ..." sec. 3: blocks leave the free list from the front
   and return at its back.
+* "PagedAttention: Mathematical Foundations, ..." sec. 6, preemption by swapping: the
+  blocks of a preempted request are evicted to host RAM and brought back on resume.
 
 Readings: a sequence's next token goes to slot len % B of logical block len // B; when
 len % B == 0 that block does not exist yet (overflow: pop one block); otherwise, if the
 last block's reference count exceeds 1, it is copied first (copy-on-write).  Appends in
 one call are applied in the order given.  A call that would need more blocks than are
-free changes nothing.
+free changes nothing.  Swapping moves a gang of sequences (e.g. all samples of a request)
+at once: each distinct block of the gang gets one slot on the other side (host slots
+from their own FIFO list, ascending initially), in order of first appearance (gang order,
+then table order); the old side loses the gang's references.
 """
 from __future__ import annotations
 
@@ -33,6 +38,7 @@ class _Seq:
     blocks: list
     length: int
     live: bool = True
+    swapped: bool = False
 
 
 @dataclass
@@ -43,10 +49,54 @@ class LifecycleOracle:
     refs: list = field(default_factory=list)
     seqs: list = field(default_factory=list)
 
+    host_free: list = field(default_factory=list)
+    host_refs: list = field(default_factory=list)
+
     @classmethod
     def create(cls, num_blocks, block_size, free_order=None):
         order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
         return cls(num_blocks, block_size, order, [0] * num_blocks, [])
+
+    def host_pool(self, n):
+        assert all(r == 0 for r in self.host_refs)
+        self.host_free = list(range(n))
+        self.host_refs = [0] * n
+
+    def _move(self, handles, out):
+        """Swap a gang out (device -> host) or in; returns the (old, new) id pairs or
+        None when the other side has too few free ids (nothing changes)."""
+        for h in handles:
+            assert self.seqs[h].live and self.seqs[h].swapped == (not out)
+        assert len(set(handles)) == len(handles)
+        order = []
+        for h in handles:
+            for b in self.seqs[h].blocks:
+                if b not in order:
+                    order.append(b)
+        from_refs, to_refs = (self.refs, self.host_refs) if out else (self.host_refs, self.refs)
+        from_free, to_free = (self.free, self.host_free) if out else (self.host_free, self.free)
+        if len(order) > len(to_free):
+            return None
+        new = {}
+        for b in order:
+            new[b] = to_free.pop(0)
+            to_refs[new[b]] = 0
+        for h in handles:
+            seq = self.seqs[h]
+            for j, b in enumerate(seq.blocks):
+                from_refs[b] -= 1
+                if from_refs[b] == 0:
+                    from_free.append(b)
+                to_refs[new[b]] += 1
+                seq.blocks[j] = new[b]
+            seq.swapped = out
+        return [(b, new[b]) for b in order]
+
+    def swap_out(self, handles):
+        return self._move(list(handles), True)
+
+    def swap_in(self, handles):
+        return self._move(list(handles), False)
 
     # -- allocation of new sequences (same rule as the table builder of oracle.cpp)
     def alloc(self, context_lens, prefix_group=None, prefix_lens=None):
@@ -86,7 +136,7 @@ class LifecycleOracle:
     def fork(self, parent, n):
         """n new sequences sharing every block of `parent` (parallel sampling)."""
         p = self.seqs[parent]
-        assert p.live
+        assert p.live and not p.swapped
         out = []
         for _ in range(n):
             for b in p.blocks:
@@ -99,6 +149,7 @@ class LifecycleOracle:
         """Reserve the next token's slot of every handle, in order.  Returns
         (blocks, slots, copies) or None when the free list is too short (no change)."""
         B = self.block_size
+        assert all(self.seqs[h].live and not self.seqs[h].swapped for h in handles)
         # dry run on copies of the counters
         refs = list(self.refs)
         lens = {h: self.seqs[h].length for h in handles}
@@ -143,10 +194,12 @@ class LifecycleOracle:
         for h in handles:
             seq = self.seqs[h]
             assert seq.live
+            refs, free = (self.host_refs, self.host_free) if seq.swapped else (self.refs, self.free)
             for b in seq.blocks:
-                self.refs[b] -= 1
-                if self.refs[b] == 0:
-                    self.free.append(b)
+                refs[b] -= 1
+                if refs[b] == 0:
+                    free.append(b)
+            seq.swapped = False
             seq.blocks = []
             seq.live = False
 

@@ -68,6 +68,11 @@ def lib() -> ctypes.CDLL:
     L.pa_bm_fork.argtypes = [vp, i32, i32, vp]
     L.pa_bm_append.argtypes = [vp, i32, vp, vp, vp, vp, i32, vp]
     L.pa_bm_table.argtypes = [vp, i32, vp, i32, vp, vp]
+    L.pa_bm_host_pool.argtypes = [vp, i32]
+    L.pa_bm_host_stats.argtypes = [vp, vp, vp]
+    L.pa_bm_swap_out.argtypes = [vp, i32, vp, vp, i32, vp]
+    L.pa_bm_swap_in.argtypes = [vp, i32, vp, vp, i32, vp]
+    L.pa_swap_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, c.c_int, vp]
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, c.c_int, vp]
     L.pa_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32,
                               c.c_int, c.c_int, f32, f32, vp]
@@ -91,6 +96,8 @@ def lib() -> ctypes.CDLL:
     for name in ("pa_bm_create", "pa_alloc_tables", "pa_bm_free", "pa_bm_stats",
                  "pa_bm_free_list", "pa_bm_fork", "pa_bm_append", "pa_bm_table",
                  "pa_copy_blocks", "pa_write_kv", "pa_decode_plan", "pa_decode",
+                 "pa_bm_host_pool", "pa_bm_host_stats", "pa_bm_swap_out", "pa_bm_swap_in",
+                 "pa_swap_blocks",
                  "pa_decode_shared_prefix", "pa_decode_multi"):
         getattr(L, name).restype = c.c_int
     _lib = L
@@ -186,6 +193,36 @@ class BlockManager:
                                   _ptr(copies), copies.shape[0], _ptr(nc)))
         return blocks, offs, copies[: nc[0]].copy()
 
+    def host_pool(self, num_host_blocks: int):
+        """Give the manager num_host_blocks host slots for swapping."""
+        _check(lib().pa_bm_host_pool(self._h, int(num_host_blocks)))
+        self.num_host_blocks = int(num_host_blocks)
+
+    def host_stats(self):
+        """(host refcounts int32 [num_host_blocks], num_host_free)."""
+        n = getattr(self, "num_host_blocks", 0)
+        ref = np.empty(max(n, 1), np.int32)
+        nf = np.zeros(1, np.int32)
+        _check(lib().pa_bm_host_stats(self._h, _ptr(ref), _ptr(nf)))
+        return ref[:n].copy(), int(nf[0])
+
+    def _swap(self, fn, seq_handles, max_pairs):
+        h = _np(seq_handles)
+        pairs = np.empty((max(int(max_pairs), 1), 2), np.int32)
+        n = np.zeros(1, np.int32)
+        _check(fn(self._h, h.size, _ptr(h), _ptr(pairs), int(max_pairs), _ptr(n)))
+        return pairs[: n[0]].copy()
+
+    def swap_out(self, seq_handles, max_pairs: int | None = None) -> np.ndarray:
+        """Move a gang of sequences to host slots; returns (device block, host slot) pairs."""
+        cap = self.num_blocks if max_pairs is None else max_pairs
+        return self._swap(lib().pa_bm_swap_out, seq_handles, cap)
+
+    def swap_in(self, seq_handles, max_pairs: int | None = None) -> np.ndarray:
+        """Bring a swapped-out gang back; returns (host slot, device block) pairs."""
+        cap = getattr(self, "num_host_blocks", 0) if max_pairs is None else max_pairs
+        return self._swap(lib().pa_bm_swap_in, seq_handles, cap)
+
     def table(self, seq_handles, max_blocks_per_seq: int):
         """(block_tables [n, MB], context_lens [n]) of live sequences."""
         h = _np(seq_handles)
@@ -226,6 +263,31 @@ def _dev(t, name):
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous GPU tensor")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _mapped(t, name):
+    """A device tensor, or a pinned host tensor (the library maps it for the device)."""
+    if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a contiguous GPU tensor or pinned host tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_pairs, stream=None):
+    """pa_swap_blocks: dst block pairs[i][1] of (dst_k, dst_v) receives src block
+    pairs[i][0] of (src_k, src_v).  Pools [blocks, Hkv, B, D]; each is a GPU tensor or a
+    pinned host tensor; block_pairs [n, 2] int32 (GPU or pinned)."""
+    NBs, Hkv, B, D = src_k.shape
+    NBd = dst_k.shape[0]
+    if (src_v.shape != src_k.shape or tuple(dst_k.shape[1:]) != (Hkv, B, D)
+            or dst_v.shape != dst_k.shape or src_k.dtype != dst_k.dtype):
+        raise ValueError("swap_blocks: pool shape or dtype mismatch")
+    n = int(block_pairs.shape[0]) if block_pairs.numel() else 0
+    if n and (block_pairs.dim() != 2 or block_pairs.shape[1] != 2):
+        raise ValueError("swap_blocks: block_pairs must be [n, 2]")
+    _check(lib().pa_swap_blocks(
+        _mapped(src_k, "src_k"), _mapped(src_v, "src_v"), _mapped(dst_k, "dst_k"),
+        _mapped(dst_v, "dst_v"), _mapped(block_pairs, "block_pairs") if n else None, n, NBs, NBd,
+        Hkv, B, D, _dtype_code(src_k), _stream(stream)))
 
 
 def write_kv(k_src, v_src, k_cache, v_cache, block_tables, seq_ids, positions,

@@ -194,8 +194,65 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pair
     return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block size in bytes must be a multiple of 16");
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: NULL pointer");
-  CopyArgs a{k_cache, v_cache, block_pairs, num_pairs, num_blocks, bytes};
+  CopyArgs a{k_cache, v_cache, k_cache, v_cache, block_pairs, num_pairs, num_blocks, num_blocks,
+             bytes};
   return hip_status(launch_copy_blocks(a, (hipStream_t)stream), "pa_copy_blocks launch");
+}
+
+// Device-visible address of a pool: device memory as is; pinned host memory through its
+// mapping.  Anything else (pageable host memory, unknown pointers) is refused, so the
+// kernel never touches an address the device cannot reach.
+static pa_status device_view(const void* p, const char* name, void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID_ARG, std::string("pa_swap_blocks: ") + name +
+                                        " is neither device memory nor pinned host memory");
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = const_cast<void*>(p);
+    return PA_OK;
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || !d) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_INVALID_ARG, std::string("pa_swap_blocks: ") + name +
+                                          " is host memory without a device mapping");
+    }
+    *out = d;
+    return PA_OK;
+  }
+  return fail(PA_ERR_INVALID_ARG, std::string("pa_swap_blocks: ") + name +
+                                      " is neither device memory nor pinned host memory (type " +
+                                      std::to_string((int)attr.type) + ")");
+}
+
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const int32_t* block_pairs, int32_t num_pairs, int32_t src_blocks,
+                         int32_t dst_blocks, int32_t num_kv_heads, int32_t block_size,
+                         int32_t head_dim, pa_dtype cache_dtype, void* stream) {
+  g_last_error.clear();
+  int ck;
+  if (!dtype_kind(cache_dtype, &ck)) return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: unknown dtype");
+  if (num_pairs < 0 || src_blocks < 1 || dst_blocks < 1 || num_kv_heads < 1 || block_size < 1 ||
+      head_dim < 1)
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: bad size");
+  const int64_t bytes = (int64_t)num_kv_heads * block_size * head_dim * (ck == KIND_E4M3 ? 1 : 2);
+  if (bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: block size in bytes must be a multiple of 16");
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs)
+    return fail(PA_ERR_INVALID_ARG, "pa_swap_blocks: NULL pointer");
+  void *sk, *sv, *dk, *dv, *pp;
+  pa_status st;
+  if ((st = device_view(src_k, "src_k", &sk)) != PA_OK) return st;
+  if ((st = device_view(src_v, "src_v", &sv)) != PA_OK) return st;
+  if ((st = device_view(dst_k, "dst_k", &dk)) != PA_OK) return st;
+  if ((st = device_view(dst_v, "dst_v", &dv)) != PA_OK) return st;
+  if ((st = device_view(block_pairs, "block_pairs", &pp)) != PA_OK) return st;
+  CopyArgs a{sk, sv, dk, dv, (const int32_t*)pp, num_pairs, src_blocks, dst_blocks, bytes};
+  return hip_status(launch_copy_blocks(a, (hipStream_t)stream), "pa_swap_blocks launch");
 }
 
 pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

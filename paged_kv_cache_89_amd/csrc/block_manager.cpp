@@ -9,6 +9,10 @@
 //
 // The free list is a ring buffer of capacity num_blocks (it can never hold more), so both
 // ends are O(1) and the list keeps its exact order.
+//
+// Swapping (same page, sec. 6: a preempted request's blocks are evicted to host RAM and
+// brought back on resume): an optional host pool of slots with its own free list and
+// reference counts.  A swapped-out sequence's table holds host slot ids.
 #include <stdint.h>
 
 #include <string>
@@ -18,29 +22,44 @@
 
 void pa_set_error(const std::string& msg);  // defined in api.hip
 
-struct pa_block_manager {
-  int32_t num_blocks = 0;
-  int32_t block_size = 0;
-  std::vector<int32_t> ring;     // free ids, ring[(head + k) % num_blocks], k < free_count
+// FIFO free list over ids 0..capacity-1 (ring buffer).
+struct FreeRing {
+  std::vector<int32_t> ring;     // free ids, ring[(head + k) % capacity], k < count
   int64_t head = 0;
-  int64_t free_count = 0;
-  std::vector<int32_t> refs;     // references per physical block
-  struct Seq {
-    std::vector<int32_t> blocks; // logical block j -> physical id
-    int32_t context_len = 0;
-    bool live = false;
-  };
-  std::vector<Seq> seqs;         // indexed by handle
-
+  int64_t count = 0;
   int32_t pop_front() {
     const int32_t id = ring[head];
-    head = (head + 1) % num_blocks;
-    --free_count;
+    head = (head + 1) % (int64_t)ring.size();
+    --count;
     return id;
   }
   void push_back(int32_t id) {
-    ring[(head + free_count) % num_blocks] = id;
-    ++free_count;
+    ring[(head + count) % (int64_t)ring.size()] = id;
+    ++count;
+  }
+  int32_t at(int64_t k) const { return ring[(head + k) % (int64_t)ring.size()]; }
+};
+
+struct pa_block_manager {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  FreeRing dev;                  // device free list
+  std::vector<int32_t> refs;     // references per physical block
+  FreeRing host;                 // host slot free list (empty until pa_bm_host_pool)
+  std::vector<int32_t> host_refs;
+  struct Seq {
+    std::vector<int32_t> blocks; // logical block j -> physical id (host slot if swapped)
+    int32_t context_len = 0;
+    bool live = false;
+    bool swapped = false;
+  };
+  std::vector<Seq> seqs;         // indexed by handle
+
+  int64_t free_count() const { return dev.count; }
+  int32_t pop_front() { return dev.pop_front(); }
+  void push_back(int32_t id) { dev.push_back(id); }
+  bool resident(int32_t h) const {
+    return h >= 0 && h < (int32_t)seqs.size() && seqs[h].live && !seqs[h].swapped;
   }
 };
 
@@ -72,8 +91,8 @@ pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* fr
   auto* bm = new pa_block_manager();
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
-  bm->ring = std::move(ring);
-  bm->free_count = num_blocks;
+  bm->dev.ring = std::move(ring);
+  bm->dev.count = num_blocks;
   bm->refs.assign(num_blocks, 0);
   *out = bm;
   return PA_OK;
@@ -126,9 +145,9 @@ pa_status pa_alloc_tables(pa_block_manager* bm, int32_t num_seqs, const int32_t*
     }
     need += nb - shared;
   }
-  if (need > bm->free_count) {
+  if (need > bm->free_count()) {
     pa_set_error("pa_alloc_tables: need " + std::to_string(need) + " blocks, " +
-                 std::to_string(bm->free_count) + " free");
+                 std::to_string(bm->free_count()) + " free");
     return PA_ERR_NO_BLOCKS;
   }
   // Commit.
@@ -177,8 +196,14 @@ pa_status pa_bm_free(pa_block_manager* bm, int32_t n, const int32_t* seq_handles
   }
   for (int32_t k = 0; k < n; ++k) {
     auto& seq = bm->seqs[seq_handles[k]];
-    for (int32_t id : seq.blocks)
-      if (--bm->refs[id] == 0) bm->push_back(id);
+    if (seq.swapped) {  // its blocks live in host slots
+      for (int32_t id : seq.blocks)
+        if (--bm->host_refs[id] == 0) bm->host.push_back(id);
+    } else {
+      for (int32_t id : seq.blocks)
+        if (--bm->refs[id] == 0) bm->push_back(id);
+    }
+    seq.swapped = false;
     seq.blocks.clear();
     seq.blocks.shrink_to_fit();
     seq.live = false;
@@ -194,11 +219,12 @@ pa_status pa_bm_stats(const pa_block_manager* bm, int32_t* refcounts, int32_t* n
   }
   if (refcounts)
     for (int32_t b = 0; b < bm->num_blocks; ++b) refcounts[b] = bm->refs[b];
-  if (num_free) *num_free = (int32_t)bm->free_count;
+  if (num_free) *num_free = (int32_t)bm->free_count();
   if (waste_slots) {
     int64_t w = 0;
     for (const auto& seq : bm->seqs)
-      if (seq.live) w += (int64_t)seq.blocks.size() * bm->block_size - seq.context_len;
+      if (seq.live && !seq.swapped)
+        w += (int64_t)seq.blocks.size() * bm->block_size - seq.context_len;
     *waste_slots = w;
   }
   return PA_OK;
@@ -210,16 +236,15 @@ pa_status pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int32_t capa
     pa_set_error("pa_bm_free_list: invalid arguments");
     return PA_ERR_INVALID_ARG;
   }
-  *count = (int32_t)bm->free_count;
-  const int64_t k_end = bm->free_count < capacity ? bm->free_count : capacity;
-  for (int64_t k = 0; k < k_end; ++k) out[k] = bm->ring[(bm->head + k) % bm->num_blocks];
+  *count = (int32_t)bm->free_count();
+  const int64_t k_end = bm->free_count() < capacity ? bm->free_count() : capacity;
+  for (int64_t k = 0; k < k_end; ++k) out[k] = bm->dev.at(k);
   return PA_OK;
 }
 
 pa_status pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t n, int32_t* child_handles) {
-  if (!bm || n < 0 || (n > 0 && !child_handles) || parent < 0 ||
-      parent >= (int32_t)bm->seqs.size() || !bm->seqs[parent].live) {
-    pa_set_error("pa_bm_fork: invalid arguments or parent is not a live sequence");
+  if (!bm || n < 0 || (n > 0 && !child_handles) || !bm->resident(parent)) {
+    pa_set_error("pa_bm_fork: invalid arguments or parent is not a live, resident sequence");
     return PA_ERR_INVALID_ARG;
   }
   for (int32_t k = 0; k < n; ++k) {
@@ -245,8 +270,9 @@ pa_status pa_bm_append(pa_block_manager* bm, int32_t n, const int32_t* seq_handl
   const int32_t B = bm->block_size;
   for (int32_t k = 0; k < n; ++k) {
     const int32_t h = seq_handles[k];
-    if (h < 0 || h >= (int32_t)bm->seqs.size() || !bm->seqs[h].live) {
-      pa_set_error("pa_bm_append: handle " + std::to_string(h) + " is not a live sequence");
+    if (!bm->resident(h)) {
+      pa_set_error("pa_bm_append: handle " + std::to_string(h) +
+                   " is not a live, resident sequence");
       return PA_ERR_INVALID_ARG;
     }
   }
@@ -285,9 +311,9 @@ pa_status pa_bm_append(pa_block_manager* bm, int32_t n, const int32_t* seq_handl
       fresh_tail[k] = 1;
     }
   }
-  if (need > bm->free_count) {
+  if (need > bm->free_count()) {
     pa_set_error("pa_bm_append: need " + std::to_string(need) + " blocks, " +
-                 std::to_string(bm->free_count) + " free");
+                 std::to_string(bm->free_count()) + " free");
     return PA_ERR_NO_BLOCKS;
   }
   if (ncopy > max_copies) {
@@ -329,8 +355,9 @@ pa_status pa_bm_table(const pa_block_manager* bm, int32_t n, const int32_t* seq_
   }
   for (int32_t k = 0; k < n; ++k) {
     const int32_t h = seq_handles[k];
-    if (h < 0 || h >= (int32_t)bm->seqs.size() || !bm->seqs[h].live) {
-      pa_set_error("pa_bm_table: handle " + std::to_string(h) + " is not a live sequence");
+    if (!bm->resident(h)) {
+      pa_set_error("pa_bm_table: handle " + std::to_string(h) +
+                   " is not a live, resident sequence");
       return PA_ERR_INVALID_ARG;
     }
     if ((int32_t)bm->seqs[h].blocks.size() > max_blocks_per_seq) {
@@ -346,6 +373,112 @@ pa_status pa_bm_table(const pa_block_manager* bm, int32_t n, const int32_t* seq_
     if (context_lens) context_lens[k] = seq.context_len;
   }
   return PA_OK;
+}
+
+pa_status pa_bm_host_pool(pa_block_manager* bm, int32_t num_host_blocks) {
+  if (!bm || num_host_blocks < 0) {
+    pa_set_error("pa_bm_host_pool: invalid arguments");
+    return PA_ERR_INVALID_ARG;
+  }
+  for (int32_t r : bm->host_refs)
+    if (r != 0) {
+      pa_set_error("pa_bm_host_pool: host slots are in use");
+      return PA_ERR_INVALID_ARG;
+    }
+  bm->host.ring.resize(num_host_blocks);
+  for (int32_t k = 0; k < num_host_blocks; ++k) bm->host.ring[k] = k;
+  bm->host.head = 0;
+  bm->host.count = num_host_blocks;
+  bm->host_refs.assign(num_host_blocks, 0);
+  return PA_OK;
+}
+
+pa_status pa_bm_host_stats(const pa_block_manager* bm, int32_t* host_refcounts,
+                           int32_t* num_host_free) {
+  if (!bm) {
+    pa_set_error("pa_bm_host_stats: NULL manager");
+    return PA_ERR_INVALID_ARG;
+  }
+  if (host_refcounts)
+    for (size_t k = 0; k < bm->host_refs.size(); ++k) host_refcounts[k] = bm->host_refs[k];
+  if (num_host_free) *num_host_free = (int32_t)bm->host.count;
+  return PA_OK;
+}
+
+// Move a gang of sequences between the device pool and the host pool.  Every distinct
+// block the gang references (first appearance in handle order, then table order) gets one
+// new block on the other side; sharing inside the gang is kept, references from outside
+// the gang stay on the old side.  All-or-nothing.
+static pa_status swap_gang(pa_block_manager* bm, bool out, int32_t n, const int32_t* handles,
+                           int32_t* pairs, int32_t max_pairs, int32_t* num_pairs) {
+  const char* who = out ? "pa_bm_swap_out" : "pa_bm_swap_in";
+  if (!bm || n < 0 || max_pairs < 0 || !num_pairs || (n > 0 && !handles) ||
+      (max_pairs > 0 && !pairs)) {
+    pa_set_error(std::string(who) + ": invalid arguments");
+    return PA_ERR_INVALID_ARG;
+  }
+  std::vector<char> hit(bm->seqs.size(), 0);
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t h = handles[k];
+    if (h < 0 || h >= (int32_t)bm->seqs.size() || !bm->seqs[h].live || hit[h] ||
+        bm->seqs[h].swapped != !out) {
+      pa_set_error(std::string(who) + ": handle " + std::to_string(h) + " is not a live " +
+                   (out ? "resident" : "swapped-out") + " sequence (or is repeated)");
+      return PA_ERR_INVALID_ARG;
+    }
+    hit[h] = 1;
+  }
+  std::vector<int32_t>& from_refs = out ? bm->refs : bm->host_refs;
+  std::vector<int32_t>& to_refs = out ? bm->host_refs : bm->refs;
+  FreeRing& from_free = out ? bm->dev : bm->host;
+  FreeRing& to_free = out ? bm->host : bm->dev;
+  std::vector<int32_t> order;               // distinct old ids, first appearance
+  std::vector<int32_t> slot(from_refs.size(), -1);
+  for (int32_t k = 0; k < n; ++k)
+    for (int32_t id : bm->seqs[handles[k]].blocks)
+      if (slot[id] == -1) {
+        slot[id] = (int32_t)order.size();
+        order.push_back(id);
+      }
+  if ((int64_t)order.size() > to_free.count) {
+    pa_set_error(std::string(who) + ": need " + std::to_string(order.size()) + " " +
+                 (out ? "host slots" : "blocks") + ", " + std::to_string(to_free.count) + " free");
+    return PA_ERR_NO_BLOCKS;
+  }
+  if ((int64_t)order.size() > max_pairs) {
+    pa_set_error(std::string(who) + ": " + std::to_string(order.size()) +
+                 " block moves exceed max_pairs");
+    return PA_ERR_INVALID_ARG;
+  }
+  std::vector<int32_t> target(order.size());
+  for (size_t q = 0; q < order.size(); ++q) {
+    target[q] = to_free.pop_front();
+    to_refs[target[q]] = 0;
+    pairs[2 * q] = order[q];
+    pairs[2 * q + 1] = target[q];
+  }
+  for (int32_t k = 0; k < n; ++k) {
+    auto& seq = bm->seqs[handles[k]];
+    for (int32_t& id : seq.blocks) {
+      const int32_t nid = target[slot[id]];
+      if (--from_refs[id] == 0) from_free.push_back(id);
+      to_refs[nid] += 1;
+      id = nid;
+    }
+    seq.swapped = out;
+  }
+  *num_pairs = (int32_t)order.size();
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_out(pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
+                         int32_t* block_pairs, int32_t max_pairs, int32_t* num_pairs) {
+  return swap_gang(bm, true, n, seq_handles, block_pairs, max_pairs, num_pairs);
+}
+
+pa_status pa_bm_swap_in(pa_block_manager* bm, int32_t n, const int32_t* seq_handles,
+                        int32_t* block_pairs, int32_t max_pairs, int32_t* num_pairs) {
+  return swap_gang(bm, false, n, seq_handles, block_pairs, max_pairs, num_pairs);
 }
 
 }  // extern "C"

@@ -94,10 +94,12 @@ hipError_t launch_write_kv(int head_dim, int block_size, int src_kind, int cache
                            const WriteArgs& a, hipStream_t stream);
 
 struct CopyArgs {
-  void* k_cache;
-  void* v_cache;
-  const int32_t* pairs;      // [num_pairs][2]: (src, dst) physical block ids
-  int32_t num_pairs, num_blocks;
+  const void* src_k;         // source pools (may equal the destination pools)
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int32_t* pairs;      // [num_pairs][2]: (src, dst) block ids
+  int32_t num_pairs, src_blocks, dst_blocks;
   int64_t block_bytes;       // Hkv * B * d * e, a multiple of 16
 };
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);

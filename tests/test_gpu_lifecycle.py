@@ -113,3 +113,176 @@ def test_parallel_sampling_copy_on_write_end_to_end(kv, q):
         atol, rrel = (2e-2, None) if kv == "e4m3" else (2e-3, 1e-2)
         compare(out.double().cpu().numpy(), ref, atol, rrel, q)
     assert np.array_equal(to_bits(kd), k_or) and np.array_equal(to_bits(vd), v_or)
+
+
+def _pinned_like(a: np.ndarray, dtype: str):
+    """Pinned host tensor holding the storage bits of `a`, typed like to_dev()'s tensors."""
+    t = torch.empty(a.shape, dtype=torch.uint8 if dtype == "e4m3" else torch.int16,
+                    pin_memory=True)
+    t.copy_(torch.from_numpy(np.ascontiguousarray(a).view(np.uint8 if dtype == "e4m3" else np.int16)))
+    if dtype == "e4m3":
+        return t
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+
+
+@pytest.mark.parametrize("kv", ["f16", "e4m3"])
+@pytest.mark.parametrize("pairs_on_host", [False, True])
+def test_swap_blocks_bit_exact(kv, pairs_on_host):
+    """Device pool -> pinned host pool and back in one launch each: moved blocks are equal
+    bit for bit, everything else untouched, out-of-range pairs skipped."""
+    rng = np.random.default_rng(8)
+    sp = workloads.Spec("s", 1, 8, 4, 128, 16, 1, 1, 48, 4, "bf16", kv, 0.1)
+    hsp = workloads.Spec("h", 1, 8, 4, 128, 16, 1, 1, 20, 4, "bf16", kv, 0.1)
+
+    def rand_pool(spec):
+        a = workloads.empty_cache(spec, poison=False)
+        a[:] = rng.integers(0, 1 << (8 * a.itemsize), a.shape, dtype=np.uint64).astype(a.dtype)
+        return a
+
+    k, v, hk0, hv0 = rand_pool(sp), rand_pool(sp), rand_pool(hsp), rand_pool(hsp)
+    kd, vd = to_dev(k, kv), to_dev(v, kv)
+    hk, hv = _pinned_like(hk0, kv), _pinned_like(hv0, kv)
+    dev_ids, host_ids = rng.permutation(48)[:12], rng.permutation(20)[:12]
+
+    def pairs_arg(p, n_src, n_dst):
+        p = np.concatenate([p, [[n_src, 0], [0, n_dst], [-1, 3]]]).astype(np.int32)  # skipped
+        t = torch.from_numpy(p)
+        return t.pin_memory() if pairs_on_host else t.cuda()
+
+    out_pairs = np.stack([dev_ids, host_ids], 1)
+    pa.swap_blocks(kd, vd, hk, hv, pairs_arg(out_pairs, 48, 20))
+    torch.cuda.synchronize()
+    ek, ev = hk0.copy(), hv0.copy()
+    ek[host_ids], ev[host_ids] = k[dev_ids], v[dev_ids]
+    assert np.array_equal(to_bits(hk), ek) and np.array_equal(to_bits(hv), ev)
+    # bring them back into other device blocks
+    back = rng.permutation(48)[:12]
+    pa.swap_blocks(hk, hv, kd, vd, pairs_arg(np.stack([host_ids, back], 1), 20, 48))
+    torch.cuda.synchronize()
+    k2, v2 = k.copy(), v.copy()
+    k2[back], v2[back] = k[dev_ids], v[dev_ids]
+    assert np.array_equal(to_bits(kd), k2) and np.array_equal(to_bits(vd), v2)
+
+
+def test_swap_blocks_refuses_pageable_host_memory():
+    """A pool in ordinary (pageable) host memory is refused before any launch."""
+    L = pa.lib()
+    import ctypes
+    host = np.zeros((4, 1, 16, 64), np.uint16)
+    dev = torch.zeros((4, 1, 16, 64), dtype=torch.float16, device="cuda")
+    pairs = dev_i32([[0, 1]])
+    p = ctypes.c_void_p
+    st = L.pa_swap_blocks(p(dev.data_ptr()), p(dev.data_ptr()), p(host.ctypes.data),
+                          p(host.ctypes.data), p(pairs.data_ptr()), 1, 4, 4, 1, 16, 64,
+                          pa.F16, None)
+    assert st == -1 and b"pinned" in L.pa_last_error()
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dev).item() == 0
+
+
+@pytest.mark.parametrize("kv,q", [("f16", "f16"), ("e4m3", "bf16")])
+def test_swap_out_reuse_swap_in_decode_unchanged(kv, q):
+    """Preempt a gang of two samples by swapping: their blocks go to a pinned host pool,
+    another request takes every free block (including the released ones) and overwrites
+    them, then the gang comes back into different blocks.  Block pairs equal the oracle's,
+    the restored caches equal the oracle's, and the decode output is bit-identical to the
+    output before the swap (and within tolerance of the oracle)."""
+    rng = np.random.default_rng(9)
+    B, Hkv, Hq, d, NB, MB, NH = 16, 4, 8, 128, 40, 8, 24
+    sp = workloads.Spec("w", 3, Hq, Hkv, d, B, 1, 1, NB, MB, q, kv, 1 / np.sqrt(d))
+    free = rng.permutation(NB)
+    o = LifecycleOracle.create(NB, B, free)
+    bm = pa.BlockManager(NB, B, free)
+    o.host_pool(NH)
+    bm.host_pool(NH)
+    src = sp.src_dtype
+    inv = scl = 1.0
+    if kv == "e4m3":
+        scl = float(np.float32(4.0 / 448.0))
+        inv = float(np.float32(1.0) / np.float32(scl))
+    [po] = o.alloc([40])
+    _, hb = bm.alloc_tables([40], MB)
+    so, sb = o.fork(po, 2), bm.fork(int(hb[0]), 2)
+    assert sb.tolist() == so
+    [co] = o.alloc([70])
+    _, hc = bm.alloc_tables([70], MB)
+    o.free_seqs([po])
+    bm.free(hb)
+    handles_o, handles_b = so + [co], sb.tolist() + hc.tolist()
+    k_or, v_or = workloads.empty_cache(sp), workloads.empty_cache(sp)
+    kd, vd = to_dev(k_or, kv), to_dev(v_or, kv)
+    lens = np.array([40, 40, 70], np.int32)
+    for step in range(10):                     # private tokens: copy-on-write, overflow
+        blk_o, _, cp_o = o.append(so)
+        blk_b, _, cp_b = bm.append(sb)
+        assert blk_b.tolist() == blk_o and [tuple(c) for c in cp_b.tolist()] == cp_o
+        copy_blocks(k_or, cp_o)
+        copy_blocks(v_or, cp_o)
+        if len(cp_b):
+            pa.copy_blocks(kd, vd, dev_i32(cp_b))
+    tables, lens = bm.table(handles_b, MB)
+    t_o, l_o = o.table(handles_o, MB)
+    assert np.array_equal(tables, t_o) and np.array_equal(lens, l_o)
+    # fill every valid slot of all three sequences (shared slots are written by each owner
+    # with the same row, so the contents are well defined)
+    rows = {}
+    for i in range(3):
+        for which in ("k", "v"):
+            rows[i, which] = workloads._round_bits(
+                rng.standard_normal((int(lens[i]), Hkv, d), dtype=np.float32), src)
+    rows[1, "k"][:40], rows[1, "v"][:40] = rows[0, "k"][:40], rows[0, "v"][:40]
+    for i in range(3):
+        seq = np.full(int(lens[i]), i, np.int32)
+        pos = np.arange(int(lens[i]), dtype=np.int32)
+        oracle.scatter(rows[i, "k"], DT[src], k_or, DT[kv], tables, seq, pos, B, inv)
+        oracle.scatter(rows[i, "v"], DT[src], v_or, DT[kv], tables, seq, pos, B, inv)
+        pa.write_kv(to_dev(rows[i, "k"], src), to_dev(rows[i, "v"], src), kd, vd,
+                    dev_i32(tables), dev_i32(seq), dev_i32(pos), inv, inv)
+    qd = to_dev(workloads._round_bits(rng.standard_normal((3, Hq, d), dtype=np.float32), q), q)
+    before = pa.decode(qd, kd, vd, dev_i32(tables), dev_i32(lens), int(lens.max()), sp.scale,
+                       scl, scl)
+    torch.cuda.synchronize()
+    before = before.clone()
+    # swap the gang out
+    hk = _pinned_like(np.zeros((NH,) + k_or.shape[1:], k_or.dtype), kv)
+    hv = _pinned_like(np.zeros((NH,) + v_or.shape[1:], v_or.dtype), kv)
+    hk_or = np.zeros((NH,) + k_or.shape[1:], k_or.dtype)
+    hv_or = np.zeros_like(hk_or)
+    p_o = o.swap_out(so)
+    p_b = bm.swap_out(sb)
+    assert [tuple(x) for x in p_b.tolist()] == p_o
+    for dv, hs in p_o:
+        hk_or[hs], hv_or[hs] = k_or[dv], v_or[dv]
+    pa.swap_blocks(kd, vd, hk, hv, dev_i32(p_b))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(hk), hk_or) and np.array_equal(to_bits(hv), hv_or)
+    # another request takes every free block and overwrites it
+    n_free = bm.stats()[1]
+    [xo] = o.alloc([B * n_free])
+    _, hx = bm.alloc_tables([B * n_free], NB)
+    taken = o.seqs[xo].blocks
+    assert sorted(taken) == sorted(bm.table(hx, NB)[0][0][:n_free].tolist())
+    k_or[taken] = 0x7E00 if kv != "e4m3" else 0x7F
+    v_or[taken] = 0x7E00 if kv != "e4m3" else 0x7F
+    kd[taken], vd[taken] = to_dev(k_or[taken], kv), to_dev(v_or[taken], kv)
+    o.free_seqs([xo])
+    bm.free(hx)
+    # swap back in
+    p_o = o.swap_in(so)
+    p_b = bm.swap_in(sb)
+    assert [tuple(x) for x in p_b.tolist()] == p_o
+    for hs, dv in p_o:
+        k_or[dv], v_or[dv] = hk_or[hs], hv_or[hs]
+    pa.swap_blocks(hk, hv, kd, vd, dev_i32(p_b))
+    tables2, lens2 = bm.table(handles_b, MB)
+    assert np.array_equal(tables2, o.table(handles_o, MB)[0]) and np.array_equal(lens2, lens)
+    assert not np.array_equal(tables2[:2], tables[:2])
+    after = pa.decode(qd, kd, vd, dev_i32(tables2), dev_i32(lens), int(lens.max()), sp.scale,
+                      scl, scl)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kd), k_or) and np.array_equal(to_bits(vd), v_or)
+    assert torch.equal(after.view(torch.int16), before.view(torch.int16))
+    ref = oracle.decode(to_bits(qd), DT[q], k_or, v_or, DT[kv], tables2, lens, Hkv, B, sp.scale,
+                        scl, scl)
+    atol, rrel = (2e-2, None) if kv == "e4m3" else (2e-3, 1e-2)
+    compare(after.double().cpu().numpy(), ref, atol, rrel, q)

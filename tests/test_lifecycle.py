@@ -123,6 +123,76 @@ def test_oracle_decode_after_copy_on_write_equals_private_copies():
     assert all(tables[i, shared_partial] != tables[0, shared_partial] for i in range(1, K)) or K == 1
 
 
+def test_oracle_swap_worked_example():
+    """Two samples share a prompt block (7) and own one block each; a third sequence also
+    holds block 7.  Swapping the samples out copies each distinct block once (7 once),
+    frees their private blocks, keeps block 7 on the device for the third sequence; swapping
+    them back takes fresh device blocks from the front of the free list."""
+    o = LifecycleOracle.create(8, 4, [7, 1, 2, 3, 4, 5, 6, 0])
+    o.host_pool(4)
+    [p] = o.alloc([4])                       # block 7
+    a, b = o.fork(p, 2)
+    [c] = o.alloc([1])                       # block 1
+    o.seqs[c].blocks = [7]                   # make c share the prompt block too
+    o.refs[1] -= 1
+    o.free.append(1)
+    o.refs[7] += 1
+    o.free_seqs([p])
+    assert o.append([a, b]) == ([2, 3], [0, 0], [])   # overflow: private blocks 2 and 3
+    pairs = o.swap_out([a, b])
+    assert pairs == [(7, 0), (2, 1), (3, 2)]
+    assert o.seqs[a].blocks == [0, 1] and o.seqs[b].blocks == [0, 2]
+    assert o.host_refs == [2, 1, 1, 0] and o.host_free == [3]
+    assert o.refs[7] == 1 and o.refs[2] == 0 and o.refs[3] == 0
+    assert o.free[-2:] == [2, 3]
+    pairs = o.swap_in([b, a])
+    front = [4, 5, 6]
+    assert pairs == [(0, front[0]), (2, front[1]), (1, front[2])]
+    assert o.seqs[b].blocks == [4, 5] and o.seqs[a].blocks == [4, 6]
+    assert o.host_refs == [0, 0, 0, 0] and o.host_free == [3, 2, 0, 1]   # b releases 2, a 0 and 1
+    assert o.refs[4] == 2
+
+
+def test_oracle_swap_round_trip_keeps_decode():
+    """Swap a gang out, let other sequences reuse (and overwrite) the freed device blocks,
+    swap it back into different blocks: the decode output is unchanged, bit for bit."""
+    rng = np.random.default_rng(4)
+    B, Hkv, d, NB, MB = 16, 2, 64, 24, 8
+    sp = workloads.Spec("sw", 1, 2 * Hkv, Hkv, d, B, 1, 1, NB, MB, "f16", "f16", 0.125)
+    o = LifecycleOracle.create(NB, B, rng.permutation(NB))
+    o.host_pool(16)
+    kc, vc = workloads.empty_cache(sp), workloads.empty_cache(sp)
+    lens = [40, 70, 17]
+    hs = o.alloc(lens)
+    t, _ = o.table(hs, MB)
+    for which, cache in (("k", kc), ("v", vc)):
+        for i, n in enumerate(lens):
+            rows = workloads._round_bits(rng.standard_normal((n, Hkv, d), dtype=np.float32), "f16")
+            oracle.scatter(rows, DT["f16"], cache, DT["f16"], t, np.full(n, i, np.int32),
+                           np.arange(n, dtype=np.int32), B)
+    q = workloads._round_bits(rng.standard_normal((3, 2 * Hkv, d), dtype=np.float32), "f16")
+    before = oracle.decode(q, DT["f16"], kc, vc, DT["f16"], t, np.array(lens, np.int32), Hkv, B,
+                           0.125)
+    hk = np.zeros((16,) + kc.shape[1:], kc.dtype)
+    hv = np.zeros_like(hk)
+    pairs = o.swap_out(hs[:2])
+    for dev, host in pairs:
+        hk[host], hv[host] = kc[dev], vc[dev]
+    [other] = o.alloc([B * len(o.free)])     # takes every free block, incl. the released ones
+    for bid in o.seqs[other].blocks:
+        kc[bid] = 0x7E00
+        vc[bid] = 0x7E00
+    o.free_seqs([other])
+    pairs = o.swap_in(hs[:2])
+    for host, dev in pairs:
+        kc[dev], vc[dev] = hk[host], hv[host]
+    t2, _ = o.table(hs, MB)
+    assert not np.array_equal(t2[:2], t[:2])
+    after = oracle.decode(q, DT["f16"], kc, vc, DT["f16"], t2, np.array(lens, np.int32), Hkv, B,
+                          0.125)
+    assert np.array_equal(before, after)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
 def test_block_manager_matches_lifecycle_oracle(seed):
     """Random interleavings of alloc / fork / append / free: tables, slots, copies, refcounts
@@ -132,11 +202,44 @@ def test_block_manager_matches_lifecycle_oracle(seed):
     free = rng.permutation(NB)
     o = LifecycleOracle.create(NB, B, free)
     bm = pa.BlockManager(NB, B, free)
-    live = []
+    o.host_pool(48)
+    bm.host_pool(48)
+    live = []      # resident sequences
+    swapped = []   # swapped-out gangs
     MB = NB
     for step in range(300):
-        op = rng.choice(["alloc", "fork", "append", "free"], p=[0.2, 0.15, 0.5, 0.15])
-        if op == "alloc" or not live:
+        op = rng.choice(["alloc", "fork", "append", "free", "swap_out", "swap_in"],
+                        p=[0.2, 0.1, 0.4, 0.1, 0.1, 0.1])
+        if op == "swap_out" and live:
+            gang = rng.choice(live, int(rng.integers(1, min(len(live), 3) + 1)),
+                              replace=False).tolist()
+            res = o.swap_out(gang)
+            if res is None:
+                with pytest.raises(pa.PagedAttnError) as e:
+                    bm.swap_out(gang)
+                assert e.value.status == -3
+            else:
+                assert [tuple(x) for x in bm.swap_out(gang).tolist()] == res
+                live = [h for h in live if h not in gang]
+                swapped.append(gang)
+        elif op == "swap_in" and swapped:
+            gang = swapped[int(rng.integers(len(swapped)))]
+            res = o.swap_in(gang)
+            if res is None:
+                with pytest.raises(pa.PagedAttnError) as e:
+                    bm.swap_in(gang)
+                assert e.value.status == -3
+            else:
+                assert [tuple(x) for x in bm.swap_in(gang).tolist()] == res
+                swapped.remove(gang)
+                live += gang
+        elif op == "free" and swapped and rng.random() < 0.3:
+            gang = swapped.pop(int(rng.integers(len(swapped))))
+            o.free_seqs(gang)
+            bm.free(gang)
+        elif op in ("swap_out", "swap_in"):
+            pass
+        elif op == "alloc" or not live:
             lens = rng.integers(0, 3 * B, rng.integers(1, 4)).astype(np.int32)
             ho = o.alloc(lens.tolist())
             if ho is None:
@@ -171,6 +274,8 @@ def test_block_manager_matches_lifecycle_oracle(seed):
             live = [h for h in live if h not in hs]
         ref, nfree, _ = bm.stats()
         assert ref.tolist() == o.refs and bm.free_list().tolist() == o.free
+        href, hfree = bm.host_stats()
+        assert href.tolist() == o.host_refs and hfree == len(o.host_free)
         if live:
             t1, l1 = bm.table(live, MB)
             t2, l2 = o.table(live, MB)
