@@ -41,6 +41,28 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+// e4m3 caches: 1 = contract the codes on the fp8 matrix cores (no widening); 0 = widen
+// them to the query's 16-bit type while staging (compile-time switch for measurements).
+#ifndef PA_FP8_NATIVE
+#define PA_FP8_NATIVE 1
+#endif
+
+// fp8 MFMA with per-operand power-of-two scales (E8M0 exponents, 127 = 2^0); operands are
+// e4m3 (format code 0).  16 x 16 output, 128-long contraction, 32 codes per lane.
+__device__ __forceinline__ f32x4 mfma_e4m3(v8i a, v8i b, f32x4 c, int a_exp, int b_exp) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, a_exp, 0, b_exp);
+}
+
+// Four floats -> four e4m3 codes (round to nearest even; |x| <= 448 here), and back.
+__device__ __forceinline__ uint32_t e4m3x4_pack(float x0, float x1, float x2, float x3) {
+  int d = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  d = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, d, true);
+  return (uint32_t)d;
+}
 
 template <int QK> struct MfmaOps;
 
@@ -103,9 +125,24 @@ __device__ __forceinline__ void e4m3x16_widen(const u32x4 src, u32x4 (&dst)[2]) 
   }
 }
 
+// e4m3 caches (PA_FP8_NATIVE): K and V stay 1-byte codes in LDS and both contractions run
+// on the fp8 matrix core (v_mfma_scale_f32_16x16x128_f8f6f4).  e4m3 keeps 4 significant
+// bits, so the 16-bit query enters as three e4m3 terms (q = hi + mid + lo, each the
+// rounding residual of the one before; about 12 bits together) after scaling each head by
+// a power of two 2^e that puts its largest element in [128, 256); the operand scale 2^-e
+// of the matrix core undoes it exactly.  The softmax weights enter as hi + lo under a
+// per-(head, block) power of two that lifts the block's largest weight into [128, 256)
+// (the operand scale undoes it), so small weights do not fall below e4m3's range; the
+// denominator sums the unrounded fp32 weights.  Lane layouts (measured on the device with
+// an in-bounds probe): lane (r, c) supplies row / column c and 32 codes of the contraction
+// for both operands alike; the scale of row / column c comes from a lane of column c,
+// which is why the scales here are per head.  V's operand is built with
+// ds_read_b64_tr_b8: 16 lanes each name 8 bytes of one of 8 rows, and lane c receives
+// byte c of each row.
+//
 // Supported: D in {64, 128}, B = 16 (one MFMA token tile per block), fp16 or bf16 Q with a
-// cache of the same type or e4m3 (widened to Q's type while it is staged into LDS),
-// 2 <= G <= 16.
+// cache of the same type or e4m3 (contracted as e4m3, or widened to Q's type while it is
+// staged into LDS), 2 <= G <= 16.
 // LANE: per-column visibility (each query column has its own token range and draft
 // mask), needed by the prefix units of the shared-prefix decode and by multi-token
 // queries; plain and suffix units share one token count and use the cheaper mask.
@@ -120,11 +157,14 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   constexpr int TPLS = 64 / LPTS;            // token rows per 1 KiB wave load
   constexpr int STILE = BS * D * E;          // cache bytes of one (block, KV head) tile
   constexpr int NLDS = STILE / 1024;         // wave loads per cache tile
-  constexpr int CPL = EPLS / 8;              // 16-byte LDS chunks one lane's load becomes
-  constexpr int CPR = D / 8;                 // 16-byte chunks per LDS row
-  constexpr int PITCH = D * 2;               // LDS row pitch (bytes, Q's 16-bit type)
+  constexpr bool NATIVE = PA_FP8_NATIVE && KVK == KIND_E4M3;  // e4m3 codes on the fp8 MFMA
+  constexpr int LE = NATIVE ? 1 : 2;         // LDS bytes per element
+  constexpr int CPL = NATIVE ? 1 : EPLS / 8; // 16-byte LDS chunks one lane's load becomes
+  constexpr int CPR = D * LE / 16;           // 16-byte chunks per LDS row
+  constexpr int PITCH = D * LE;              // LDS row pitch (bytes)
   constexpr int RPB = 256 / PITCH;           // rows per 256-byte bank period
-  constexpr int TILE = BS * D * 2;           // LDS bytes of one tile
+  constexpr int TILE = BS * D * LE;          // LDS bytes of one tile
+  constexpr int QD = D / 4;                  // native: query elements per lane
   static_assert(NLDS * 1024 == STILE, "tile must be covered by whole wave loads");
   static_assert(G >= 2 && G <= 16, "group size");
   using Ops = MfmaOps<QK>;
@@ -134,7 +174,11 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   // 16-byte chunk x of LDS row `row` holds chunk x ^ swz(row) of the V row: the two
   // chunks every ds_read_b64_tr_b16 takes from each of 16 rows then fall on distinct
   // banks (2 passes for 512 bytes), and each ds_write_b128 covers whole bank periods.
-  auto swz = [](int row) { return 2 * ((row / RPB) % (D / 16)); };
+  // Native e4m3 tiles: chunk x of row t at x ^ (t mod CPR), for K and V alike.
+  auto swz = [](int row) {
+    if constexpr (NATIVE) return row % CPR;
+    else return 2 * ((row / RPB) % (D / 16));
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -220,13 +264,62 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   }
 
   // Q^T operand: lane (r, c) holds head c's dims 32kk + 8r .. +8 (zero for padding heads)
-  u32x4 qop[KSTEPS];
+  u32x4 qop[NATIVE ? 1 : KSTEPS];
+  // native: head c's dims QD*r .. +QD as three e4m3 terms (zero for padding heads), and
+  // the E8M0 exponent 127 - e of the operand scale 2^-e that undoes the head's 2^e
+  v8i qn[NATIVE ? 3 : 1];
+  int q_exp = 127;
+  if constexpr (NATIVE) {
+    float qv[QD];
+    if (c < G) {
+      const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + row_of(c) * D + QD * r);
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    if (c < G)
-      qop[kk] = *(const u32x4*)((const uint16_t*)a.q + row_of(c) * D + 32 * kk + 8 * r);
-    else
-      qop[kk] = u32x4{0, 0, 0, 0};
+      for (int k = 0; k < QD / 8; ++k) {
+        const u32x4 t = qp[k];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          qv[8 * k + 2 * w] = (QK == KIND_BF16) ? bf16_lo(t[w]) : f16_lo(t[w]);
+          qv[8 * k + 2 * w + 1] = (QK == KIND_BF16) ? bf16_hi(t[w]) : f16_hi(t[w]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < QD; ++i) qv[i] = 0.f;
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < QD; ++i) mx = fmaxf(mx, fabsf(qv[i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // mx in [2^(x-1), 2^x) -> scale by 2^(8-x): the largest element lands in [128, 256)
+    int e = (mx > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(mx) : 0;
+    e = e > 127 ? 127 : e;
+    q_exp = 127 - e;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) qn[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < QD / 4; ++w) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __builtin_amdgcn_ldexpf(qv[4 * w + i], e);
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {  // each term takes the rounding residual of the last
+        const uint32_t code = e4m3x4_pack(x[0], x[1], x[2], x[3]);
+        qn[t][w] = (int)code;
+        float back[4];
+        e4m3x4_to_f32(code, back);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] -= back[i];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (c < G)
+        qop[kk] = *(const u32x4*)((const uint16_t*)a.q + row_of(c) * D + 32 * kk + 8 * r);
+      else
+        qop[kk] = u32x4{0, 0, 0, 0};
+    }
   }
 
   // Output accumulators (matrix-core C operands) hold P . V relative to the reference
@@ -276,7 +369,9 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 #pragma unroll
     for (int i = 0; i < NLDS; ++i) {
       u32x4 w[CPL];
-      if constexpr (KVK == KIND_E4M3) {
+      if constexpr (NATIVE) {
+        w[0] = t[i];
+      } else if constexpr (KVK == KIND_E4M3) {
         u32x4 two[2];
         e4m3x16_widen<QK>(t[i], two);
         w[0] = two[0];
@@ -293,11 +388,23 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
   // logits of block j: C[token 4r+i][head c]
   auto logits = [&]() {
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NATIVE) {
+      // K's operand: token c, the same dims QD*r .. +QD that lane (r, c) holds of Q
+      const uint8_t* row = kt + c * PITCH;
+      const u32x4 lo = *(const u32x4*)(row + ((((QD / 16) * r) ^ (c % CPR)) * 16));
+      u32x4 hi = u32x4{0, 0, 0, 0};
+      if constexpr (QD == 32) hi = *(const u32x4*)(row + (((2 * r + 1) ^ (c % CPR)) * 16));
+      const v8i kop = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int chunk = (4 * kk + r) ^ (c % CPR);
-      const u32x4 kop = *(const u32x4*)(kt + c * PITCH + chunk * 16);
-      sc = Ops::qk(kop, qop[kk], sc);
+      for (int t = 0; t < 3; ++t) sc = mfma_e4m3(kop, qn[t], sc, 127, q_exp);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int chunk = (4 * kk + r) ^ (c % CPR);
+        const u32x4 kop = *(const u32x4*)(kt + c * PITCH + chunk * 16);
+        sc = Ops::qk(kop, qop[kk], sc);
+      }
     }
     return sc;
   };
@@ -330,6 +437,39 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
       }
     }
     const float ms = (m_ref == -INFINITY) ? 0.f : m_ref;
+    if constexpr (NATIVE) {
+      // weights 2^(z - ms) <= 2^8, lifted by 2^kb so the block's largest is in [2^7, 2^8)
+      const float rel = bm - ms;
+      int kb = 0;
+      if (rel > -INFINITY) {
+        kb = 7 - (int)floorf(rel);
+        kb = kb > 126 ? 126 : kb;
+      }
+      float p[4], pp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(z[i] - ms);
+        pp[i] = fast_exp2(z[i] - ms + (float)kb);
+      }
+      const uint32_t hi = e4m3x4_pack(pp[0], pp[1], pp[2], pp[3]);
+      float back[4];
+      e4m3x4_to_f32(hi, back);
+      const uint32_t lo = e4m3x4_pack(pp[0] - back[0], pp[1] - back[1], pp[2] - back[2],
+                                      pp[3] - back[3]);
+      // P's operand: head c, tokens 4r .. 4r+3 as hi then lo; V's operand repeats those
+      // four tokens so both halves meet the same values
+      const v8i pop8 = v8i{(int)hi, (int)lo, 0, 0, 0, 0, 0, 0};
+      l_part += (p[0] + p[1]) + (p[2] + p[3]);
+      const int rho = 4 * r + ((c >> 1) & 3);
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) {
+        const v2i vv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_v2i*)(vt + rho * PITCH + ((t ^ swz(rho)) * 16) + 8 * (c & 1)));
+        const v8i vop = v8i{vv[0], vv[1], 0, 0, 0, 0, 0, 0};
+        cacc[t] = mfma_e4m3(pop8, vop, cacc[t], 127 - kb, 127);
+      }
+      return;
+    }
     float p[4], rp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - ms);

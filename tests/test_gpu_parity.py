@@ -205,6 +205,39 @@ def test_few_dominant_tokens_with_distant_values(qd):
         compare(_f64(_gpu_decode(case, tables, k, v, partition_size=0)), ref, 2e-3, 1e-2, qd)
 
 
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+def test_e4m3_sink_token_with_many_small_weights(qd):
+    """Position 0 of every sequence scores about 9 (natural log units) above the rest for
+    one query head per KV head, so each other token weighs ~2^-13 of it, yet together they
+    carry about a third of the mass.  On the fp8 matrix-core path those small weights
+    must keep their precision (they are lifted per block before rounding to e4m3), not
+    fall below e4m3's range; the vector kernel (G = 1) runs the same case."""
+    lens = [1500, 700, 33]
+    for G in (1, 4):
+        sp = workloads.Spec("sink", len(lens), 4 * G, 4, 128, 16, 1, 1,
+                            sum(math.ceil(n / 16) for n in lens) + 5, 96, qd, "e4m3",
+                            1 / math.sqrt(128))
+        case = workloads.generate(sp, 500 + G, context_lens=lens)
+        src = sp.src_dtype
+        q = workloads.bits_to_f32(case.q, qd).astype(np.float64)
+        k32 = workloads.bits_to_f32(case.k_src, src)
+        for row in np.nonzero(case.positions == 0)[0]:
+            s = case.seq_ids[row]
+            for g in range(4):
+                qh = q[s, g * G]
+                k32[row, g] = (9.0 * math.sqrt(128) * qh / (qh @ qh)).astype(np.float32)
+        case.k_src = workloads._round_bits(k32, src)
+        amax = np.float32(np.abs(workloads.bits_to_f32(case.k_src, src)).max())
+        case.k_scale = float(np.float32(amax / np.float32(448.0)))
+        case.k_inv_scale = float(np.float32(1.0) / np.float32(case.k_scale))
+        tables, _, _ = oracle_tables(case)
+        k, v = oracle_caches(case, tables)
+        ref = oracle_decode(case, tables, k, v)
+        for P in (0, 1024):
+            out = _f64(_gpu_decode(case, tables, k, v, partition_size=P))
+            compare(out, ref, 2e-2, None, qd)
+
+
 def test_single_token_returns_v1_bit_exact():
     for qd, kvd in (("f16", "f16"), ("bf16", "bf16"), ("bf16", "e4m3"), ("f16", "e4m3")):
         sp = workloads.Spec("n1", 6, 8, 2, 128, 16, 1, 1, 12, 2, qd, kvd, 0.0883883)
