@@ -35,11 +35,15 @@ def measured_traffic(workload: str, decode_path: str):
     path, or the kernel sources changed since the counters were taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"decode_counters_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path))
-    if rec.get("decode_path", "plain") != decode_path:
+    rec = None
+    for name in (f"decode_counters_{workload}.json", f"decode_counters_{workload}_{decode_path}.json"):
+        path = os.path.join(ROOT, "profiles", name)
+        if os.path.exists(path):
+            r = json.load(open(path))
+            if r.get("decode_path", "plain") == decode_path:
+                rec = r
+                break
+    if rec is None:
         return None
     h = hashlib.sha256()
     for f in rec["kernel_sources"]:

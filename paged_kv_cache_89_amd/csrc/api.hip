@@ -592,8 +592,8 @@ bool decode_supported(const DecodeShape& s) {
 }
 
 
-// Grouped-query shapes with 16-token blocks and fp16/bf16 caches run the matrix-core
-// kernel; every other shape runs the vector kernel (which also covers e4m3 caches).
+// Grouped-query shapes with 16-token blocks run the matrix-core kernel (fp16/bf16 caches on
+// the 16-bit MFMA, e4m3 caches on the fp8 MFMA); every other shape runs the vector kernel.
 hipError_t launch_decode(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream) {
   if (gqa_mfma_supported(s))
     return launch_decode_gqa_mfma(s, a, stream);

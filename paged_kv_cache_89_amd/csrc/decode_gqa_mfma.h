@@ -45,6 +45,11 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
+// Minimum waves per SIMD the register allocation must allow (compile-time tuning knob).
+#ifndef PA_GQA_MIN_WAVES
+#define PA_GQA_MIN_WAVES 1
+#endif
+
 // e4m3 caches: 1 = contract the codes on the fp8 matrix cores (no widening); 0 = widen
 // them to the query's 16-bit type while staging (compile-time switch for measurements).
 #ifndef PA_FP8_NATIVE
@@ -147,7 +152,7 @@ __device__ __forceinline__ void e4m3x16_widen(const u32x4 src, u32x4 (&dst)[2]) 
 // mask), needed by the prefix units of the shared-prefix decode and by multi-token
 // queries; plain and suffix units share one token count and use the cheaper mask.
 template <int D, int QK, int KVK, int G, bool NT, bool LANE>
-__global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256, PA_GQA_MIN_WAVES) void paged_decode_gqa_mfma_kernel(const DecodeArgs a) {
   constexpr int BS = 16;
   constexpr int KSTEPS = D / 32;             // 16x16x32 steps over the head dimension
   constexpr int NTILES = D / 16;             // 16-wide output slices
@@ -182,28 +187,12 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int wg = blockIdx.x;
-  if (a.xcd_remap) {
-    const int G8 = gridDim.x, x = wg % 8, loc = wg / 8, per = G8 / 8, rem = G8 % 8;
-    wg = (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
-  }
-  const int unit = wg * 4 + wave;
-  if (unit >= a.num_units) return;
   const bool prefix = LANE && a.mode == MODE_PREFIX;
   const bool multi = LANE && a.mode == MODE_MULTI;
   const int rows = prefix ? a.num_groups : a.num_seqs;
-  int s, kvh, part;  // s: the sequence, or in prefix mode the group
-  if (a.seq_fastest == 0) {
-    kvh = unit % a.num_kv_heads;
-    const int rest = unit / a.num_kv_heads;
-    part = rest % a.num_parts;
-    s = rest / a.num_parts;
-  } else {
-    s = unit % rows;
-    const int rest = unit / rows;
-    kvh = rest % a.num_kv_heads;
-    part = rest / a.num_kv_heads;
-  }
+  const UnitCoords uc = unit_coords(a, 4, wave, rows);
+  if (!uc.ok) return;
+  const int s = uc.s, kvh = uc.kvh, part = uc.part;  // s: the sequence, or in prefix mode the group
   const int r = lane >> 4;
   const int c = lane & 15;
   // Query column cc < G of the unit reads and writes row row_of(cc) of the [rows, D]
@@ -569,7 +558,7 @@ __global__ __launch_bounds__(256) void paged_decode_gqa_mfma_kernel(const Decode
 
 template <int D, int QK, int KVK, int G, bool NT>
 hipError_t launch_gqa_mfma_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid((a.num_units + 3) / 4);
+  const dim3 grid = decode_grid(a, 4);
   if (a.mode == MODE_PREFIX || a.mode == MODE_MULTI)
     hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true>), grid, dim3(256), 0,
                        stream, a);

@@ -78,27 +78,9 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int wg = blockIdx.x;
-  if (a.xcd_remap) {
-    // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that XCD x runs a
-    // contiguous range of logical workgroups (a bijection for any grid size).
-    const int G8 = gridDim.x, x = wg % 8, loc = wg / 8, per = G8 / 8, rem = G8 % 8;
-    wg = (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
-  }
-  const int unit = wg * PA_DECODE_WAVES + wave;
-  if (unit >= a.num_units) return;
-  int s, kvh, part;
-  if (a.seq_fastest == 0) {  // (seq, part, kv head): neighbouring heads of the same blocks
-    kvh = unit % a.num_kv_heads;
-    const int rest = unit / a.num_kv_heads;
-    part = rest % a.num_parts;
-    s = rest / a.num_parts;
-  } else {                   // (part, kv head, seq): sequences that share blocks run together
-    s = unit % a.num_seqs;
-    const int rest = unit / a.num_seqs;
-    kvh = rest % a.num_kv_heads;
-    part = rest / a.num_kv_heads;
-  }
+  const UnitCoords uc = unit_coords(a, PA_DECODE_WAVES, wave, a.num_seqs);
+  if (!uc.ok) return;
+  const int s = uc.s, kvh = uc.kvh, part = uc.part;
   const int h0 = kvh * G;
 
   int n = a.ctx[s];
@@ -369,8 +351,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
 
 template <int D, int BS, int QK, int KVK, int G, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid((a.num_units + PA_DECODE_WAVES - 1) / PA_DECODE_WAVES);
-  hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT>), grid, dim3(64 * PA_DECODE_WAVES),
+  hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT>), decode_grid(a, PA_DECODE_WAVES), dim3(64 * PA_DECODE_WAVES),
                      0, stream, a);
   return hipGetLastError();
 }
@@ -392,12 +373,24 @@ hipError_t launch_decode_d(const DecodeShape& s, const DecodeArgs& a, hipStream_
   if (s.q_kind == KIND_F16 && s.kv_kind == KIND_E4M3) { PA_G(BS, KIND_F16, KIND_E4M3) } \
   if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_E4M3) { PA_G(BS, KIND_BF16, KIND_E4M3) } \
   return hipErrorInvalidValue;
+  // 16-token blocks with G >= 2 always run on the matrix-core kernel: only G = 1 here.
+#define PA_G1(BS, QK, KVK) \
+  if (s.group == 1) return launch_decode_t<D, BS, QK, KVK, 1, NT>(a, stream); \
+  return hipErrorInvalidValue;
+#define PA_DT16                                                                            \
+  if (s.q_kind == KIND_F16 && s.kv_kind == KIND_F16) { PA_G1(16, KIND_F16, KIND_F16) }     \
+  if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_BF16) { PA_G1(16, KIND_BF16, KIND_BF16) } \
+  if (s.q_kind == KIND_F16 && s.kv_kind == KIND_E4M3) { PA_G1(16, KIND_F16, KIND_E4M3) }   \
+  if (s.q_kind == KIND_BF16 && s.kv_kind == KIND_E4M3) { PA_G1(16, KIND_BF16, KIND_E4M3) } \
+  return hipErrorInvalidValue;
   switch (s.block_size) {
     case 8: { PA_DT(8) }
-    case 16: { PA_DT(16) }
+    case 16: { PA_DT16 }
     case 32: { PA_DT(32) }
     default: return hipErrorInvalidValue;
   }
+#undef PA_DT16
+#undef PA_G1
 #undef PA_DT
 #undef PA_G
 }

@@ -117,6 +117,42 @@ struct TableSlice {
   }
 };
 
+// Work-unit coordinates (row s, KV head, partition) of wavefront `wave` of this
+// workgroup (`waves` per workgroup); false when the wavefront has no unit.
+//   xcd_remap 1: the hardware deals workgroups to the 8 XCDs round-robin; they are
+//     renumbered so that XCD x runs a contiguous range of logical workgroups (a bijection
+//     for any grid size).  0: launch order.
+//   seq_fastest 0: units in (row, partition, KV head) order, neighbouring heads of the
+//     same blocks side by side; 1: (partition, KV head, row), the rows that share blocks
+//     side by side.
+struct UnitCoords {
+  int s, kvh, part;
+  bool ok;
+};
+__device__ __forceinline__ UnitCoords unit_coords(const DecodeArgs& a, int waves, int wave,
+                                                  int rows) {
+  int wg = blockIdx.x;
+  if (a.xcd_remap == 1) {
+    const int G8 = gridDim.x, x = wg % 8, loc = wg / 8, per = G8 / 8, rem = G8 % 8;
+    wg = (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
+  }
+  const int unit = wg * waves + wave;
+  UnitCoords u;
+  u.ok = unit < a.num_units;
+  if (a.seq_fastest == 0) {
+    u.kvh = unit % a.num_kv_heads;
+    const int rest = unit / a.num_kv_heads;
+    u.part = rest % a.num_parts;
+    u.s = rest / a.num_parts;
+  } else {
+    u.s = unit % rows;
+    const int rest = unit / rows;
+    u.kvh = rest % a.num_kv_heads;
+    u.part = rest / a.num_kv_heads;
+  }
+  return u;
+}
+
 // Tokens of its group's shared prefix that a sequence of length n attends (cascade modes):
 // the group's shared blocks, clamped to [0, max_prefix_blocks], in tokens, capped at n.
 __device__ __forceinline__ int prefix_tokens(const DecodeArgs& a, int group, int block_size, int n) {

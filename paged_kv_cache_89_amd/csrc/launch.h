@@ -61,6 +61,11 @@ struct DecodeShape {
   bool nontemporal;          // K/V loads with the non-temporal hint
 };
 
+// Grid of a decode launch with `waves` units per workgroup.
+inline dim3 decode_grid(const DecodeArgs& a, int waves) {
+  return dim3((a.num_units + waves - 1) / waves);
+}
+
 bool decode_supported(const DecodeShape& s);
 hipError_t launch_decode(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
 // The matrix-core kernel alone (the only one that runs shared-prefix units).

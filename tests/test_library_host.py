@@ -215,3 +215,62 @@ def test_multi_token_workspace_and_errors_without_gpu():
     assert call(T=8, Hq=8, Hkv=4) == -1         # 16 columns: supported, NULL pointers
     assert call(T=0) == -1
     assert call(S=0) == 0
+
+
+def _kernel_resources():
+    """{mangled kernel name: (scratch bytes per lane, VGPRs)} from the gfx950 code objects
+    embedded in the built library (every offload bundle of its .hip_fatbin section)."""
+    import shutil
+    import struct
+    import tempfile
+    readelf = "/opt/rocm/llvm/bin/llvm-readelf"
+    if not (shutil.which("objcopy") and os.path.exists(readelf) and os.path.exists(pa.library_path)):
+        pytest.skip("objcopy / llvm-readelf or the built library not available")
+    kernels = {}
+    with tempfile.TemporaryDirectory() as d:
+        fb = os.path.join(d, "fatbin")
+        subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fb}", pa.library_path],
+                       check=True, capture_output=True)
+        data = open(fb, "rb").read()
+        magic = b"__CLANG_OFFLOAD_BUNDLE__"
+        pos, n = data.find(magic), 0
+        while pos >= 0:
+            (count,) = struct.unpack_from("<Q", data, pos + 24)
+            off = pos + 32
+            for _ in range(count):
+                o, size, tlen = struct.unpack_from("<QQQ", data, off)
+                triple = data[off + 24: off + 24 + tlen].decode()
+                off += 24 + tlen
+                if "gfx950" not in triple:
+                    continue
+                co = os.path.join(d, f"co{n}.elf")
+                n += 1
+                open(co, "wb").write(data[pos + o: pos + o + size])
+                notes = subprocess.run([readelf, "--notes", co], capture_output=True,
+                                       text=True, check=True).stdout
+                for m in re.finditer(r"\.name:\s+(\S+)\n(?:(?!\.name:).)*?"
+                                     r"\.private_segment_fixed_size:\s+(\d+)(?:(?!\.name:).)*?"
+                                     r"\.vgpr_count:\s+(\d+)", notes, re.S):
+                    kernels[m.group(1)] = (int(m.group(2)), int(m.group(3)))
+            pos = data.find(magic, pos + 1)
+    return kernels
+
+
+def test_hot_kernels_use_no_scratch():
+    """Register spills to scratch add HBM traffic to a bandwidth-bound kernel: every
+    instantiation except the vector kernel's G = 4 / 8 fallbacks (grouped queries with 8- or
+    32-token blocks) must keep everything in registers and LDS."""
+    k = _kernel_resources()
+    assert any("paged_decode_gqa_mfma_kernel" in n for n in k) and len(k) > 100
+    spilled = {}
+    for name, (scratch, _) in k.items():
+        m = re.match(r"_ZN2pa19paged_decode_kernelILi\d+ELi\d+ELi\dELi\dELi(\d)", name)
+        fallback = m is not None and int(m.group(1)) >= 4
+        if scratch and not fallback:
+            spilled[name] = scratch
+    assert not spilled, spilled
+    # the kernels the five workloads run, with their occupancy-setting register counts
+    hot = {"_ZN2pa19paged_decode_kernelILi128ELi16ELi0ELi0ELi1ELb1EEEvNS_10DecodeArgsE": 128,
+           "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0EEEvNS_10DecodeArgsE": 168}
+    for name, vgpr_max in hot.items():
+        assert k[name][0] == 0 and k[name][1] <= vgpr_max, (name, k[name])
