@@ -220,18 +220,30 @@ def test_multi_token_workspace_and_errors_without_gpu():
 def _kernel_resources():
     """{mangled kernel name: (scratch bytes per lane, VGPRs)} from the gfx950 code objects
     embedded in the built library (every offload bundle of its .hip_fatbin section)."""
-    import shutil
     import struct
     import tempfile
     readelf = "/opt/rocm/llvm/bin/llvm-readelf"
-    if not (shutil.which("objcopy") and os.path.exists(readelf) and os.path.exists(pa.library_path)):
-        pytest.skip("objcopy / llvm-readelf or the built library not available")
+    if not (os.path.exists(readelf) and os.path.exists(pa.library_path)):
+        pytest.skip("llvm-readelf or the built library not available")
+    # the .hip_fatbin section, located through the ELF64 section headers (read only: the
+    # library file is never rewritten while it is loaded)
+    elf = open(pa.library_path, "rb").read()
+    shoff, = struct.unpack_from("<Q", elf, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
+
+    def section(i):
+        name, _, _, _, off, size = struct.unpack_from("<IIQQQQ", elf, shoff + i * shentsize)
+        return name, off, size
+
+    _, stroff, _ = section(shstrndx)
+    data = None
+    for i in range(shnum):
+        name, off, size = section(i)
+        if elf[stroff + name: elf.index(b"\0", stroff + name)] == b".hip_fatbin":
+            data = elf[off: off + size]
+    assert data is not None, "no .hip_fatbin section"
     kernels = {}
     with tempfile.TemporaryDirectory() as d:
-        fb = os.path.join(d, "fatbin")
-        subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fb}", pa.library_path],
-                       check=True, capture_output=True)
-        data = open(fb, "rb").read()
         magic = b"__CLANG_OFFLOAD_BUNDLE__"
         pos, n = data.find(magic), 0
         while pos >= 0:
