@@ -446,7 +446,10 @@ __global__ __launch_bounds__(256, PA_GQA_MIN_WAVES) void paged_decode_gqa_mfma_k
       const uint32_t lo = e4m3x4_pack(pp[0] - back[0], pp[1] - back[1], pp[2] - back[2],
                                       pp[3] - back[3]);
       // P's operand: head c, tokens 4r .. 4r+3 as hi then lo; V's operand repeats those
-      // four tokens so both halves meet the same values
+      // four tokens so both halves meet the same values; the A-operand scale 2^-kb undoes
+      // the lift.  The operands carry 8 codes of the 32 the instruction takes (the rest
+      // zero); one tile at a time keeps a single zero-padded V operand live (153 instead of
+      // 184 VGPRs at D = 128: three waves per SIMD instead of two, +4 % measured).
       const v8i pop8 = v8i{(int)hi, (int)lo, 0, 0, 0, 0, 0, 0};
       l_part += (p[0] + p[1]) + (p[2] + p[3]);
       const int rho = 4 * r + ((c >> 1) & 3);
@@ -456,6 +459,8 @@ __global__ __launch_bounds__(256, PA_GQA_MIN_WAVES) void paged_decode_gqa_mfma_k
             (lds_v2i*)(vt + rho * PITCH + ((t ^ swz(rho)) * 16) + 8 * (c & 1)));
         const v8i vop = v8i{vv[0], vv[1], 0, 0, 0, 0, 0, 0};
         cacc[t] = mfma_e4m3(pop8, vop, cacc[t], 127 - kb, 127);
+        // (per-column-mask units stay at two waves per SIMD either way; leave them free)
+        if constexpr (!LANE) __builtin_amdgcn_sched_barrier(0);
       }
       return;
     }

@@ -133,12 +133,13 @@ def test_decode_plan_and_workspace():
     P, n = pa.decode_plan(8, 32, 32, 128, 32, 32768, 512)
     assert (P, n) == (512, 64)
     assert pa.decode_workspace_size(8, 32, 32, 128, 32, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    # library choice: contexts <= 256 unsplit; else 512-token partitions, halved (down to
-    # 128) while the grid has < 4096 units
-    assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0) == (512, 4)
-    assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (512, 64)
+    # library choice: contexts <= 256 unsplit; else 768-token partitions, halved (staying
+    # at least 128) while the grid has < 4096 units
+    assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0) == (768, 3)
+    assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (768, 43)
     assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (0, 1)
-    assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0) == (128, 16)
+    assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0) == (192, 11)
+    assert pa.decode_plan(16, 8, 8, 64, 16, 8192, 0) == (192, 43)
     assert pa.decode_plan(1, 8, 8, 64, 16, 48, 0) == (0, 1)
     assert pa.decode_plan(4, 8, 8, 64, 16, 256, 4096) == (0, 1)  # explicit P >= context
     # a unit walks at most 64 blocks: longer partitions / unsplit contexts are cut
@@ -174,8 +175,9 @@ def test_decode_argument_errors_without_gpu():
 
 def test_shared_prefix_workspace_and_errors_without_gpu():
     # fp8 shared-prompt shape: 256 seqs, 32 heads, d 128, B 16, max context 1536, prompts
-    # of 64 blocks.  P = 512 (pa_decode's choice); 2 prefix slots + 3 per-sequence slots.
-    assert pa.decode_plan(256, 32, 32, 128, 16, 1536, 0) == (512, 3)
+    # of 64 blocks.  The shared-prefix decode splits by 512 tokens (its prompts are block
+    # aligned; pa_decode alone would take 768): 2 prefix slots + 3 per-sequence slots.
+    assert pa.decode_plan(256, 32, 32, 128, 16, 1536, 0) == (768, 2)
     ws = pa.decode_shared_prefix_workspace_size(256, 32, 32, 128, 16, 1536, 64)
     assert ws == 256 * 32 * (2 + 3) * 130 * 4
     # unsplit choice: the whole context (rounded to B) is one slot on each side
