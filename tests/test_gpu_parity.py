@@ -353,3 +353,76 @@ def test_full_size_sampled_rows(name):
                         sp.num_kv_heads, sp.block_size, sp.scale, ks, vs, rows=rows)
     atol, rrel = tolerance(sp)
     compare(got[rows[:, 0], rows[:, 1]], ref[rows[:, 0], rows[:, 1]], atol, rrel, sp.q_dtype)
+
+
+@pytest.mark.parametrize("kv,q,G", [("f16", "f16", 1), ("bf16", "bf16", 4), ("e4m3", "bf16", 1),
+                                    ("e4m3", "bf16", 4)])
+def test_pools_beyond_4_gib(kv, q, G):
+    """Every block the batch uses lies above byte 2^32 of pools larger than 4 GiB: the KV
+    write, the batched block copy and the decode (vector kernel for G = 1, matrix cores for
+    G = 4) must form 64-bit addresses.  The oracle sees the same blocks renumbered from 0."""
+    Hkv, d, B = 8, 128, 16
+    e = 1 if kv == "e4m3" else 2
+    block_bytes = Hkv * B * d * e
+    used = 64
+    nb_big = (1 << 32) // block_bytes + used          # pool of more than 4 GiB
+    base = nb_big - used                              # first block above byte 2^32
+    assert base * block_bytes >= 1 << 32
+    lens = np.array([37, 300, 16, 1], np.int32)
+    S, MB = lens.size, 24
+    small = np.full((S, MB), -1, np.int32)
+    nxt = 0
+    for s_, n in enumerate(lens):
+        nb = -(-int(n) // B)
+        small[s_, :nb] = np.arange(nxt, nxt + nb)
+        nxt += nb
+    spare = used - 1                                  # destination of the block copy
+    assert nxt < spare
+    big = np.where(small >= 0, small + base, -1).astype(np.int32)
+    sp = workloads.Spec("big", S, Hkv * G, Hkv, d, B, 1, 1, used, MB, q, kv, 1 / math.sqrt(d))
+    rng = np.random.default_rng(21 + G)
+    src = sp.src_dtype
+    seq_ids = np.concatenate([np.full(n, i, np.int32) for i, n in enumerate(lens)])
+    pos = np.concatenate([np.arange(n, dtype=np.int32) for n in lens])
+    rows = {w: workloads._round_bits(rng.standard_normal((seq_ids.size, Hkv, d),
+                                                         dtype=np.float32), src) for w in "kv"}
+    scale, inv = 1.0, 1.0
+    if kv == "e4m3":
+        scale = float(np.float32(4.0 / 448.0))
+        inv = float(np.float32(1.0) / np.float32(scale))
+    k_or, v_or = workloads.empty_cache(sp), workloads.empty_cache(sp)
+    oracle.scatter(rows["k"], DT[src], k_or, DT[kv], small, seq_ids, pos, B, inv)
+    oracle.scatter(rows["v"], DT[src], v_or, DT[kv], small, seq_ids, pos, B, inv)
+    valid = np.zeros((used, B), bool)                 # slots holding a token (small ids)
+    for s_, n in enumerate(lens):
+        for t in range(int(n)):
+            valid[small[s_, t // B], t % B] = True
+    valid[spare] = valid[small[1, 0]]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "e4m3": torch.uint8}[kv]
+    kd = torch.empty((nb_big, Hkv, B, d), dtype=tdt, device="cuda")
+    vd = torch.empty_like(kd)
+    try:
+        pa.write_kv(to_dev(rows["k"], src), to_dev(rows["v"], src), kd, vd, dev_i32(big),
+                    dev_i32(seq_ids), dev_i32(pos), inv, inv)
+        # copy the first block of sequence 1 to the spare block and point the table at it
+        pa.copy_blocks(kd, vd, dev_i32([[big[1, 0], base + spare]]))
+        k_or[spare], v_or[spare] = k_or[small[1, 0]], v_or[small[1, 0]]
+        small[1, 0], big[1, 0] = spare, base + spare
+        torch.cuda.synchronize()
+        ids = torch.arange(base, nb_big, device="cuda")
+        for dev_pool, ref_pool in ((kd, k_or), (vd, v_or)):
+            got = to_bits(dev_pool.index_select(0, ids)).transpose(0, 2, 1, 3)  # [blk, B, H, d]
+            want = ref_pool.transpose(0, 2, 1, 3)
+            assert np.array_equal(got[valid], want[valid])   # every written (and copied) slot
+        qd = to_dev(workloads._round_bits(rng.standard_normal((S, Hkv * G, d), dtype=np.float32),
+                                          q), q)
+        out = pa.decode(qd, kd, vd, dev_i32(big), dev_i32(lens), int(lens.max()), sp.scale,
+                        scale, scale, partition_size=64)
+        torch.cuda.synchronize()
+        ref = oracle.decode(to_bits(qd), DT[q], k_or, v_or, DT[kv], small, lens, Hkv, B,
+                            sp.scale, scale, scale)
+        atol, rrel = (2e-2, None) if kv == "e4m3" else (2e-3, 1e-2)
+        compare(_f64(out), ref, atol, rrel, q)
+    finally:
+        del kd, vd
+        torch.cuda.empty_cache()
