@@ -5,6 +5,8 @@ token of every sequence into its slot, then pa_decode (plus its partition merge 
 the plan splits) attends over every sequence's context.  Block tables come from the
 library's block manager before timing (allocation is host work, off the timed path).
 Inputs are synthetic, seeded, and resident in HBM before the timed region starts.
+Consecutive steps use two layers' K/V pools in turn (same tables), so a step never reads
+K/V that the previous step left in the Infinity Cache.
 
 Prints one JSON line: value = algorithmic KV bytes read per step / step time (GB/s),
 plus decode tokens/s, a roofline entry for the decode kernel (HIP events on the launch
@@ -100,7 +102,13 @@ def main():
     pg, pl = workloads.prefix_groups(sp)
     bm = pa.BlockManager(sp.num_blocks, sp.block_size, free)
     tables, _ = bm.alloc_tables(ctx, sp.max_blocks, pg, pl)
+    # Two layers' K/V pools that share the block tables (as every layer of a model does):
+    # the timed steps alternate between them, so no step finds the K/V it reads left in the
+    # 256 MB Infinity Cache by the step before (in a real model the other layers run in
+    # between).  Each layer has its own e4m3 scales.
     q, kc, vc, k_scale, v_scale = workloads.device_pool(sp, seed)
+    _, kc2, vc2, k_scale2, v_scale2 = workloads.device_pool(sp, seed + 1000)
+    layers = [(kc, vc, k_scale, v_scale), (kc2, vc2, k_scale2, v_scale2)]
     S, Hq, Hkv, D, B = sp.num_seqs, sp.num_heads, sp.num_kv_heads, sp.head_dim, sp.block_size
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 1)
@@ -116,12 +124,13 @@ def main():
     used_P, nparts = pa.decode_plan(S, Hq, Hkv, D, B, max_ctx, P)
     ws_bytes = pa.decode_workspace_size(S, Hq, Hkv, D, B, max_ctx, P)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    k_inv = 1.0 / k_scale if sp.kv_dtype == "e4m3" else 1.0
-    v_inv = 1.0 / v_scale if sp.kv_dtype == "e4m3" else 1.0
     stream = torch.cuda.current_stream()
 
-    def write():
-        pa.write_kv(k_new, v_new, kc, vc, tables_d, seq_ids, positions, k_inv, v_inv,
+    def write(layer):
+        lk, lv, ks, vs = layers[layer]
+        k_inv = 1.0 / ks if sp.kv_dtype == "e4m3" else 1.0
+        v_inv = 1.0 / vs if sp.kv_dtype == "e4m3" else 1.0
+        pa.write_kv(k_new, v_new, lk, lv, tables_d, seq_ids, positions, k_inv, v_inv,
                     stream=stream)
 
     path = args.decode_path
@@ -150,18 +159,20 @@ def main():
         kernels = ("paged_decode_gqa_mfma_kernel (group prefixes) + paged_decode_kernel "
                    "(own tokens) + merge_partitions_kernel")
 
-        def decode():
-            pa.decode_shared_prefix(q, kc, vc, tables_d, ctx_d, pb_d, sp.group_size, max_ctx,
-                                    max_pb, sp.scale, k_scale, v_scale, partition_size=P,
+        def decode(layer):
+            lk, lv, ks, vs = layers[layer]
+            pa.decode_shared_prefix(q, lk, lv, tables_d, ctx_d, pb_d, sp.group_size, max_ctx,
+                                    max_pb, sp.scale, ks, vs, partition_size=P,
                                     flags=flags, out=out, workspace=ws, stream=stream)
     else:
-        def decode():
-            pa.decode(q, kc, vc, tables_d, ctx_d, max_ctx, sp.scale, k_scale, v_scale,
+        def decode(layer):
+            lk, lv, ks, vs = layers[layer]
+            pa.decode(q, lk, lv, tables_d, ctx_d, max_ctx, sp.scale, ks, vs,
                       partition_size=P, flags=flags, out=out, workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        write()
-        decode()
+    for i in range(args.warmup):
+        write(i % 2)
+        decode(i % 2)
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps, device synchronised on both sides
@@ -170,9 +181,9 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        write()
+        write(i % 2)
         ev[i][0].record(stream)
-        decode()
+        decode(i % 2)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -190,6 +201,32 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    # Latency distribution of the decode call: as timed above (layers alternating), and
+    # with one layer only, with and without a 512 MiB write before each call (evicts L2
+    # and the Infinity Cache); the write is outside the events.
+    def distribution(flush, reps, alternate):
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if flush else None
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(reps)]
+        for i in range(reps):
+            if flush:
+                scratch.fill_(i & 0xFF)
+            layer = i % 2 if alternate else 0
+            write(layer)
+            e[i][0].record(stream)
+            decode(layer)
+            e[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in e])
+        return {"median_ms": round(float(np.median(ms)), 5),
+                "p10_ms": round(float(np.percentile(ms, 10)), 5),
+                "p90_ms": round(float(np.percentile(ms, 90)), 5),
+                "median_GBps": round(unique_bytes / (float(np.median(ms)) * 1e-3) / 1e9, 2)}
+
+    latency = {"two_layers": distribution(False, args.steps, True),
+               "one_layer": distribution(False, args.steps, False),
+               "one_layer_flushed_512MiB": distribution(True, args.steps, False)}
 
     swap = swap_leg(sp, kc, vc, tables, args.swap) if args.swap > 0 else None
 
@@ -229,6 +266,7 @@ def main():
             "mean_launch_ms": round(dec_ms_mean, 5),
             "median_launch_ms": round(float(np.median(dec_ms)), 5),
         },
+        "decode_latency": latency,
         "cpu_baseline": cpu,
     }
     if swap is not None:
