@@ -65,14 +65,20 @@ def parse():
                     help="-1: the workload's setting (0 = library choice)")
     ap.add_argument("--decode-flags", type=int, default=-1,
                     help="-1: the workload's setting (PA_DECODE_SHARED_KV for shared prompts)")
-    ap.add_argument("--decode-path", choices=["auto", "plain", "shared_prefix"], default="auto",
+    ap.add_argument("--decode-path", choices=["auto", "plain", "shared_prefix", "multi"],
+                    default="auto",
                     help="auto: the shared-prefix (cascade) decode for workloads whose "
-                         "sequences share prompt blocks, else the plain decode")
+                         "sequences share prompt blocks, else the plain decode; multi: "
+                         "--query-len draft tokens per sequence verified in one pass")
+    ap.add_argument("--query-len", type=int, default=4,
+                    help="draft tokens per sequence for --decode-path multi (causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one device copy of 1 GiB (for hardware-counter scaling)")
+    ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
+                    help="also time one pa_copy_blocks launch of N block pairs (copy-on-write)")
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="also time pa_swap_blocks moving the blocks of the first N sequences "
                          "to pinned host memory and back, beside a DMA copy of the same bytes")
@@ -113,12 +119,16 @@ def main():
     g = torch.Generator(device="cuda")
     g.manual_seed(seed + 1)
     src_t = {"f16": torch.float16, "bf16": torch.bfloat16}[sp.src_dtype]
-    k_new = torch.randn((S, Hkv, D), generator=g, device="cuda").to(src_t)
-    v_new = torch.randn((S, Hkv, D), generator=g, device="cuda").to(src_t)
+    # new rows per step: one token per sequence (the last position), or the query_len
+    # draft positions of the multi-token path
+    T = args.query_len if args.decode_path == "multi" else 1
+    k_new = torch.randn((S * T, Hkv, D), generator=g, device="cuda").to(src_t)
+    v_new = torch.randn((S * T, Hkv, D), generator=g, device="cuda").to(src_t)
     tables_d = torch.from_numpy(tables).cuda()
     ctx_d = torch.from_numpy(ctx).cuda()
-    seq_ids = torch.arange(S, dtype=torch.int32, device="cuda")
-    positions = (ctx_d - 1).to(torch.int32)
+    seq_ids = torch.arange(S, dtype=torch.int32, device="cuda").repeat_interleave(T)
+    positions = (ctx_d.repeat_interleave(T) - T
+                 + torch.arange(T, dtype=torch.int32, device="cuda").repeat(S)).to(torch.int32)
     max_ctx = int(ctx.max())
     out = torch.empty_like(q)
     used_P, nparts = pa.decode_plan(S, Hq, Hkv, D, B, max_ctx, P)
@@ -143,8 +153,23 @@ def main():
         flags = args.decode_flags
     kv_bytes = workloads.kv_bytes(sp, ctx)  # K+V bytes of every sequence's own context
     unique_bytes = kv_bytes                 # K+V bytes one decode pass must read
-    kernels = "paged_decode_kernel" + (" + merge_partitions_kernel" if nparts > 1 else "")
-    if path == "shared_prefix":
+    mfma = B == 16 and Hq // Hkv >= 2        # grouped queries run on the matrix-core kernel
+    kernels = (("paged_decode_gqa_mfma_kernel" if mfma else "paged_decode_kernel")
+               + (" + merge_partitions_kernel" if nparts > 1 else ""))
+    if path == "multi":
+        qm = torch.randn((S, T, Hq, D), generator=g, device="cuda").to(q.dtype)
+        outm = torch.empty_like(qm)
+        ws_bytes = pa.decode_multi_workspace_size(S, T, Hq, Hkv, D, B, max_ctx, P)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        kernels = ("paged_decode_gqa_mfma_kernel (query_len x group columns)"
+                   + (" + merge_partitions_kernel" if nparts > 1 else ""))
+
+        def decode(layer):
+            lk, lv, ks, vs = layers[layer]
+            pa.decode_multi(qm, lk, lv, tables_d, ctx_d, max_ctx, sp.scale, ks, vs,
+                            partition_size=P, flags=flags, out=outm, workspace=ws,
+                            stream=stream)
+    elif path == "shared_prefix":
         if not sp.group_size:
             raise SystemExit("--decode-path shared_prefix needs a workload with shared prompts")
         prefix_blocks = (pl // B).astype(np.int32)
@@ -229,6 +254,7 @@ def main():
                "one_layer_flushed_512MiB": distribution(True, args.steps, False)}
 
     swap = swap_leg(sp, kc, vc, tables, args.swap) if args.swap > 0 else None
+    copy = copy_leg(sp, kc, vc, tables, args.copy_blocks) if args.copy_blocks > 0 else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -248,7 +274,7 @@ def main():
         "dtype": sp.kv_dtype,
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "decode_tokens_per_s": round(S * T / (ms_per_step * 1e-3), 1),
         "config": {
             "workload": sp.name, "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": B, "context_lens": f"U[{sp.ctx_lo},{sp.ctx_hi}]"
@@ -257,7 +283,7 @@ def main():
             "num_partitions": nparts, "kv_bytes_per_step": kv_bytes,
             "unique_kv_bytes_per_step": unique_bytes, "seed": seed,
             "decode_flags": flags, "decode_path": path,
-        },
+        } | ({"query_len": T} if path == "multi" else {}),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -271,7 +297,40 @@ def main():
     }
     if swap is not None:
         line["swap"] = swap
+    if copy is not None:
+        line["copy_blocks"] = copy
     print(json.dumps(line), flush=True)
+
+
+def copy_leg(sp, kc, vc, tables, n):
+    """Batched copy-on-write: one pa_copy_blocks launch duplicating n distinct blocks of the
+    batch into n free blocks (K and V), timed with HIP events; GB/s = bytes read + written
+    over the launch time."""
+    import torch
+
+    import paged_kv_cache_89_amd as pa
+
+    used = np.unique(tables[tables >= 0])
+    free = np.setdiff1d(np.arange(sp.num_blocks), used)
+    n = int(min(n, used.size, free.size))
+    rng = np.random.default_rng(7)
+    pairs = np.stack([rng.choice(used, n, replace=False), rng.choice(free, n, replace=False)],
+                     1).astype(np.int32)
+    pd = torch.from_numpy(pairs).cuda()
+    stream = torch.cuda.current_stream()
+    pa.copy_blocks(kc, vc, pd, stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    a.record(stream)
+    for _ in range(reps):
+        pa.copy_blocks(kc, vc, pd, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    moved = 2 * 2 * n * kc[0].numel() * kc.element_size()   # K and V, read + write
+    return {"pairs": n, "bytes_read_and_written": moved, "ms": round(ms, 4),
+            "GBps": round(moved / (ms * 1e-3) / 1e9, 2)}
 
 
 def swap_leg(sp, kc, vc, tables, nseq):

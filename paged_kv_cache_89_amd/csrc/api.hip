@@ -54,10 +54,10 @@ struct Plan {
 // 256 tokens run unsplit (the merge launch would cost more than it balances).  Otherwise
 // partitions of `base` tokens keep units long enough to stream efficiently while cutting
 // ragged batches into near-uniform pieces; when that leaves too few units to fill the
-// chip's wave slots (256 CUs), the partition is halved while it stays at least 128 tokens.  Measured on
-// MI355X: 768-token partitions beat 512 by 3 % on the GQA workload and 0.5-1 % on the
-// OPT-13B one; the shared-prefix decode keeps 512, which splits its block-aligned prompts
-// evenly (768 measured 4 % slower there).
+// chip's wave slots (256 CUs), the partition is halved while it stays at least 128 tokens.
+// Measured on MI355X: 768-token partitions beat 512 by 3 % on the GQA workload and
+// 0.5-1 % on the OPT-13B one; the shared-prefix decode keeps 512, which splits its
+// block-aligned prompts evenly (768 measured 4 % slower there).
 constexpr int32_t kAutoPartition = 768;
 constexpr int32_t kCascadePartition = 512;
 
