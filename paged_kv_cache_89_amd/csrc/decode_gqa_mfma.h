@@ -151,8 +151,17 @@ __device__ __forceinline__ void e4m3x16_widen(const u32x4 src, u32x4 (&dst)[2]) 
 // LANE: per-column visibility (each query column has its own token range and draft
 // mask), needed by the prefix units of the shared-prefix decode and by multi-token
 // queries; plain and suffix units share one token count and use the cheaper mask.
+// Waves per SIMD the register allocation must allow.  e4m3 blocks carry half the bytes of
+// 16-bit ones, so each wave keeps half as much in flight and occupancy matters: the
+// per-column-mask e4m3 units (G <= 8) fit three waves per SIMD without spilling; the other
+// instantiations are left to the compiler (they run at the same speed with two or three).
+constexpr int gqa_min_waves(int kvk, bool lane, int g) {
+  return (kvk == KIND_E4M3 && lane && g <= 8) ? 3 : PA_GQA_MIN_WAVES;
+}
+
 template <int D, int QK, int KVK, int G, bool NT, bool LANE>
-__global__ __launch_bounds__(256, PA_GQA_MIN_WAVES) void paged_decode_gqa_mfma_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode_gqa_mfma_kernel(
+    const DecodeArgs a) {
   constexpr int BS = 16;
   constexpr int KSTEPS = D / 32;             // 16x16x32 steps over the head dimension
   constexpr int NTILES = D / 16;             // 16-wide output slices
@@ -449,7 +458,7 @@ __global__ __launch_bounds__(256, PA_GQA_MIN_WAVES) void paged_decode_gqa_mfma_k
       // four tokens so both halves meet the same values; the A-operand scale 2^-kb undoes
       // the lift.  The operands carry 8 codes of the 32 the instruction takes (the rest
       // zero); one tile at a time keeps a single zero-padded V operand live (153 instead of
-      // 184 VGPRs at D = 128: three waves per SIMD instead of two, +4 % measured).
+      // 184 VGPRs at D = 128 for plain units: three waves per SIMD instead of two).
       const v8i pop8 = v8i{(int)hi, (int)lo, 0, 0, 0, 0, 0, 0};
       l_part += (p[0] + p[1]) + (p[2] + p[3]);
       const int rho = 4 * r + ((c >> 1) & 3);
@@ -459,8 +468,7 @@ __global__ __launch_bounds__(256, PA_GQA_MIN_WAVES) void paged_decode_gqa_mfma_k
             (lds_v2i*)(vt + rho * PITCH + ((t ^ swz(rho)) * 16) + 8 * (c & 1)));
         const v8i vop = v8i{vv[0], vv[1], 0, 0, 0, 0, 0, 0};
         cacc[t] = mfma_e4m3(pop8, vop, cacc[t], 127 - kb, 127);
-        // (per-column-mask units stay at two waves per SIMD either way; leave them free)
-        if constexpr (!LANE) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       return;
     }
