@@ -59,6 +59,23 @@ const char* pa_last_error(void);
 /* Library version string, e.g. "0.1.0". */
 const char* pa_version(void);
 
+/* Validation mode (off by default; on when the environment has PA_VALIDATE=1 at the first
+ * call, or after pa_set_validate(1)).  The device operations read index data that lives in
+ * device memory -- context_lens, block_tables, prefix_blocks, seq_ids / positions, block
+ * pairs -- and trust it: out-of-range entries are skipped or clamped as each operation
+ * documents, never dereferenced.  In validation mode each of pa_write_kv, pa_copy_blocks,
+ * pa_swap_blocks, pa_decode, pa_decode_shared_prefix and pa_decode_multi first copies that
+ * data to the host on its stream (after everything queued before it), synchronises and
+ * checks it: ids inside their pools, context_lens in [0, max_context_len] and within the
+ * table's reach (at least query_len for pa_decode_multi), the table entries a sequence
+ * reads, prefix_blocks in [0, max_prefix_blocks] with every member's prefix entries equal
+ * to the first member's, no cache slot or destination block written twice in one call,
+ * and (pa_copy_blocks) no destination that another pair reads.  The first violation is
+ * returned as PA_ERR_INVALID_ARG with its index in pa_last_error(), and nothing is
+ * launched.  A debugging aid: every call then costs a host round trip.
+ * Returns the previous setting (0 or 1). */
+int32_t pa_set_validate(int32_t on);
+
 /* ------------------------------------------------------------------------------------
  * CPU block manager.
  * [P1] sec. 4 "Allocation Lifecycle": a prompt of N tokens takes ceil(N / B) blocks from

@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, f32, sz = c.c_void_p, c.c_int32, c.c_float, c.c_size_t
     L.pa_last_error.restype = c.c_char_p
     L.pa_version.restype = c.c_char_p
+    L.pa_set_validate.argtypes = [i32]
+    L.pa_set_validate.restype = i32
     L.pa_bm_create.argtypes = [i32, i32, vp, c.POINTER(vp)]
     L.pa_bm_destroy.argtypes = [vp]
     L.pa_bm_destroy.restype = None
@@ -111,6 +113,12 @@ def _check(status: int):
 
 def version() -> str:
     return lib().pa_version().decode()
+
+
+def set_validate(on: bool) -> bool:
+    """pa_set_validate: host-side checks of every device operation's index data (tables,
+    lengths, slots, block pairs) before it launches; returns the previous setting."""
+    return bool(lib().pa_set_validate(1 if on else 0))
 
 
 def _np(a, dtype=np.int32):

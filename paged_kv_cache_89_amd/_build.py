@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 MFMA_SOURCES = ["decode_gqa_d64_nt.hip", "decode_gqa_d64_t.hip", "decode_gqa_d128_nt.hip",
                 "decode_gqa_d128_t.hip"]
-SOURCES = ["api.hip", "block_manager.cpp", "write_kv.hip", "merge.hip", "copy_blocks.hip",
+SOURCES = ["api.hip", "validate.hip", "block_manager.cpp", "write_kv.hip", "merge.hip", "copy_blocks.hip",
            "decode_d64_nt.hip", "decode_d64_t.hip", "decode_d128_nt.hip", "decode_d128_t.hip",
            "decode_gqa.hip", *MFMA_SOURCES]
 

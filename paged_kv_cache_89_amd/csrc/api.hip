@@ -9,6 +9,7 @@
 
 #include "launch.h"
 #include "paged_attn.h"
+#include "validate.h"
 
 static thread_local std::string g_last_error;
 
@@ -148,6 +149,8 @@ const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 const char* pa_version(void) { return "0.1.0"; }
 
+int32_t pa_set_validate(int32_t on) { return set_validate(on != 0); }
+
 uint64_t pa_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
                                pa_dtype kv_dtype) {
   int kind;
@@ -177,6 +180,12 @@ pa_status pa_write_kv(const void* k_src, const void* v_src, void* k_cache, void*
     return fail(PA_ERR_INVALID_ARG, "pa_write_kv: NULL pointer");
   if (ck == KIND_E4M3 && !(std::isfinite(k_inv_scale) && std::isfinite(v_inv_scale)))
     return fail(PA_ERR_INVALID_ARG, "pa_write_kv: non-finite inverse scale");
+  if (validate_enabled()) {
+    std::string err;
+    if (!validate_write(block_tables, seq_ids, positions, num_seqs, max_blocks_per_seq, num_tokens,
+                        num_blocks, block_size, stream, &err))
+      return fail(PA_ERR_INVALID_ARG, err);
+  }
   WriteArgs a;
   a.k_src = k_src; a.v_src = v_src; a.k_cache = k_cache; a.v_cache = v_cache;
   a.tables = block_tables; a.seq_ids = seq_ids; a.positions = positions;
@@ -201,6 +210,12 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pair
     return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block size in bytes must be a multiple of 16");
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID_ARG, "pa_copy_blocks: NULL pointer");
+  if (validate_enabled()) {
+    std::string err;
+    if (!validate_pairs("pa_copy_blocks", block_pairs, num_pairs, num_blocks, num_blocks, true,
+                        stream, &err))
+      return fail(PA_ERR_INVALID_ARG, err);
+  }
   CopyArgs a{k_cache, v_cache, k_cache, v_cache, block_pairs, num_pairs, num_blocks, num_blocks,
              bytes};
   return hip_status(launch_copy_blocks(a, (hipStream_t)stream), "pa_copy_blocks launch");
@@ -258,6 +273,12 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void
   if ((st = device_view(dst_k, "dst_k", &dk)) != PA_OK) return st;
   if ((st = device_view(dst_v, "dst_v", &dv)) != PA_OK) return st;
   if ((st = device_view(block_pairs, "block_pairs", &pp)) != PA_OK) return st;
+  if (validate_enabled()) {
+    std::string err;
+    if (!validate_pairs("pa_swap_blocks", block_pairs, num_pairs, src_blocks, dst_blocks, false,
+                        stream, &err))
+      return fail(PA_ERR_INVALID_ARG, err);
+  }
   CopyArgs a{sk, sv, dk, dv, (const int32_t*)pp, num_pairs, src_blocks, dst_blocks, bytes};
   return hip_status(launch_copy_blocks(a, (hipStream_t)stream), "pa_swap_blocks launch");
 }
@@ -332,6 +353,12 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
   if (need > 0 && (!workspace || workspace_bytes_given < need))
     return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace needs " + std::to_string(need) +
                                         " bytes, got " + std::to_string(workspace_bytes_given));
+  if (validate_enabled()) {
+    std::string err;
+    if (!validate_decode("pa_decode", block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                         num_blocks, block_size, max_context_len, 0, stream, &err))
+      return fail(PA_ERR_INVALID_ARG, err);
+  }
 
   DecodeArgs a;
   a.out = out; a.q = query; a.k = k_cache; a.v = v_cache;
@@ -438,6 +465,15 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
   if (!workspace || workspace_bytes_given < need)
     return fail(PA_ERR_INVALID_ARG, std::string(who) + ": workspace needs " + std::to_string(need) +
                                         " bytes, got " + std::to_string(workspace_bytes_given));
+  if (validate_enabled()) {
+    std::string err;
+    if (!validate_decode(who, block_tables, context_lens, num_seqs, max_blocks_per_seq, num_blocks,
+                         block_size, max_context_len, 0, stream, &err) ||
+        !validate_prefix(who, block_tables, context_lens, prefix_blocks, num_seqs, seq_group,
+                         max_blocks_per_seq, num_blocks, block_size, max_prefix_blocks, stream,
+                         &err))
+      return fail(PA_ERR_INVALID_ARG, err);
+  }
   const int32_t slots = cp.pre_parts + cp.suf_parts;
   const int32_t groups = num_seqs / seq_group;
   const int64_t pre_units = (int64_t)groups * num_kv_heads * cp.pre_parts;
@@ -547,6 +583,12 @@ pa_status pa_decode_multi(void* out, const void* query, const void* k_cache, con
   if (need > 0 && (!workspace || workspace_bytes_given < need))
     return fail(PA_ERR_INVALID_ARG, who + ": workspace needs " + std::to_string(need) +
                                         " bytes, got " + std::to_string(workspace_bytes_given));
+  if (validate_enabled()) {
+    std::string err;
+    if (!validate_decode(who.c_str(), block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                         num_blocks, block_size, max_context_len, query_len, stream, &err))
+      return fail(PA_ERR_INVALID_ARG, err);
+  }
   DecodeArgs a;
   a.out = out; a.q = query; a.k = k_cache; a.v = v_cache;
   a.tables = block_tables; a.ctx = context_lens;
