@@ -151,6 +151,24 @@ __device__ __forceinline__ void e4m3x16_widen(const u32x4 src, u32x4 (&dst)[2]) 
 // LANE: per-column visibility (each query column has its own token range and draft
 // mask), needed by the prefix units of the shared-prefix decode and by multi-token
 // queries; plain and suffix units share one token count and use the cheaper mask.
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one matrix-core column's four
+// row groups) with the gfx950 row swaps, which stay on the VALU.  Measured lane layout:
+// permlane16_swap(x, x) returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of x, permlane32_swap(x,
+// x) halves (0, 0) and (1, 1); combining the two results is combining x with x ^ 16
+// (x ^ 32).  Every lane ends with the same value.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Waves per SIMD the register allocation must allow.  e4m3 blocks carry half the bytes of
 // 16-bit ones, so each wave keeps half as much in flight and occupancy matters: the
 // per-column-mask e4m3 units (G <= 8) fit three waves per SIMD without spilling; the other
@@ -287,8 +305,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     float mx = 0.f;
 #pragma unroll
     for (int i = 0; i < QD; ++i) mx = fmaxf(mx, fabsf(qv[i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows_max(mx);
     // mx in [2^(x-1), 2^x) -> scale by 2^(8-x): the largest element lands in [128, 256)
     int e = (mx > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(mx) : 0;
     e = e > 127 ? 127 : e;
@@ -418,8 +435,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
       z[i] = ok ? sv[i] * qk_scale : -INFINITY;
     }
     float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = rows_max(bm);
     const bool move = bm > m_ref + kLazyRescaleLog2;  // false for padding heads (bm = -inf)
     if (__builtin_amdgcn_ballot_w64(move)) {
       const float mn = move ? bm : m_ref;
@@ -447,7 +463,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         p[i] = fast_exp2(z[i] - ms);
-        pp[i] = fast_exp2(z[i] - ms + (float)kb);
+        pp[i] = __builtin_amdgcn_ldexpf(p[i], kb);  // exact
       }
       const uint32_t hi = e4m3x4_pack(pp[0], pp[1], pp[2], pp[3]);
       float back[4];
@@ -516,10 +532,14 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   TableSlice ts;
   ts.init(table_row, j0, j1, a.num_blocks, lane);
   u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
+  // The barrier keeps the scheduler from hoisting the next block's LDS staging (and its
+  // wait for that block's loads) above these loads: the loads of block j+1 must be in
+  // flight before the wave waits for block j.
   auto fetch = [&](int jj, u32x4 (&kr)[NLDS], u32x4 (&vr)[NLDS]) {
     const int p = ts.get(jj);
     load_tile(kbase, p, kr);
     load_tile(vbase, p, vr);
+    __builtin_amdgcn_sched_barrier(0);
   };
   fetch(j0, ka, va);
   // steady state: every load in the loop is unconditional (see the vector kernel)
@@ -540,8 +560,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   }
 
   // head c's denominator: sum of its four lanes' shares
-  float L = l_part + __shfl_xor(l_part, 16);
-  L += __shfl_xor(L, 32);
+  const float L = rows_sum(l_part);
   // accumulator row 4r + i (lane c holds dim 16t + c of slice t) belongs to head 4r + i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
