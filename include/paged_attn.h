@@ -21,7 +21,10 @@
  *     outside [0, num_blocks) are never dereferenced (the decode clamps them to block 0,
  *     the writer skips them) so malformed tables give wrong numbers, not faults;
  *   - the library allocates no device memory: scratch space is a caller-provided
- *     workspace sized by pa_decode_workspace_size().
+ *     workspace sized by pa_decode_workspace_size();
+ *   - a call enqueues kernels only (no allocation, memset or host wait), so it can be
+ *     captured into a HIP graph and replayed; validation mode (pa_set_validate) waits on
+ *     the stream and must be off while a stream is captured.
  *
  * Cache layout (both K and V, every dtype): [num_blocks][num_kv_heads][block_size][head_dim],
  * i.e. the per-block [block_size, head_dim] key and value tiles of [P1] sec. 3 (eq. for
