@@ -134,9 +134,12 @@ def test_decode_plan_and_workspace():
     assert (P, n) == (512, 64)
     assert pa.decode_workspace_size(8, 32, 32, 128, 32, 32768, 512) == 8 * 32 * 64 * 130 * 4
     # library choice: contexts <= 256 unsplit; else 768-token partitions, halved (staying
-    # at least 128) while the grid has < 4096 units
+    # at least 128) while the grid has < 4096 units; bounds of >= 16 such partitions take
+    # 64-block partitions when that still gives >= 4096 units
     assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0) == (768, 3)
-    assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (768, 43)
+    assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (2048, 16)
+    assert pa.decode_plan(4, 32, 32, 128, 32, 32768, 0) == (768, 43)   # 2048 units only
+    assert pa.decode_plan(128, 32, 8, 128, 16, 8192, 0) == (768, 11)  # below 16 x 768
     assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (0, 1)
     assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0) == (192, 11)
     assert pa.decode_plan(16, 8, 8, 64, 16, 8192, 0) == (192, 43)
