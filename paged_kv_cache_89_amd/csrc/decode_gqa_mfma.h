@@ -169,12 +169,46 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// e4m3 tiles on the fp8 matrix cores: 1 = K/V go from HBM straight into two LDS stages per
+// wave (global_load_lds; no register staging, about 110 VGPRs, four waves per SIMD);
+// 0 = through registers like the 16-bit tiles (compile-time switch for measurements).
+#ifndef PA_FP8_LDS_DMA
+#define PA_FP8_LDS_DMA 1
+#endif
+
+// One 16-byte-per-lane load from global memory into LDS: lane l's 16 bytes land at LDS
+// byte lds + 16 l (the wave fills 1 KiB).  The LDS address travels in M0, which nothing
+// else in these kernels uses.  vmcnt drops once the bytes are in LDS (wait_vmcnt).  The
+// stage being refilled was read by the block before: lgkmcnt(0) first, so those reads have
+// returned before the new bytes can land.
+template <bool NT>
+__device__ __forceinline__ void load_lds_x4(const void* src, uint32_t lds) {
+  if constexpr (NT)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(src), "s"(lds) : "memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds) : "memory");
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Waves per SIMD the register allocation must allow.  e4m3 blocks carry half the bytes of
-// 16-bit ones, so each wave keeps half as much in flight and occupancy matters: the
-// per-column-mask e4m3 units (G <= 8) fit three waves per SIMD without spilling; the other
-// instantiations are left to the compiler (they run at the same speed with two or three).
+// 16-bit ones, so each wave keeps half as much in flight and occupancy matters: with the
+// LDS ring every e4m3 instantiation fits four waves per SIMD (the ring's 32 KiB per
+// workgroup allows five); through registers, the per-column-mask e4m3 units (G <= 8) fit
+// three without spilling.  The 16-bit instantiations are left to the compiler (they run at
+// the same speed with two or three).
 constexpr int gqa_min_waves(int kvk, bool lane, int g) {
-  return (kvk == KIND_E4M3 && lane && g <= 8) ? 3 : PA_GQA_MIN_WAVES;
+  return kvk == KIND_E4M3 ? (PA_FP8_NATIVE && PA_FP8_LDS_DMA ? 4 : (lane && g <= 8) ? 3
+                                                                                  : PA_GQA_MIN_WAVES)
+                          : PA_GQA_MIN_WAVES;
 }
 
 template <int D, int QK, int KVK, int G, bool NT, bool LANE>
@@ -200,8 +234,10 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   static_assert(NLDS * 1024 == STILE, "tile must be covered by whole wave loads");
   static_assert(G >= 2 && G <= 16, "group size");
   using Ops = MfmaOps<QK>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[4][TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_ktiles[4][TILE];
+  // per wave: NST stages of (K tile, V tile)
+  constexpr bool DMA = NATIVE && PA_FP8_LDS_DMA;
+  constexpr int NST = DMA ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_buf[4][NST][2][TILE];
 
   // 16-byte chunk x of LDS row `row` holds chunk x ^ swz(row) of the V row: the two
   // chunks every ds_read_b64_tr_b16 takes from each of 16 rows then fall on distinct
@@ -279,6 +315,67 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     return;
   }
 
+  // The query's loads go out together with the table-slice load (neither depends on the
+  // other), and the first block's loads before the query is converted: those latencies
+  // hide the unit's set-up.  Lane (r, c) loads head c's elements (zeros for c >= G):
+  // dims QD*r .. +QD for the e4m3 contraction, dims 32kk + 8r .. +8 otherwise.
+  constexpr int QL = NATIVE ? QD / 8 : KSTEPS;  // 16-byte query loads per lane
+  u32x4 qraw[QL];
+  if (c < G) {
+    const uint16_t* qrow = (const uint16_t*)a.q + row_of(c) * D;
+#pragma unroll
+    for (int k = 0; k < QL; ++k)
+      qraw[k] = *(const u32x4*)(qrow + (NATIVE ? QD * r + 8 * k : 32 * k + 8 * r));
+  } else {
+#pragma unroll
+    for (int k = 0; k < QL; ++k) qraw[k] = u32x4{0, 0, 0, 0};
+  }
+  const size_t blk_stride = (size_t)a.num_kv_heads * STILE;
+  const char* kbase = (const char*)a.k + (size_t)kvh * STILE;
+  const char* vbase = (const char*)a.v + (size_t)kvh * STILE;
+  const uint32_t voff = (uint32_t)lane * 16;  // natural 1 KiB wave loads (K and V)
+  auto load_tile = [&](const char* base, int phys, u32x4 (&t)[NLDS]) {
+    const char* p = base + (size_t)phys * blk_stride;
+#pragma unroll
+    for (int i = 0; i < NLDS; ++i) {
+      if constexpr (NT) t[i] = __builtin_nontemporal_load((const u32x4*)(p + voff + 1024 * i));
+      else t[i] = *(const u32x4*)(p + voff + 1024 * i);
+    }
+  };
+  TableSlice ts;
+  ts.init(table_row, j0, j1, a.num_blocks, lane);
+  u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
+  // The barrier keeps the scheduler from hoisting the next block's LDS staging (and its
+  // wait for that block's loads) above these loads: the loads of block j+1 must be in
+  // flight before the wave waits for block j.
+  auto fetch = [&](int jj, u32x4 (&kr)[NLDS], u32x4 (&vr)[NLDS]) {
+    const int p = ts.get(jj);
+    load_tile(kbase, p, kr);
+    load_tile(vbase, p, vr);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // LDS-ring path: block j sits in stage (j - j0) mod 2.  Byte 16 * lane of 1 KiB piece i
+  // of a tile is row i * TPLS + lane / LPTS, chunk lane % LPTS, which must hold the row's
+  // chunk (lane % LPTS) ^ (row mod CPR) of the swizzled layout: that is what the lane
+  // fetches, so the wave still reads whole 1 KiB pieces.
+  uint32_t goff[NLDS];
+#pragma unroll
+  for (int i = 0; i < NLDS; ++i) {
+    const int row = i * TPLS + lane / LPTS;
+    goff[i] = i * 1024 + (lane / LPTS) * (D * E) + (((lane % LPTS) ^ (row % CPR)) * 16);
+  }
+  auto issue = [&](int jj, int st) {
+    const size_t boff = (size_t)ts.get(jj) * blk_stride;
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][st][0]));
+    const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][st][1]));
+#pragma unroll
+    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(kbase + boff + goff[i], kl + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(vbase + boff + goff[i], vl + 1024 * i);
+  };
+  if constexpr (DMA) issue(j0, 0);
+  else fetch(j0, ka, va);
+
   // Q^T operand: lane (r, c) holds head c's dims 32kk + 8r .. +8 (zero for padding heads)
   u32x4 qop[NATIVE ? 1 : KSTEPS];
   // native: head c's dims QD*r .. +QD as three e4m3 terms (zero for padding heads), and
@@ -287,20 +384,13 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   int q_exp = 127;
   if constexpr (NATIVE) {
     float qv[QD];
-    if (c < G) {
-      const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + row_of(c) * D + QD * r);
 #pragma unroll
-      for (int k = 0; k < QD / 8; ++k) {
-        const u32x4 t = qp[k];
+    for (int k = 0; k < QD / 8; ++k) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          qv[8 * k + 2 * w] = (QK == KIND_BF16) ? bf16_lo(t[w]) : f16_lo(t[w]);
-          qv[8 * k + 2 * w + 1] = (QK == KIND_BF16) ? bf16_hi(t[w]) : f16_hi(t[w]);
-        }
+      for (int w = 0; w < 4; ++w) {
+        qv[8 * k + 2 * w] = (QK == KIND_BF16) ? bf16_lo(qraw[k][w]) : f16_lo(qraw[k][w]);
+        qv[8 * k + 2 * w + 1] = (QK == KIND_BF16) ? bf16_hi(qraw[k][w]) : f16_hi(qraw[k][w]);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < QD; ++i) qv[i] = 0.f;
     }
     float mx = 0.f;
 #pragma unroll
@@ -329,12 +419,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     }
   } else {
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (c < G)
-        qop[kk] = *(const u32x4*)((const uint16_t*)a.q + row_of(c) * D + 32 * kk + 8 * r);
-      else
-        qop[kk] = u32x4{0, 0, 0, 0};
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) qop[kk] = qraw[kk];
   }
 
   // Output accumulators (matrix-core C operands) hold P . V relative to the reference
@@ -345,12 +430,8 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   float m_ref = -INFINITY;  // reference maximum of head c (log2 units), same in its 4 lanes
   float l_part = 0.f;       // this lane's share of head c's denominator
 
-  const size_t blk_stride = (size_t)a.num_kv_heads * STILE;
-  const char* kbase = (const char*)a.k + (size_t)kvh * STILE;
-  const char* vbase = (const char*)a.v + (size_t)kvh * STILE;
-  const uint32_t voff = (uint32_t)lane * 16;  // natural 1 KiB wave loads (K and V)
-  uint8_t* vt = lds_tiles[wave];
-  uint8_t* kt = lds_ktiles[wave];
+  uint8_t* kt = lds_buf[wave][0][0];
+  uint8_t* vt = lds_buf[wave][0][1];
   const float qk_scale = a.qk_scale;
   // This lane's share of a tile: wave load i, token row i*TPLS + lane/LPTS, elements
   // (lane % LPTS) * EPLS .. +EPLS, i.e. LDS chunks (lane % LPTS) * CPL .. +CPL of that row.
@@ -369,14 +450,6 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   }
   const int trow = 4 * r + c / 4;
 
-  auto load_tile = [&](const char* base, int phys, u32x4 (&t)[NLDS]) {
-    const char* p = base + (size_t)phys * blk_stride;
-#pragma unroll
-    for (int i = 0; i < NLDS; ++i) {
-      if constexpr (NT) t[i] = __builtin_nontemporal_load((const u32x4*)(p + voff + 1024 * i));
-      else t[i] = *(const u32x4*)(p + voff + 1024 * i);
-    }
-  };
   // widen (e4m3) and write one tile into LDS; rows at or beyond n become zeros when
   // `mask` (their bytes may be NaN and the matrix core would turn 0 * NaN into NaN)
   auto stage = [&](uint8_t* dst, const uint32_t (&off)[NLDS][CPL], bool mask, int j,
@@ -529,34 +602,44 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     stage(vt, vw_off, true, j, vr);
     finish(j, logits());
   };
-  TableSlice ts;
-  ts.init(table_row, j0, j1, a.num_blocks, lane);
-  u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
-  // The barrier keeps the scheduler from hoisting the next block's LDS staging (and its
-  // wait for that block's loads) above these loads: the loads of block j+1 must be in
-  // flight before the wave waits for block j.
-  auto fetch = [&](int jj, u32x4 (&kr)[NLDS], u32x4 (&vr)[NLDS]) {
-    const int p = ts.get(jj);
-    load_tile(kbase, p, kr);
-    load_tile(vbase, p, vr);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  fetch(j0, ka, va);
-  // steady state: every load in the loop is unconditional (see the vector kernel)
-  int j = j0;
-  while (j + 2 < j1) {
-    fetch(j + 1, kb, vb);
-    process(j, ka, va);
-    fetch(j + 2, ka, va);
-    process(j + 1, kb, vb);
-    j += 2;
-  }
-  if (j + 1 < j1) {
-    fetch(j + 1, kb, vb);
-    process(j, ka, va);
-    process(j + 1, kb, vb);
+  if constexpr (DMA) {
+    constexpr int PER = 2 * NLDS;  // vector-memory operations per block
+    int st = 0;
+    for (int j = j0; j < j1; ++j) {
+      // fill the other stage (read by block j - 1) with block j + 1, then wait for block j
+      if (j + 1 < j1) {
+        issue(j + 1, st ^ 1);
+        wait_vmcnt<PER>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      kt = lds_buf[wave][st][0];
+      vt = lds_buf[wave][st][1];
+      if (j * BS + BS > n) {  // V rows at or beyond n become zeros (their bytes may be NaN)
+#pragma unroll
+        for (int x = lane; x < TILE / 16; x += 64)
+          if (j * BS + x / CPR >= n) *(u32x4*)(vt + x * 16) = u32x4{0, 0, 0, 0};
+      }
+      finish(j, logits());
+      st ^= 1;
+    }
   } else {
-    process(j, ka, va);
+    // steady state: every load in the loop is unconditional (see the vector kernel)
+    int j = j0;
+    while (j + 2 < j1) {
+      fetch(j + 1, kb, vb);
+      process(j, ka, va);
+      fetch(j + 2, ka, va);
+      process(j + 1, kb, vb);
+      j += 2;
+    }
+    if (j + 1 < j1) {
+      fetch(j + 1, kb, vb);
+      process(j, ka, va);
+      process(j + 1, kb, vb);
+    } else {
+      process(j, ka, va);
+    }
   }
 
   // head c's denominator: sum of its four lanes' shares
