@@ -546,8 +546,8 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
       // P's operand: head c, tokens 4r .. 4r+3 as hi then lo; V's operand repeats those
       // four tokens so both halves meet the same values; the A-operand scale 2^-kb undoes
       // the lift.  The operands carry 8 codes of the 32 the instruction takes (the rest
-      // zero); one tile at a time keeps a single zero-padded V operand live (153 instead of
-      // 184 VGPRs at D = 128 for plain units: three waves per SIMD instead of two).
+      // zero); issuing one tile at a time keeps a single zero-padded V operand live (about
+      // 30 fewer VGPRs at D = 128 than letting the compiler build all eight up front).
       const v8i pop8 = v8i{(int)hi, (int)lo, 0, 0, 0, 0, 0, 0};
       l_part += (p[0] + p[1]) + (p[2] + p[3]);
       const int rho = 4 * r + ((c >> 1) & 3);
