@@ -412,20 +412,31 @@ def cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, target_s):
         qb = q[:nseq].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
         return qb, bits(kc), bits(vc), t, ctx[:nseq].copy()
 
-    def run(nseq):
+    def run(nseq, nthreads=threads):
         qb, kb, vb, t, c = sample(nseq)
         t0 = time.perf_counter()
         oracle.decode(qb, dt[sp.q_dtype], kb, vb, dt[sp.kv_dtype], t, c, sp.num_kv_heads,
-                      sp.block_size, sp.scale, k_scale, v_scale, threads=threads)
+                      sp.block_size, sp.scale, k_scale, v_scale, threads=nthreads)
         return time.perf_counter() - t0, workloads.kv_bytes(sp, c)
 
     dt1, _ = run(1)  # probe: one sequence
     nseq = int(max(1, min(sp.num_seqs, target_s / max(dt1, 1e-3))))
     secs, nbytes = run(nseq)
+    # one thread, on a sample of about a second of work
+    n1 = int(max(1, min(nseq, 1.0 / max(dt1 * threads, 1e-3))))
+    secs1, nbytes1 = run(n1, 1)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(secs, 2),
+            "single_thread_value": round(nbytes1 / secs1 / 1e9, 4), "cpu": model,
             "sample": f"{nseq} of {sp.num_seqs} sequences, all {sp.num_heads} heads "
-                      f"({nbytes} KV bytes), fp64 C++ oracle with {threads} threads"}
+                      f"({nbytes} KV bytes), fp64 C++ oracle with {threads} threads; "
+                      f"single thread: {n1} sequences"}
 
 
 if __name__ == "__main__":
