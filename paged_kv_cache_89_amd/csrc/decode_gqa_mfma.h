@@ -242,10 +242,18 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   // 16-byte chunk x of LDS row `row` holds chunk x ^ swz(row) of the V row: the two
   // chunks every ds_read_b64_tr_b16 takes from each of 16 rows then fall on distinct
   // banks (2 passes for 512 bytes), and each ds_write_b128 covers whole bank periods.
-  // Native e4m3 tiles: chunk x of row t at x ^ (t mod CPR), for K and V alike.
+  // Native e4m3 V tiles: chunk x of row t at x ^ (t mod CPR).
   auto swz = [](int row) {
     if constexpr (NATIVE) return row % CPR;
     else return 2 * ((row / RPB) % (D / 16));
+  };
+  // K tiles: chunk x of row t sits at x ^ kswz(t).  The logit operand reads of 16 lanes take
+  // one chunk from each of 16 rows; rows one 256-byte bank period apart share banks, so the
+  // e4m3 tiles (128- or 64-byte rows) rotate by the row's period index, which puts the 16
+  // reads on 16 different bank groups.  16-bit rows are a full period or more: t mod CPR.
+  auto kswz = [](int row) {
+    if constexpr (NATIVE) return (row / RPB) % CPR;
+    else return row % CPR;
   };
 
   const int lane = threadIdx.x & 63;
@@ -356,22 +364,24 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   };
   // LDS-ring path: block j sits in stage (j - j0) mod 2.  Byte 16 * lane of 1 KiB piece i
   // of a tile is row i * TPLS + lane / LPTS, chunk lane % LPTS, which must hold the row's
-  // chunk (lane % LPTS) ^ (row mod CPR) of the swizzled layout: that is what the lane
-  // fetches, so the wave still reads whole 1 KiB pieces.
-  uint32_t goff[NLDS];
+  // chunk (lane % LPTS) ^ kswz(row) (K) or ^ swz(row) (V) of the swizzled layouts: that is
+  // what the lane fetches, so the wave still reads whole 1 KiB pieces.
+  uint32_t goffk[NLDS], goffv[NLDS];
 #pragma unroll
   for (int i = 0; i < NLDS; ++i) {
     const int row = i * TPLS + lane / LPTS;
-    goff[i] = i * 1024 + (lane / LPTS) * (D * E) + (((lane % LPTS) ^ (row % CPR)) * 16);
+    const uint32_t base = i * 1024 + (lane / LPTS) * (D * E);
+    goffk[i] = base + (((lane % LPTS) ^ kswz(row)) * 16);
+    goffv[i] = base + (((lane % LPTS) ^ swz(row)) * 16);
   }
   auto issue = [&](int jj, int st) {
     const size_t boff = (size_t)ts.get(jj) * blk_stride;
     const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][st][0]));
     const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][st][1]));
 #pragma unroll
-    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(kbase + boff + goff[i], kl + 1024 * i);
+    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(kbase + boff + goffk[i], kl + 1024 * i);
 #pragma unroll
-    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(vbase + boff + goff[i], vl + 1024 * i);
+    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(vbase + boff + goffv[i], vl + 1024 * i);
   };
   if constexpr (DMA) issue(j0, 0);
   else fetch(j0, ka, va);
@@ -435,8 +445,8 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   const float qk_scale = a.qk_scale;
   // This lane's share of a tile: wave load i, token row i*TPLS + lane/LPTS, elements
   // (lane % LPTS) * EPLS .. +EPLS, i.e. LDS chunks (lane % LPTS) * CPL .. +CPL of that row.
-  // K's chunk x of row t sits at x ^ (t mod CPR): the A-operand reads (row c, chunk
-  // 4kk + r) of 16 lanes hit 16 different bank groups.  V's chunk x sits at x ^ swz(t).
+  // K's chunk x of row t sits at x ^ kswz(t): the operand reads (row c, one chunk) of 16
+  // lanes hit 16 different bank groups.  V's chunk x sits at x ^ swz(t).
   uint32_t kw_off[NLDS][CPL], vw_off[NLDS][CPL];
 #pragma unroll
   for (int i = 0; i < NLDS; ++i) {
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
       const int chunk = (lane % LPTS) * CPL + q;
-      kw_off[i][q] = row * PITCH + ((chunk ^ (row % CPR)) * 16);
+      kw_off[i][q] = row * PITCH + ((chunk ^ kswz(row)) * 16);
       vw_off[i][q] = row * PITCH + ((chunk ^ swz(row)) * 16);
     }
   }
@@ -479,9 +489,9 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     if constexpr (NATIVE) {
       // K's operand: token c, the same dims QD*r .. +QD that lane (r, c) holds of Q
       const uint8_t* row = kt + c * PITCH;
-      const u32x4 lo = *(const u32x4*)(row + ((((QD / 16) * r) ^ (c % CPR)) * 16));
+      const u32x4 lo = *(const u32x4*)(row + ((((QD / 16) * r) ^ kswz(c)) * 16));
       u32x4 hi = u32x4{0, 0, 0, 0};
-      if constexpr (QD == 32) hi = *(const u32x4*)(row + (((2 * r + 1) ^ (c % CPR)) * 16));
+      if constexpr (QD == 32) hi = *(const u32x4*)(row + (((2 * r + 1) ^ kswz(c)) * 16));
       const v8i kop = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
@@ -489,7 +499,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     } else {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int chunk = (4 * kk + r) ^ (c % CPR);
+        const int chunk = (4 * kk + r) ^ kswz(c);
         const u32x4 kop = *(const u32x4*)(kt + c * PITCH + chunk * 16);
         sc = Ops::qk(kop, qop[kk], sc);
       }
