@@ -91,3 +91,41 @@ def test_multi_token_causal_row_equals_plain_decode_of_truncated_length():
         torch.cuda.synchronize()
         # both results are rounded to bf16: allow one bf16 ulp besides the kernel error
         compare(out[:, t], ref.double().cpu().numpy(), 1e-2, 2e-2, "bf16")
+
+
+@pytest.mark.parametrize("name", ["opt13b_layer", "gqa_llama", "fp8_prefix"])
+def test_full_size_multi_token_sampled_sequences(name):
+    """Four causal draft tokens per sequence over each workload at full size, launched as
+    the benchmark's multi-token path launches it; the oracle checks every query row of a
+    sample of sequences (the longest among them), every output is finite."""
+    T = 4
+    sp = workloads.SPECS[name]
+    seed = 8900 + list(workloads.SPECS).index(name)
+    ctx, free = workloads.draw_lengths(sp, seed)
+    pg, pl = workloads.prefix_groups(sp)
+    st, tables, _, _ = oracle.build_tables(sp.num_blocks, sp.block_size, free, ctx,
+                                           sp.max_blocks, pg, pl)
+    assert st == 0 and ctx.min() >= T
+    _, kd, vd, ks, vs = workloads.device_pool(sp, seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed + 7)
+    qt = torch.float16 if sp.q_dtype == "f16" else torch.bfloat16
+    qm = torch.randn((sp.num_seqs, T, sp.num_heads, sp.head_dim), generator=g,
+                     device="cuda").to(qt)
+    flags = pa.DECODE_SHARED_KV if sp.group_size else 0
+    out = pa.decode_multi(qm, kd, vd, dev_i32(tables), dev_i32(ctx), int(ctx.max()), sp.scale,
+                          ks, vs, partition_size=sp.partition_size, flags=flags)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(seed)
+    sel = np.unique(np.concatenate([rng.integers(0, sp.num_seqs, 4), [int(np.argmax(ctx))]]))
+    qb = qm.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)[sel]
+    kb = kd.cpu().numpy() if kd.dtype == torch.uint8 else kd.cpu().view(torch.int16).numpy().view(np.uint16)
+    vb = vd.cpu().numpy() if vd.dtype == torch.uint8 else vd.cpu().view(torch.int16).numpy().view(np.uint16)
+    del kd, vd
+    ref = oracle.decode_multi(qb, DT[sp.q_dtype], kb, vb, DT[sp.kv_dtype],
+                              np.ascontiguousarray(tables[sel]), np.ascontiguousarray(ctx[sel]),
+                              sp.num_kv_heads, sp.block_size, sp.scale, ks, vs)
+    atol, rrel = tolerance(sp)
+    compare(got[sel], ref, atol, rrel, sp.q_dtype)
