@@ -1,9 +1,10 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
-One step = one pass of the whole hot path over one batch: pa_write_kv stores the new
-token of every sequence into its slot, then pa_decode (plus its partition merge when
-the plan splits) attends over every sequence's context.  Block tables come from the
-library's block manager before timing (allocation is host work, off the timed path).
+One step = one pass of the whole hot path over one batch: the new token of every sequence
+goes into its slot and the decode (plus its partition merge when the plan splits) attends
+over every sequence's context -- pa_write_kv followed by the decode, or with --step fused
+one pa_decode_append call that does both (plain path, no shared blocks).  Block tables
+come from the library's block manager before timing (allocation is host work, off the timed path).
 Inputs are synthetic, seeded, and resident in HBM before the timed region starts.
 Consecutive steps use two layers' K/V pools in turn (same tables), so a step never reads
 K/V that the previous step left in the Infinity Cache.
@@ -70,6 +71,10 @@ def parse():
                     help="auto: the shared-prefix (cascade) decode for workloads whose "
                          "sequences share prompt blocks, else the plain decode; multi: "
                          "--query-len draft tokens per sequence verified in one pass")
+    ap.add_argument("--step", choices=["fused", "separate"], default="separate",
+                    help="separate: pa_write_kv, then the decode; fused: the KV write and "
+                         "the decode in one call (pa_decode_append; plain path, workloads "
+                         "without shared blocks)")
     ap.add_argument("--query-len", type=int, default=4,
                     help="draft tokens per sequence for --decode-path multi (causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -195,6 +200,28 @@ def main():
             pa.decode(q, lk, lv, tables_d, ctx_d, max_ctx, sp.scale, ks, vs,
                       partition_size=P, flags=flags, out=out, workspace=ws, stream=stream)
 
+    # The step: the new tokens' KV write and the decode, as two launches or as one
+    # (pa_decode_append stores each sequence's new row from the unit that reads its block;
+    # a new token must not land in a block another sequence reads).  The two launches are
+    # the default: the fused call measured about 0.4% slower per step on the OPT-13B layer.
+    fused = args.step == "fused"
+    if fused and (path != "plain" or sp.group_size):
+        raise SystemExit("--step fused needs the plain decode path and no shared blocks")
+    if fused:
+        kernels = kernels.replace("paged_decode_kernel", "paged_decode_kernel (storing the new token)", 1) \
+            .replace("paged_decode_gqa_mfma_kernel", "paged_decode_gqa_mfma_kernel (storing the new token)", 1)
+
+        def decode(layer):
+            lk, lv, ks, vs = layers[layer]
+            k_inv = 1.0 / ks if sp.kv_dtype == "e4m3" else 1.0
+            v_inv = 1.0 / vs if sp.kv_dtype == "e4m3" else 1.0
+            pa.decode_append(q, k_new, v_new, lk, lv, tables_d, ctx_d, max_ctx, sp.scale, ks, vs,
+                             k_inv, v_inv, partition_size=P, flags=flags, out=out, workspace=ws,
+                             stream=stream)
+
+        def write(layer):  # part of the fused call
+            pass
+
     for i in range(args.warmup):
         write(i % 2)
         decode(i % 2)
@@ -289,6 +316,8 @@ def main():
             "num_partitions": nparts, "kv_bytes_per_step": kv_bytes,
             "unique_kv_bytes_per_step": unique_bytes, "seed": seed,
             "decode_flags": flags, "decode_path": path,
+            "step": ("fused: pa_decode_append stores the new tokens and decodes in one call"
+                     if fused else "pa_write_kv, then the decode"),
         } | ({"query_len": T} if path == "multi" else {}),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

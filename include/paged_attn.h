@@ -75,7 +75,9 @@ const char* pa_version(void);
  * to the first member's, no cache slot or destination block written twice in one call,
  * and (pa_copy_blocks) no destination that another pair reads.  The first violation is
  * returned as PA_ERR_INVALID_ARG with its index in pa_last_error(), and nothing is
- * launched.  A debugging aid: every call then costs a host round trip.
+ * launched (pa_decode_append is checked as pa_decode, and its new tokens' blocks must be
+ * named by no other table entry the decode reads).  A debugging aid: every call then
+ * costs a host round trip.
  * Returns the previous setting (0 or 1). */
 int32_t pa_set_validate(int32_t on);
 
@@ -297,6 +299,30 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
                     int32_t partition_size, uint32_t flags, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* Decode step with the new token written in the same launch: pa_write_kv of one new token
+ * per sequence followed by pa_decode ([P1] sec. 4 "Decoding Step": the new token's key and
+ * value go to their slot, then every query attends the sequence including it).  The new
+ * token of sequence s is at position n - 1 of its length n = context_lens[s] (clamped as
+ * pa_decode clamps it); the unit of the decode that walks that block stores the rows first,
+ * so results and cache contents equal those of the two calls.
+ *   k_new, v_new  device [num_seqs, num_kv_heads, head_dim] in q_dtype: the new rows
+ *   k_inv_scale, v_inv_scale  as for pa_write_kv (e4m3 caches: code of x * inv_scale)
+ *   Other arguments as for pa_decode; a sequence with n = 0 gets no row and a zero output.
+ * A table entry outside [0, num_blocks) for the new token's block skips the write (as
+ * pa_write_kv skips it).  Precondition: no other sequence of the batch reads the block the
+ * new token goes to (after pa_bm_append's copy-on-write a shared last block has been
+ * replaced by a private one); otherwise that sequence may see the block before or after
+ * the store.  Same support as pa_decode. */
+pa_status pa_decode_append(void* out, const void* query, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t num_blocks,
+                           int32_t max_context_len, float scale, pa_dtype q_dtype,
+                           pa_dtype kv_dtype, float k_scale, float v_scale, float k_inv_scale,
+                           float v_inv_scale, int32_t partition_size, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Shared-prefix (cascade) decode.  Same result as pa_decode (the attention definition of

@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_plan.argtypes = [i32] * 7 + [vp, vp]
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                             f32, c.c_int, c.c_int, f32, f32, i32, c.c_uint32, vp, sz, vp]
+    L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                   i32, i32, i32, f32, c.c_int, c.c_int, f32, f32, f32, f32,
+                                   i32, c.c_uint32, vp, sz, vp]
     L.pa_decode_shared_prefix_workspace_size.argtypes = [i32] * 8
     L.pa_decode_shared_prefix_workspace_size.restype = sz
     L.pa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -97,7 +100,7 @@ def lib() -> ctypes.CDLL:
     L.pa_kv_bytes_per_token.restype = c.c_uint64
     for name in ("pa_bm_create", "pa_alloc_tables", "pa_bm_free", "pa_bm_stats",
                  "pa_bm_free_list", "pa_bm_fork", "pa_bm_append", "pa_bm_table",
-                 "pa_copy_blocks", "pa_write_kv", "pa_decode_plan", "pa_decode",
+                 "pa_copy_blocks", "pa_write_kv", "pa_decode_plan", "pa_decode", "pa_decode_append",
                  "pa_bm_host_pool", "pa_bm_host_stats", "pa_bm_swap_out", "pa_bm_swap_in",
                  "pa_swap_blocks",
                  "pa_decode_shared_prefix", "pa_decode_multi"):
@@ -368,6 +371,36 @@ def decode(query, k_cache, v_cache, block_tables, context_lens, max_context_len:
                            _dtype_code(k_cache), float(k_scale), float(v_scale),
                            int(partition_size), int(flags), ws_ptr, ws_bytes,
                            _stream(stream)))
+    return out
+
+
+def decode_append(query, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                  max_context_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                  k_inv_scale: float = 1.0, v_inv_scale: float = 1.0, partition_size: int = 0,
+                  flags: int = 0, out=None, workspace=None, stream=None):
+    """pa_decode_append: the new rows k_new / v_new [S, Hkv, D] (query dtype) go to position
+    context_lens[s] - 1 of each sequence, then the decode; returns out [S, Hq, D]."""
+    torch = _torch()
+    S, Hq, D = query.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if (D2 != D or v_cache.shape != k_cache.shape or tuple(k_new.shape) != (S, Hkv, D)
+            or v_new.shape != k_new.shape or k_new.dtype != query.dtype):
+        raise ValueError("decode_append: shape or dtype mismatch")
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    need = decode_workspace_size(S, Hq, Hkv, D, B, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode_append(
+        _dev(out, "out"), _dev(query, "query"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B, MB, NB, int(max_context_len),
+        float(scale), _dtype_code(query), _dtype_code(k_cache), float(k_scale), float(v_scale),
+        float(k_inv_scale), float(v_inv_scale), int(partition_size), int(flags), ws_ptr,
+        ws_bytes, _stream(stream)))
     return out
 
 

@@ -153,6 +153,109 @@ size_t cascade_workspace_bytes(const CascadePlan& cp, int32_t num_seqs, int32_t 
 
 }  // namespace
 
+static pa_status decode_impl(const char* who, void* out, const void* query, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                    int32_t num_blocks, int32_t max_context_len, float scale,
+                    pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                    int32_t partition_size, uint32_t flags, void* workspace,
+                    size_t workspace_bytes_given, void* stream, const void* k_new,
+                    const void* v_new, float k_inv_scale, float v_inv_scale) {
+  g_last_error.clear();
+  int qk, kk;
+  if (!dtype_kind(q_dtype, &qk) || !dtype_kind(kv_dtype, &kk))
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": unknown dtype");
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
+      max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0 || partition_size < 0)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": bad size");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": num_heads must be a multiple of num_kv_heads");
+  if (partition_size % block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": partition_size must be a multiple of block_size");
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": non-finite scale");
+  if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": unknown flag bits");
+  const bool shared = (flags & PA_DECODE_SHARED_KV) != 0;
+  // Read-once K/V streams with the non-temporal hint; blocks shared between sequences of
+  // the batch stay cacheable and the sharing sequences are visited together.
+  DecodeShape shape{head_dim, block_size, qk, kk, num_heads / num_kv_heads, !shared};
+  if (!decode_supported(shape))
+    return fail(PA_ERR_UNSUPPORTED, std::string(who) + ": unsupported head_dim/block_size/group/dtype pair");
+  const bool append = k_new != nullptr || v_new != nullptr;
+  if (append && kk == KIND_E4M3 && !(std::isfinite(k_inv_scale) && std::isfinite(v_inv_scale)))
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": non-finite inverse scale");
+  if (num_seqs == 0) return PA_OK;
+  if (append && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, std::string(who) + ": NULL pointer");
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": NULL pointer");
+
+  // Tokens beyond the table's reach can never be addressed.
+  const int64_t reach = (int64_t)max_blocks_per_seq * block_size;
+  const int32_t max_ctx = (int32_t)(max_context_len < reach ? max_context_len : reach);
+  // Plan from the caller's bound, exactly as pa_decode_workspace_size does; units beyond
+  // the table's reach find no blocks and exit.
+  Plan plan;
+  pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, partition_size, &plan);
+  if (st != PA_OK) return st;
+  const size_t need = workspace_bytes(plan, num_seqs, num_heads, head_dim);
+  if (need > 0 && (!workspace || workspace_bytes_given < need))
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": workspace needs " + std::to_string(need) +
+                                        " bytes, got " + std::to_string(workspace_bytes_given));
+  if (validate_enabled()) {
+    std::string err;
+    if (!validate_decode(who, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                         num_blocks, block_size, max_context_len, 0, stream, &err))
+      return fail(PA_ERR_INVALID_ARG, err);
+    if (append && !validate_append_blocks(who, block_tables, context_lens, num_seqs,
+                                          max_blocks_per_seq, num_blocks, block_size, stream,
+                                          &err))
+      return fail(PA_ERR_INVALID_ARG, err);
+  }
+
+  DecodeArgs a;
+  a.out = out; a.q = query; a.k = k_cache; a.v = v_cache;
+  a.tables = block_tables; a.ctx = context_lens;
+  a.part_acc = need ? (float*)workspace : nullptr;
+  a.part_ml = need ? (float*)workspace + (size_t)num_seqs * num_heads * plan.num_parts * head_dim
+                   : nullptr;
+  a.num_seqs = num_seqs; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks; a.max_ctx = max_ctx;
+  a.num_parts = plan.num_parts;
+  a.blocks_per_part = plan.num_parts > 1 ? plan.partition_size / block_size
+                                         : (int32_t)((reach + block_size - 1) / block_size);
+  const int64_t units = (int64_t)num_seqs * num_kv_heads * plan.num_parts;
+  if (units > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, std::string(who) + ": grid too large");
+  a.num_units = (int32_t)units;
+  const bool f8 = kk == KIND_E4M3;
+  a.qk_scale = scale * kLog2e * (f8 ? k_scale : 1.0f);
+  a.v_scale = f8 ? v_scale : 1.0f;
+  a.seq_fastest = shared ? 1 : 0;
+  a.xcd_remap = 1;
+  a.num_slots = plan.num_parts > 1 ? plan.num_parts : 0;
+  a.slot_base = 0;
+  a.mode = MODE_PLAIN;
+  a.seq_group = 1; a.num_groups = num_seqs; a.max_prefix_blocks = 0; a.prefix_blocks = nullptr;
+  a.query_len = 1; a.tree_masks = nullptr;
+  a.append = append ? 1 : 0;
+  a.k_new = k_new; a.v_new = v_new;
+  a.k_inv_scale = k_inv_scale; a.v_inv_scale = v_inv_scale;
+  if (log_enabled())
+    std::fprintf(stderr, "[paged_attn] decode S=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d P=%d parts=%d units=%lld\n",
+                 num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
+                 plan.partition_size, plan.num_parts, (long long)units);
+  st = hip_status(launch_decode(shape, a, (hipStream_t)stream), (std::string(who) + " launch").c_str());
+  if (st != PA_OK || plan.num_parts <= 1) return st;
+  MergeArgs m;
+  m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
+  m.num_seqs = num_seqs; m.num_heads = num_heads; m.num_parts = plan.num_parts;
+  m.partition_size = plan.partition_size; m.max_ctx = max_ctx;
+  m.v_scale = a.v_scale; m.all_slots = 0;
+  return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream), (std::string(who) + " merge launch").c_str());
+}
+
 extern "C" {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
@@ -325,87 +428,30 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
                     int32_t partition_size, uint32_t flags, void* workspace,
                     size_t workspace_bytes_given, void* stream) {
+  return decode_impl("pa_decode", out, query, k_cache, v_cache, block_tables, context_lens,
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                     partition_size, flags, workspace, workspace_bytes_given, stream, nullptr,
+                     nullptr, 1.0f, 1.0f);
+}
+
+pa_status pa_decode_append(void* out, const void* query, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t num_blocks,
+                           int32_t max_context_len, float scale, pa_dtype q_dtype,
+                           pa_dtype kv_dtype, float k_scale, float v_scale, float k_inv_scale,
+                           float v_inv_scale, int32_t partition_size, uint32_t flags,
+                           void* workspace, size_t workspace_bytes_given, void* stream) {
   g_last_error.clear();
-  int qk, kk;
-  if (!dtype_kind(q_dtype, &qk) || !dtype_kind(kv_dtype, &kk))
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown dtype");
-  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
-      max_blocks_per_seq < 1 || num_blocks < 1 || max_context_len < 0 || partition_size < 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: bad size");
-  if (num_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: num_heads must be a multiple of num_kv_heads");
-  if (partition_size % block_size != 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: partition_size must be a multiple of block_size");
-  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: non-finite scale");
-  if (flags & ~(uint32_t)PA_DECODE_SHARED_KV)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: unknown flag bits");
-  const bool shared = (flags & PA_DECODE_SHARED_KV) != 0;
-  // Read-once K/V streams with the non-temporal hint; blocks shared between sequences of
-  // the batch stay cacheable and the sharing sequences are visited together.
-  DecodeShape shape{head_dim, block_size, qk, kk, num_heads / num_kv_heads, !shared};
-  if (!decode_supported(shape))
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: unsupported head_dim/block_size/group/dtype pair");
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: NULL pointer");
-
-  // Tokens beyond the table's reach can never be addressed.
-  const int64_t reach = (int64_t)max_blocks_per_seq * block_size;
-  const int32_t max_ctx = (int32_t)(max_context_len < reach ? max_context_len : reach);
-  // Plan from the caller's bound, exactly as pa_decode_workspace_size does; units beyond
-  // the table's reach find no blocks and exit.
-  Plan plan;
-  pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, partition_size, &plan);
-  if (st != PA_OK) return st;
-  const size_t need = workspace_bytes(plan, num_seqs, num_heads, head_dim);
-  if (need > 0 && (!workspace || workspace_bytes_given < need))
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: workspace needs " + std::to_string(need) +
-                                        " bytes, got " + std::to_string(workspace_bytes_given));
-  if (validate_enabled()) {
-    std::string err;
-    if (!validate_decode("pa_decode", block_tables, context_lens, num_seqs, max_blocks_per_seq,
-                         num_blocks, block_size, max_context_len, 0, stream, &err))
-      return fail(PA_ERR_INVALID_ARG, err);
-  }
-
-  DecodeArgs a;
-  a.out = out; a.q = query; a.k = k_cache; a.v = v_cache;
-  a.tables = block_tables; a.ctx = context_lens;
-  a.part_acc = need ? (float*)workspace : nullptr;
-  a.part_ml = need ? (float*)workspace + (size_t)num_seqs * num_heads * plan.num_parts * head_dim
-                   : nullptr;
-  a.num_seqs = num_seqs; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
-  a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks; a.max_ctx = max_ctx;
-  a.num_parts = plan.num_parts;
-  a.blocks_per_part = plan.num_parts > 1 ? plan.partition_size / block_size
-                                         : (int32_t)((reach + block_size - 1) / block_size);
-  const int64_t units = (int64_t)num_seqs * num_kv_heads * plan.num_parts;
-  if (units > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
-  a.num_units = (int32_t)units;
-  const bool f8 = kk == KIND_E4M3;
-  a.qk_scale = scale * kLog2e * (f8 ? k_scale : 1.0f);
-  a.v_scale = f8 ? v_scale : 1.0f;
-  a.seq_fastest = shared ? 1 : 0;
-  a.xcd_remap = 1;
-  a.num_slots = plan.num_parts > 1 ? plan.num_parts : 0;
-  a.slot_base = 0;
-  a.mode = MODE_PLAIN;
-  a.seq_group = 1; a.num_groups = num_seqs; a.max_prefix_blocks = 0; a.prefix_blocks = nullptr;
-  a.query_len = 1; a.tree_masks = nullptr;
-  if (log_enabled())
-    std::fprintf(stderr, "[paged_attn] decode S=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d P=%d parts=%d units=%lld\n",
-                 num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
-                 plan.partition_size, plan.num_parts, (long long)units);
-  st = hip_status(launch_decode(shape, a, (hipStream_t)stream), "pa_decode launch");
-  if (st != PA_OK || plan.num_parts <= 1) return st;
-  MergeArgs m;
-  m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
-  m.num_seqs = num_seqs; m.num_heads = num_heads; m.num_parts = plan.num_parts;
-  m.partition_size = plan.partition_size; m.max_ctx = max_ctx;
-  m.v_scale = a.v_scale; m.all_slots = 0;
-  return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream), "pa_decode merge launch");
+  if (num_seqs > 0 && (!k_new || !v_new))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_append: NULL pointer");
+  return decode_impl("pa_decode_append", out, query, k_cache, v_cache, block_tables,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, max_context_len, scale, q_dtype, kv_dtype,
+                     k_scale, v_scale, partition_size, flags, workspace, workspace_bytes_given,
+                     stream, k_new, v_new, k_inv_scale, v_inv_scale);
 }
 
 size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,

@@ -190,11 +190,6 @@ __device__ __forceinline__ void load_lds_x4(const void* src, uint32_t lds) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(src), "s"(lds) : "memory");
 }
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -352,6 +347,14 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   };
   TableSlice ts;
   ts.init(table_row, j0, j1, a.num_blocks, lane);
+  // appending decode: the unit that walks the sequence's last block stores the new token's
+  // row there first (a table entry outside the pool is skipped, as the KV write does)
+  if (a.append && a.mode == MODE_PLAIN && n > 0 && j1 == (n + BS - 1) / BS) {
+    const int raw = __builtin_amdgcn_readlane(ts.ids, (n - 1) / BS - ts.j0);
+    if ((unsigned)raw < (unsigned)a.num_blocks)
+      append_new_row<D, BS, QK, KVK>(a, s, kvh, raw, (n - 1) % BS, lane,
+                                     (n - 1) / BS - j0 < 2);
+  }
   u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
   // The barrier keeps the scheduler from hoisting the next block's LDS staging (and its
   // wait for that block's loads) above these loads: the loads of block j+1 must be in

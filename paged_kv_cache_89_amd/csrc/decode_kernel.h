@@ -277,6 +277,14 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
   // the block being consumed; the last one or two blocks are peeled off the loop.
   TableSlice ts;
   ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
+  // appending decode: the unit that walks the sequence's last block stores the new token's
+  // row there first (a table entry outside the pool is skipped, as the KV write does)
+  if (a.append && a.mode == MODE_PLAIN && n > 0 && j1 == nblk) {
+    const int raw = __builtin_amdgcn_readlane(ts.ids, (n - 1) / BS - ts.j0);
+    if ((unsigned)raw < (unsigned)a.num_blocks)
+      append_new_row<D, BS, QK, KVK>(a, s, kvh, raw, (n - 1) % BS, lane,
+                                     (n - 1) / BS - j0 < 2);
+  }
   LT ka[NLD], va[NLD], kb[NLD], vb[NLD];
   issue(ts.get(j0), ka, va);
   int j = j0;

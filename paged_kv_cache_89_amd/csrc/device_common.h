@@ -95,6 +95,68 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
   return sign | (uint32_t)m;
 }
 
+// Eight fp16/bf16 source elements (16 bytes) of a new K or V row -> their eight e4m3 cache
+// codes (8 bytes): e4m3(float(x) * inv_scale), the binary32 product rounded to nearest even
+// and saturated.  The one conversion both the KV write and the appending decode use.
+template <int SK>
+__device__ __forceinline__ u32x2 src8_to_e4m3(u32x4 x, float inv_scale) {
+  u32x2 o;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    uint32_t b = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t xw = x[2 * w + e / 2];
+      const float f = (SK == KIND_BF16) ? ((e & 1) ? bf16_hi(xw) : bf16_lo(xw))
+                                        : ((e & 1) ? f16_hi(xw) : f16_lo(xw));
+      b |= f32_to_e4m3_sat(f * inv_scale) << (8 * e);
+    }
+    o[w] = b;
+  }
+  return o;
+}
+
+// Wait until at most N vector-memory operations (loads and stores) of this wave are
+// outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Appending decode: store the new token's K and V rows (row `slot` of block `phys`, KV head
+// kvh) into the cache, as the KV write would: lane x < D * E / 16 stores 16 cache bytes of
+// chunk x, copied from a source of the cache's type or converted to e4m3 (src8_to_e4m3).
+// The caller loads that block afterwards (nothing cached it before: only this unit reads
+// it), so the stores must be done before that load is issued.  vmcnt counts loads and
+// stores together and retires them in order, so once the caller has waited for a load
+// issued after these stores they are done as well; `wait` is for the caller whose load of
+// the block goes out before any such wait (the block is among its first two).
+template <int D, int BS, int QK, int KVK>
+__device__ __forceinline__ void append_new_row(const DecodeArgs& a, int s, int kvh, int phys,
+                                               int slot, int lane, bool wait) {
+  constexpr int E = (KVK == KIND_E4M3) ? 1 : 2;
+  constexpr int CH = D * E / 16;  // 16-byte chunks of a cache row
+  if (lane < CH) {
+    const size_t src = ((size_t)s * a.num_kv_heads + kvh) * D + (size_t)lane * (16 / E);
+    const u32x4* ks = (const u32x4*)((const uint16_t*)a.k_new + src);
+    const u32x4* vs = (const u32x4*)((const uint16_t*)a.v_new + src);
+    u32x4 nk, nv;
+    if constexpr (E == 1) {
+      const u32x2 k0 = src8_to_e4m3<QK>(ks[0], a.k_inv_scale), k1 = src8_to_e4m3<QK>(ks[1], a.k_inv_scale);
+      const u32x2 v0 = src8_to_e4m3<QK>(vs[0], a.v_inv_scale), v1 = src8_to_e4m3<QK>(vs[1], a.v_inv_scale);
+      nk = u32x4{k0[0], k0[1], k1[0], k1[1]};
+      nv = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    } else {
+      nk = ks[0];
+      nv = vs[0];
+    }
+    const size_t dst = (((size_t)phys * a.num_kv_heads + kvh) * BS + slot) * (D * E) + (size_t)lane * 16;
+    *(u32x4*)((char*)a.k + dst) = nk;
+    *(u32x4*)((char*)a.v + dst) = nv;
+  }
+  if (wait) wait_vmcnt<0>();
+}
+
 // A work unit walks at most 64 blocks, so its slice of the block table fits one VGPR:
 // lane k holds entry j0 + k (loaded once, unconditionally, with the index clamped into the
 // unit's range), and the physical id of block j is read with v_readlane into a scalar

@@ -54,6 +54,14 @@ struct DecodeArgs {
   const int32_t* prefix_blocks;  // [num_groups] shared leading blocks of each group
   int32_t query_len;             // MODE_MULTI: query tokens per sequence
   const uint32_t* tree_masks;    // MODE_MULTI: [S, query_len] or null (causal)
+  // Appending decode (MODE_PLAIN only): the new token of sequence s sits at position n - 1
+  // of its (clamped) length n; its K/V rows are k_new / v_new [S, Hkv, D] in the query's
+  // type.  The unit that walks the sequence's last block stores them into the cache
+  // (e4m3 caches: code of x * inv_scale) and uses them in place of what it loaded.
+  int32_t append = 0;
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  float k_inv_scale = 1.f, v_inv_scale = 1.f;
 };
 
 struct DecodeShape {

@@ -17,6 +17,11 @@ int set_validate(int on);  // returns the previous setting
 bool validate_decode(const char* who, const int32_t* tables, const int32_t* ctx, int32_t num_seqs,
                      int32_t max_blocks, int32_t num_blocks, int32_t block_size,
                      int32_t max_context_len, int32_t min_len, void* stream, std::string* err);
+// the block each sequence's new token goes to (entry (n - 1) / block_size, n > 0) is named
+// by no other table entry that the decode reads, of this or another sequence
+bool validate_append_blocks(const char* who, const int32_t* tables, const int32_t* ctx,
+                            int32_t num_seqs, int32_t max_blocks, int32_t num_blocks,
+                            int32_t block_size, void* stream, std::string* err);
 // prefix_blocks[g] in [0, max_prefix_blocks]; the group's shared entries (first member's
 // row) in range; every member's entries inside the prefix equal to the first member's
 bool validate_prefix(const char* who, const int32_t* tables, const int32_t* ctx,

@@ -92,6 +92,39 @@ bool validate_decode(const char* who, const int32_t* tables, const int32_t* ctx,
   return true;
 }
 
+bool validate_append_blocks(const char* who, const int32_t* tables, const int32_t* ctx,
+                            int32_t num_seqs, int32_t max_blocks, int32_t num_blocks,
+                            int32_t block_size, void* stream, std::string* err) {
+  std::vector<int32_t> n, t;
+  if (!fetch_i32(ctx, (size_t)num_seqs, stream, &n, "context_lens", err)) return false;
+  if (!fetch_i32(tables, (size_t)num_seqs * max_blocks, stream, &t, "block_tables", err)) return false;
+  // every read of a block: how many entries name it, and the first two of them
+  std::vector<int32_t> refs((size_t)num_blocks, 0);
+  std::vector<int64_t> first((size_t)num_blocks, -1), second((size_t)num_blocks, -1);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t nb = ((int64_t)n[s] + block_size - 1) / block_size;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t id = t[(size_t)s * max_blocks + j];
+      if (id < 0 || id >= num_blocks) continue;  // reported by validate_decode
+      const int64_t at = (int64_t)s * max_blocks + j;
+      if (refs[id]++ == 0) first[id] = at; else if (second[id] < 0) second[id] = at;
+    }
+  }
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (n[s] <= 0) continue;
+    const int64_t j = ((int64_t)n[s] - 1) / block_size;
+    const int32_t id = t[(size_t)s * max_blocks + j];
+    if (id < 0 || id >= num_blocks || refs[id] == 1) continue;
+    const int64_t other = first[id] == (int64_t)s * max_blocks + j ? second[id] : first[id];
+    return *err = std::string(who) + ": the new token of sequence " + std::to_string(s) +
+                  " goes to block " + std::to_string(id) + " (" + at2("block_tables", s, j) +
+                  "), which " + at2("block_tables", other / max_blocks, other % max_blocks) +
+                  " also reads (a race)",
+           false;
+  }
+  return true;
+}
+
 bool validate_prefix(const char* who, const int32_t* tables, const int32_t* ctx,
                      const int32_t* prefix_blocks, int32_t num_seqs, int32_t seq_group,
                      int32_t max_blocks, int32_t num_blocks, int32_t block_size,

@@ -35,27 +35,8 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteArgs a) {
     *(u32x4*)((uint16_t*)a.v_cache + dst) = vx;
   } else {
     static_assert(CK == KIND_E4M3, "fp16/bf16 sources go to a same-type or e4m3 cache");
-    u32x2 ko, vo;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      uint32_t kb = 0, vb = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t kw = kx[2 * w + e / 2], vw = vx[2 * w + e / 2];
-        float kf, vf;
-        if constexpr (SK == KIND_BF16) {
-          kf = (e & 1) ? bf16_hi(kw) : bf16_lo(kw);
-          vf = (e & 1) ? bf16_hi(vw) : bf16_lo(vw);
-        } else {
-          kf = (e & 1) ? f16_hi(kw) : f16_lo(kw);
-          vf = (e & 1) ? f16_hi(vw) : f16_lo(vw);
-        }
-        kb |= f32_to_e4m3_sat(kf * a.k_inv_scale) << (8 * e);
-        vb |= f32_to_e4m3_sat(vf * a.v_inv_scale) << (8 * e);
-      }
-      ko[w] = kb;
-      vo[w] = vb;
-    }
+    const u32x2 ko = src8_to_e4m3<SK>(kx, a.k_inv_scale);
+    const u32x2 vo = src8_to_e4m3<SK>(vx, a.v_inv_scale);
     *(u32x2*)((uint8_t*)a.k_cache + dst) = ko;
     *(u32x2*)((uint8_t*)a.v_cache + dst) = vo;
   }

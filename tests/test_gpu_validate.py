@@ -213,3 +213,43 @@ def test_block_copies_reject_bad_pairs(validating):
     assert torch.equal(hk[3], k[3].cpu()) and torch.equal(hk[0], k[4].cpu())
     bad = torch.tensor([[3, 8]], dtype=torch.int32, device="cuda")
     _rejects(lambda: pa.swap_blocks(k, v, hk, hv, bad), "pair 0", "destination outside [0, 8)")
+
+
+def test_append_needs_its_block_to_itself(validating):
+    """pa_decode_append: valid tables give the unchecked result; a new token's block named
+    by another sequence's entry, or by a second entry of its own sequence, is a race."""
+    case, tables, q, kd, vd = _decode_inputs()
+    sp = case.spec
+    n = case.context_lens
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8900 + 44)
+    kn = torch.randn((sp.num_seqs, sp.num_kv_heads, sp.head_dim), generator=g, device="cuda").to(q.dtype)
+    vn = torch.randn((sp.num_seqs, sp.num_kv_heads, sp.head_dim), generator=g, device="cuda").to(q.dtype)
+
+    def run(t, k, v):
+        out = torch.full_like(q, 7.0)
+        pa.decode_append(q, kn, vn, k, v, dev_i32(t), dev_i32(n), int(n.max()), sp.scale,
+                         case.k_scale, case.v_scale, 1.0, 1.0, partition_size=sp.partition_size,
+                         out=out)
+        torch.cuda.synchronize()
+        return out
+
+    k1, v1 = kd.clone(), vd.clone()
+    checked = run(tables, k1, v1)
+    pa.set_validate(False)
+    k2, v2 = kd.clone(), vd.clone()
+    assert torch.equal(checked, run(tables, k2, v2))
+    # unused blocks hold NaN: compare the bits
+    assert np.array_equal(to_bits(k1), to_bits(k2)) and np.array_equal(to_bits(v1), to_bits(v2))
+    pa.set_validate(True)
+    s, o = [int(i) for i in np.argsort(n)[-2:]]          # two sequences with several blocks
+    last = (int(n[s]) - 1) // sp.block_size
+    t = tables.copy()
+    t[o, 0] = t[s, last]                                 # another sequence reads that block
+    k3 = kd.clone()
+    _rejects(lambda: run(t, k3, vd.clone()), f"sequence {s}", f"block_tables[{s}][{last}]",
+             f"block_tables[{o}][0]", "a race")
+    assert np.array_equal(to_bits(k3), to_bits(kd)), "a rejected call must launch nothing"
+    t = tables.copy()
+    t[s, 0] = t[s, last]                                 # its own earlier entry
+    _rejects(lambda: run(t, kd.clone(), vd.clone()), f"sequence {s}", f"block_tables[{s}][0]")
