@@ -373,7 +373,7 @@ def test_pools_beyond_4_gib(kv, q, G):
     small = np.full((S, MB), -1, np.int32)
     nxt = 0
     for s_, n in enumerate(lens):
-        nb = -(-int(n) // B)
+        nb = -(-int(n + 1) // B)                      # room for one appended token
         small[s_, :nb] = np.arange(nxt, nxt + nb)
         nxt += nb
     spare = used - 1                                  # destination of the block copy
@@ -423,6 +423,25 @@ def test_pools_beyond_4_gib(kv, q, G):
                             sp.scale, scale, scale)
         atol, rrel = (2e-2, None) if kv == "e4m3" else (2e-3, 1e-2)
         compare(_f64(out), ref, atol, rrel, q)
+        # the appending decode stores above 2^32 too: one more token per sequence, equal
+        # bit for bit to the KV write of that token followed by the decode
+        grown = lens + 1
+        kn, vn = (to_dev(workloads._round_bits(rng.standard_normal((S, Hkv, d), dtype=np.float32),
+                                               q), q) for _ in range(2))
+        saved = (kd[base:].clone(), vd[base:].clone())
+        pa.write_kv(kn, vn, kd, vd, dev_i32(big), dev_i32(np.arange(S, dtype=np.int32)),
+                    dev_i32(lens), inv, inv)
+        want = pa.decode(qd, kd, vd, dev_i32(big), dev_i32(grown), int(grown.max()), sp.scale,
+                         scale, scale, partition_size=64)
+        torch.cuda.synchronize()
+        want_pools = (to_bits(kd[base:]), to_bits(vd[base:]))
+        kd[base:], vd[base:] = saved
+        got = pa.decode_append(qd, kn, vn, kd, vd, dev_i32(big), dev_i32(grown), int(grown.max()),
+                               sp.scale, scale, scale, inv, inv, partition_size=64)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)
+        assert np.array_equal(to_bits(kd[base:]), want_pools[0])
+        assert np.array_equal(to_bits(vd[base:]), want_pools[1])
     finally:
         del kd, vd
         torch.cuda.empty_cache()
