@@ -349,6 +349,9 @@ pa_status pa_decode_append(void* out, const void* query, const void* k_new, cons
  *                  shared (e.g. between beams): the per-sequence launch then keeps its K/V
  *                  loads cacheable.  The prefix launch always streams (it reads each shared
  *                  block once).  Results are identical either way.
+ *   partition_size 0 = library choice: prefix partitions of a planned size, and each
+ *                  row's own blocks split into equal shares (at least 8 blocks each);
+ *                  else a positive multiple of block_size used by both launches
  *   workspace      at least pa_decode_shared_prefix_workspace_size(...) bytes (never 0
  *                  for num_seqs > 0: the two launches always leave partials)
  * Supported: what the matrix-core decode covers for the group's queries: block_size 16,

@@ -61,6 +61,8 @@ struct Plan {
 // block-aligned prompts evenly (768 measured 4 % slower there).
 constexpr int32_t kAutoPartition = 768;
 constexpr int32_t kCascadePartition = 512;
+// Shortest share of a row's own blocks in the shared-prefix decode's per-sequence launch.
+constexpr int32_t kSuffixMinBlocks = 8;
 
 // Long contexts (the bound spans at least 16 base partitions): the partial last partition
 // of a sequence is a small share of its work, so partitions take the 64-block maximum while
@@ -120,6 +122,7 @@ size_t workspace_bytes(const Plan& p, int32_t num_seqs, int32_t num_heads, int32
 // suf_parts.  Both counts come from host bounds, so some slots stay empty.
 struct CascadePlan {
   int32_t partition_size, pre_parts, suf_parts;
+  int32_t suf_min_blocks;  // > 0: the per-sequence launch splits each row's blocks evenly
 };
 
 pa_status make_cascade_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -142,6 +145,21 @@ pa_status make_cascade_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_
   cp->partition_size = (int32_t)P;
   cp->pre_parts = (int32_t)((pre_tokens + P - 1) / P);
   cp->suf_parts = (int32_t)std::max<int64_t>(1, (max_context_len + P - 1) / P);
+  cp->suf_min_blocks = 0;
+  if (partition_size == 0) {
+    // Library choice: the per-sequence tokens are what remains after the shared prefix,
+    // anything from none to the whole context, so fixed partitions sized for the whole
+    // context leave many per-sequence units short or empty.  Each row's own blocks are
+    // split instead into suf_parts equal shares of at least kSuffixMinBlocks blocks: two
+    // shares, or more where a share would exceed two partitions (64 blocks at most).
+    // Measured on the fp8 shared-prompt workload (own tokens U[0, 512]): 2 % faster than
+    // 512-token partitions, 1 % faster than three shares.
+    const int64_t max_blk = ((int64_t)std::max(max_context_len, 1) + block_size - 1) / block_size;
+    const int64_t cap = std::min<int64_t>(kMaxUnitBlocks, 2 * (P / block_size));
+    const int64_t split = std::min<int64_t>(2, (max_blk + kSuffixMinBlocks - 1) / kSuffixMinBlocks);
+    cp->suf_parts = (int32_t)std::max<int64_t>(split, (max_blk + cap - 1) / cap);
+    cp->suf_min_blocks = kSuffixMinBlocks;
+  }
   return PA_OK;
 }
 
@@ -569,6 +587,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
   // The remaining tokens are mostly private: neighbouring units take neighbouring heads of
   // the same blocks (contiguous lines); PA_DECODE_SHARED_KV only keeps the loads cacheable.
   a.mode = MODE_SUFFIX; a.slot_base = cp.pre_parts; a.num_parts = cp.suf_parts;
+  a.part_min_blocks = cp.suf_min_blocks;
   a.num_units = (int32_t)suf_units; a.seq_fastest = 0;
   st = hip_status(launch_decode(suf_shape, a, (hipStream_t)stream),
                   "pa_decode_shared_prefix suffix launch");

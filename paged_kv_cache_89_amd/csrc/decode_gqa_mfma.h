@@ -301,8 +301,9 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     table_row = a.tables + (size_t)s * a.max_blocks;
   }
   const int nblk = (n + BS - 1) / BS;
-  const int j0 = jb + part * a.blocks_per_part;
-  const int j1 = min(nblk, j0 + a.blocks_per_part);
+  const int bpp = part_share_blocks(a, jb, nblk);
+  const int j0 = jb + part * bpp;
+  const int j1 = min(nblk, j0 + bpp);
 
   if (j0 >= j1) {
     if (a.num_slots == 0) {  // direct output of an n == 0 sequence: zero rows

@@ -89,8 +89,9 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
   // suffix of a shared-prefix group: start after the blocks the prefix units cover
   const int jb = (a.mode == MODE_SUFFIX)
                      ? (prefix_tokens(a, s / a.seq_group, BS, n) + BS - 1) / BS : 0;
-  const int j0 = jb + part * a.blocks_per_part;
-  const int j1 = min(nblk, j0 + a.blocks_per_part);
+  const int bpp = part_share_blocks(a, jb, nblk);
+  const int j0 = jb + part * bpp;
+  const int j1 = min(nblk, j0 + bpp);
   const int r = lane / LPT;   // token row of this lane inside a load
   const int c = lane % LPT;   // element slice [c*EPL, c*EPL + EPL) of the head dimension
 

@@ -215,6 +215,14 @@ __device__ __forceinline__ UnitCoords unit_coords(const DecodeArgs& a, int waves
   return u;
 }
 
+// Blocks per unit of a row whose units walk blocks [jb, nblk): the fixed partition, or
+// under a balanced split an equal share of them, at least part_min_blocks.
+__device__ __forceinline__ int part_share_blocks(const DecodeArgs& a, int jb, int nblk) {
+  if (a.part_min_blocks <= 0) return a.blocks_per_part;
+  const int share = (nblk - jb + a.num_parts - 1) / a.num_parts;
+  return share > a.part_min_blocks ? share : a.part_min_blocks;
+}
+
 // Tokens of its group's shared prefix that a sequence of length n attends (cascade modes):
 // the group's shared blocks, clamped to [0, max_prefix_blocks], in tokens, capped at n.
 __device__ __forceinline__ int prefix_tokens(const DecodeArgs& a, int group, int block_size, int n) {

@@ -44,6 +44,10 @@ struct DecodeArgs {
   float* part_ml;            // [S, Hq, num_slots, 2]   running max (log2 units) and sum
   int32_t num_seqs, num_heads, num_kv_heads, max_blocks, num_blocks, max_ctx;
   int32_t num_parts, blocks_per_part, num_units;
+  // > 0: balanced split instead -- each of the num_parts units of a row takes an equal
+  // share of the row's blocks [jb, ceil(n / B)), at least part_min_blocks of them
+  // (part_share_blocks); the host keeps num_parts * 64 >= ceil(max_ctx / B)
+  int32_t part_min_blocks = 0;
   int32_t num_slots, slot_base;  // partial slots per row (0: write the output directly)
   float qk_scale;            // scale * log2(e) * k_scale
   float v_scale;

@@ -97,6 +97,28 @@ def test_shared_prefix_matches_oracle_all_variants(d, dt):
                 compare(out, ref, atol, rrel, qd)
 
 
+@pytest.mark.parametrize("dt", [("bf16", "bf16"), ("bf16", "e4m3")])
+@pytest.mark.parametrize("G", [1, 2])
+def test_per_sequence_shares(dt, G):
+    """With the library's partition choice each row's own blocks are split into equal
+    shares: rows with no own tokens, with less than one minimum share, and with own
+    contexts long enough for a dozen shares (few sequences: the planner's partition drops
+    to 128 tokens, so a share holds at most 16 blocks).  Oracle parity for the library
+    choice and for explicit 512-token partitions."""
+    qd, kvd = dt
+    B, K, prompt = 16, 2, 64
+    lens = [64, 65, 64 + 8 * B, 64 + 8 * B + 1, 300, 2200, 3000, 1000]
+    case, tables, k, v = _shared_case(G, K, 128, B, qd, kvd, lens, prompt, 91 + G)
+    ref = oracle_decode(case, tables, k, v)
+    atol, rrel = tolerance(case.spec)
+    pbs = np.full(len(lens) // K, prompt // B, np.int32)
+    for P in (0, 512):
+        for flags in (0, pa.DECODE_SHARED_KV):
+            out = _f64(_cascade(case, tables, k, v, pbs, prompt // B, partition_size=P,
+                                flags=flags))
+            compare(out, ref, atol, rrel, qd)
+
+
 def test_prefix_bound_clamps_and_equals_plain_decode():
     """prefix_blocks above max_prefix_blocks are clamped to it; any valid split gives the
     plain decode's result up to rounding, and the cascade output is deterministic."""

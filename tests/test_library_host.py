@@ -179,10 +179,17 @@ def test_decode_argument_errors_without_gpu():
 def test_shared_prefix_workspace_and_errors_without_gpu():
     # fp8 shared-prompt shape: 256 seqs, 32 heads, d 128, B 16, max context 1536, prompts
     # of 64 blocks.  The shared-prefix decode splits by 512 tokens (its prompts are block
-    # aligned; pa_decode alone would take 768): 2 prefix slots + 3 per-sequence slots.
+    # aligned; pa_decode alone would take 768): 2 prefix slots, and each row's own blocks
+    # in 2 equal shares (no share above two 32-block partitions: 96 blocks fit).
     assert pa.decode_plan(256, 32, 32, 128, 16, 1536, 0) == (768, 2)
     ws = pa.decode_shared_prefix_workspace_size(256, 32, 32, 128, 16, 1536, 64)
+    assert ws == 256 * 32 * (2 + 2) * 130 * 4
+    # an explicit partition size applies to both launches: 1536 / 512 = 3 per-sequence slots
+    ws = pa.decode_shared_prefix_workspace_size(256, 32, 32, 128, 16, 1536, 64, 512)
     assert ws == 256 * 32 * (2 + 3) * 130 * 4
+    # own blocks beyond two partitions: 4096 tokens = 256 blocks -> shares of at most 64
+    ws = pa.decode_shared_prefix_workspace_size(256, 32, 32, 128, 16, 4096, 64)
+    assert ws == 256 * 32 * (2 + 4) * 130 * 4
     # unsplit choice: the whole context (rounded to B) is one slot on each side
     assert pa.decode_shared_prefix_workspace_size(4, 8, 8, 64, 16, 100, 2) == 4 * 8 * 2 * 66 * 4
     # no prefix bound: per-sequence slots only
