@@ -274,8 +274,9 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void
  *                 then stay cacheable and sequences are visited together so that a shared
  *                 block is fetched from HBM once; without it K/V loads are streamed with
  *                 the non-temporal hint.  Results are identical either way.
- *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes
- *                 (may be NULL when that size is 0)
+ *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes, 16-byte
+ *                 aligned (hipMalloc gives 256); may be NULL when that size is 0.  The
+ *                 same holds for every workspace argument below.
  * Supported: head_dim in {64, 128}; block_size in {8, 16, 32}; num_heads / num_kv_heads in
  * {1, 2, 4, 8}; (q, kv) in {(f16, f16), (bf16, bf16), (f16, e4m3), (bf16, e4m3)}. */
 #define PA_DECODE_SHARED_KV 1u

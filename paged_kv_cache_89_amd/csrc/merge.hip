@@ -13,7 +13,21 @@
 
 namespace pa {
 
-template <int D, int QK>
+// Wave-wide max / sum (every lane gets the result).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v = fmaxf(v, __shfl_xor(v, k));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
+  return v;
+}
+
+// PF: partial outputs loaded per batch; the first batch goes out with the row's length and
+// its (m, l) pairs, so a row of at most PF slots costs one round trip to memory.
+template <int D, int QK, int PF>
 __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a) {
   constexpr int EPL = D / 64;
   const int lane = threadIdx.x & 63;
@@ -21,14 +35,32 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a
   const int row = blockIdx.x * 4 + wave;  // s * Hq + h
   if (row >= a.num_seqs * a.num_heads) return;
   const int s = row / a.num_heads;
-  int n = a.ctx[s];
-  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  const int np = a.all_slots ? (n > 0 ? a.num_parts : 0) : (n + a.partition_size - 1) / a.partition_size;
+  const int P = a.num_parts;
   uint16_t* o = (uint16_t*)a.out + (size_t)row * D + lane * EPL;
-  const float* ml = a.part_ml + (size_t)row * a.num_parts * 2;
-  const float* pacc = a.part_acc + (size_t)row * a.num_parts * D + lane * EPL;
+  const float2* ml = (const float2*)(a.part_ml + (size_t)row * P * 2);
+  const float* pacc = a.part_acc + (size_t)row * P * D + lane * EPL;
+
+  // Loads that do not depend on the length: slot `lane`'s (m, l) and the first PF slots'
+  // outputs (indices clamped into the row's slots).  Slots at or past the row's own count
+  // hold stale data; they are masked below and never enter the arithmetic.
+  int n = a.ctx[s];
+  const float2 ml0 = ml[min(lane, P - 1)];
+  float x[PF][EPL];
+#pragma unroll
+  for (int k = 0; k < PF; ++k)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[k][e] = pacc[(size_t)min(k, P - 1) * D + e];
+
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  const int np = a.all_slots ? (n > 0 ? P : 0) : (n + a.partition_size - 1) / a.partition_size;
+
+  // M = max over the row's slots (64 per pass; empty cascade slots carry m = -inf)
   float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  for (int base = 0; base < np; base += 64) {
+    const int p = base + lane;
+    const float m = base == 0 ? ml0.x : (p < P ? ml[p].x : -INFINITY);
+    M = fmaxf(M, wave_max(p < np ? m : -INFINITY));
+  }
   if (M == -INFINITY) {  // n == 0: no token, zero row
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = 0;
@@ -37,32 +69,62 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a
   float L = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int p = 0; p < np; ++p) {
-    const float mp = ml[2 * p];
-    if (a.all_slots && mp == -INFINITY) continue;  // empty slot (wave-uniform)
-    const float w = fast_exp2(mp - M);
-    L = fmaf(w, ml[2 * p + 1], L);
+  for (int base = 0; base < np; base += 64) {
+    const int p = base + lane;
+    const float2 v = base == 0 ? ml0 : (p < P ? ml[p] : make_float2(-INFINITY, 0.f));
+    const bool live = p < np && v.x != -INFINITY;
+    const float w = live ? fast_exp2(v.x - M) : 0.f;  // this lane's slot weight
+    L += wave_sum(live ? w * v.y : 0.f);
+    const int cnt = min(64, np - base);
+    int q = 0;
+    if (base == 0) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, pacc[(size_t)p * D + e], acc[e]);
+      for (int k = 0; k < PF; ++k) {
+        if (k < cnt) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wk, wk != 0.f ? x[k][e] : 0.f, acc[e]);
+        }
+      }
+      q = PF;
+    }
+    for (; q < cnt; q += PF) {  // further slots, PF loads in flight at a time
+      float y[PF][EPL];
+#pragma unroll
+      for (int k = 0; k < PF; ++k)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) y[k][e] = pacc[(size_t)min(base + q + k, P - 1) * D + e];
+#pragma unroll
+      for (int k = 0; k < PF; ++k) {
+        if (q + k < cnt) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), q + k));
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wk, wk != 0.f ? y[k][e] : 0.f, acc[e]);
+        }
+      }
+    }
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = f32_to_store<QK>(acc[e] / L * a.v_scale);
 }
 
+template <int D, int QK>
+hipError_t launch_merge_pf(const MergeArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.num_parts <= 4)
+    hipLaunchKernelGGL((merge_partitions_kernel<D, QK, 4>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((merge_partitions_kernel<D, QK, 16>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_merge(int head_dim, int q_kind, const MergeArgs& a, hipStream_t stream) {
   const dim3 grid((a.num_seqs * a.num_heads + 3) / 4);
-  if (head_dim == 128 && q_kind == KIND_F16)
-    hipLaunchKernelGGL((merge_partitions_kernel<128, KIND_F16>), grid, dim3(256), 0, stream, a);
-  else if (head_dim == 128 && q_kind == KIND_BF16)
-    hipLaunchKernelGGL((merge_partitions_kernel<128, KIND_BF16>), grid, dim3(256), 0, stream, a);
-  else if (head_dim == 64 && q_kind == KIND_F16)
-    hipLaunchKernelGGL((merge_partitions_kernel<64, KIND_F16>), grid, dim3(256), 0, stream, a);
-  else if (head_dim == 64 && q_kind == KIND_BF16)
-    hipLaunchKernelGGL((merge_partitions_kernel<64, KIND_BF16>), grid, dim3(256), 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (a.num_parts < 1) return hipErrorInvalidValue;
+  if (head_dim == 128 && q_kind == KIND_F16) return launch_merge_pf<128, KIND_F16>(a, grid, stream);
+  if (head_dim == 128 && q_kind == KIND_BF16) return launch_merge_pf<128, KIND_BF16>(a, grid, stream);
+  if (head_dim == 64 && q_kind == KIND_F16) return launch_merge_pf<64, KIND_F16>(a, grid, stream);
+  if (head_dim == 64 && q_kind == KIND_BF16) return launch_merge_pf<64, KIND_BF16>(a, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -168,6 +168,12 @@ def test_decode_argument_errors_without_gpu():
     st = L.pa_decode(None, None, None, None, None, None, 1, 8, 8, 128, 16, 4, 4, 64, 0.1,
                      0, 0, 1.0, 1.0, 0, 6, None, 0, None)
     assert st == -1 and b"flag" in L.pa_last_error()
+    # a split plan's workspace must be 16-byte aligned (checked before anything is read)
+    fake = 0x10000
+    assert pa.decode_plan(1, 8, 8, 128, 16, 2048, 0)[1] > 1
+    st = L.pa_decode(fake, fake, fake, fake, fake, fake, 1, 8, 8, 128, 16, 128, 128, 2048, 0.1,
+                     0, 0, 1.0, 1.0, 0, 0, fake + 8, 1 << 30, None)
+    assert st == -1 and b"16-byte aligned" in L.pa_last_error()
     st = L.pa_write_kv(None, None, None, None, None, 1, 4, None, None, 1, 4, 8, 128, 12,
                        0, 0, 1.0, 1.0, None)
     assert st == -2
