@@ -16,7 +16,7 @@ import torch
 
 import paged_kv_cache_89_amd as pa
 import workloads
-from helpers import dev_i32, oracle_caches, oracle_tables, to_dev
+from helpers import dev_i32, oracle_caches, oracle_tables, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +78,57 @@ def test_write_and_decode_step_replays(name, P):
                   partition_size=P, out=out, workspace=ws)
 
     _replays_match_eager(step, [out])
+
+
+def test_appending_decode_replays():
+    """pa_decode_append in a graph: each replay stores the same new rows and gives the
+    eager output and pools."""
+    case = workloads.generate(workloads.SMALL["gqa_llama"], 8900 + 52)
+    sp = case.spec
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    q, kd, vd = to_dev(case.q, sp.q_dtype), to_dev(k, sp.kv_dtype), to_dev(v, sp.kv_dtype)
+    td, cd = dev_i32(tables), dev_i32(case.context_lens)
+    mc = int(case.context_lens.max())
+    S, Hq, D = q.shape
+    NB, Hkv, B, _ = kd.shape
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8900 + 53)
+    kn = torch.randn((S, Hkv, D), generator=g, device="cuda").to(q.dtype)
+    vn = torch.randn((S, Hkv, D), generator=g, device="cuda").to(q.dtype)
+    P = B
+    assert pa.decode_plan(S, Hq, Hkv, D, B, mc, P)[1] > 1
+    ws = torch.empty(pa.decode_workspace_size(S, Hq, Hkv, D, B, mc, P), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(q)
+
+    def step():
+        pa.decode_append(q, kn, vn, kd, vd, td, cd, mc, sp.scale, case.k_scale, case.v_scale,
+                         1.0, 1.0, partition_size=P, out=out, workspace=ws)
+
+    k0, v0 = kd.clone(), vd.clone()
+    step()
+    torch.cuda.synchronize()
+    ref = (out.clone(), to_bits(kd), to_bits(vd))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for i in range(4):
+        out.fill_(float(i + 3))        # eager work between replays; the pools go back to
+        kd.copy_(k0)                   # their state before the new rows, so each replay
+        vd.copy_(v0)                   # must store them again
+        torch.randn(1 << 20, device="cuda").sum().item()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]), f"replay {i} differs from the eager result"
+        assert np.array_equal(to_bits(kd), ref[1]) and np.array_equal(to_bits(vd), ref[2])
 
 
 def test_shared_prefix_and_multi_token_replay():

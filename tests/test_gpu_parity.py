@@ -293,6 +293,26 @@ def test_load_policy_flag_gives_identical_results(name):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("qd", ["f16", "bf16"])
+@pytest.mark.parametrize("G", [1, 4])
+def test_merge_of_many_partitions(qd, G):
+    """One-block partitions over long rows: up to 200 partials per row, so the merge walks
+    several 64-slot chunks and a ragged last one; rows of 0 and 1 partials beside them."""
+    B = 16
+    lens = [3200, 1100, 17, 0, 2049, 1024, 16]
+    sp = workloads.Spec("many", len(lens), 2 * G, 2, 128, B, 1, 1,
+                        sum(math.ceil(n / B) for n in lens) + 5, math.ceil(max(lens) / B) + 1,
+                        qd, qd, 1 / math.sqrt(128))
+    case = workloads.generate(sp, 8900 + 26 + G, context_lens=lens)
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    ref = oracle_decode(case, tables, k, v)
+    assert pa.decode_plan(sp.num_seqs, sp.num_heads, sp.num_kv_heads, 128, B, max(lens), B)[1] == 200
+    out = _f64(_gpu_decode(case, tables, k, v, partition_size=B))
+    assert (out[3] == 0).all()
+    compare(out, ref, *tolerance(sp), qd)
+
+
 def test_partition_size_invariance_and_determinism():
     case = workloads.generate(workloads.SMALL["long_split"], 8900 + 24)
     sp = case.spec
