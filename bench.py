@@ -102,9 +102,11 @@ def main():
     import paged_kv_cache_89_amd as pa
     import workloads
 
-    torch.cuda.set_device(0)
     names = list(workloads.SPECS)
     sp = workloads.SPECS[args.workload]
+    if args.step == "fused" and (sp.group_size or args.decode_path not in ("auto", "plain")):
+        raise SystemExit("--step fused needs the plain decode path and no shared blocks")
+    torch.cuda.set_device(0)
     seed = 8900 + names.index(args.workload)
     P = sp.partition_size if args.partition_size < 0 else args.partition_size
 
@@ -204,9 +206,7 @@ def main():
     # (pa_decode_append stores each sequence's new row from the unit that reads its block;
     # a new token must not land in a block another sequence reads).  The two launches are
     # the default: the fused call measured about 0.4% slower per step on the OPT-13B layer.
-    fused = args.step == "fused"
-    if fused and (path != "plain" or sp.group_size):
-        raise SystemExit("--step fused needs the plain decode path and no shared blocks")
+    fused = args.step == "fused"  # (its preconditions were checked before any GPU work)
     if fused:
         kernels = kernels.replace("paged_decode_kernel", "paged_decode_kernel (storing the new token)", 1) \
             .replace("paged_decode_gqa_mfma_kernel", "paged_decode_gqa_mfma_kernel (storing the new token)", 1)
