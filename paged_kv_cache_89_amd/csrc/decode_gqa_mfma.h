@@ -607,15 +607,10 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     }
   };
 
-  // Pipeline: the K and V loads of block j+1 are issued before block j is consumed (two
-  // register sets each, as in the vector kernel); consuming block j moves V(j) into the
-  // LDS tile, runs the logit contraction on K(j), the softmax update and P . V.  The mask
-  // of slots >= n is applied branch-free (it only bites in a unit's last block).
-  auto process = [&](int j, const u32x4 (&kr)[NLDS], const u32x4 (&vr)[NLDS]) {
-    stage(kt, kw_off, false, j, kr);
-    stage(vt, vw_off, true, j, vr);
-    finish(j, logits());
-  };
+  // Pipeline (register path): two register sets of K and V tiles, as in the vector kernel;
+  // consuming block j moves K(j) and V(j) into the LDS tiles, runs the logit contraction,
+  // the softmax update and P . V.  The mask of slots >= n is applied branch-free (it only
+  // bites in a unit's last block).
   if constexpr (DMA) {
     constexpr int PER = 2 * NLDS;  // vector-memory operations per block
     int st = 0;
@@ -638,21 +633,36 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
       st ^= 1;
     }
   } else {
-    // steady state: every load in the loop is unconditional (see the vector kernel)
+    // A block's registers are free once it sits in LDS, so the block two ahead is fetched
+    // into them before the block's contractions run: two blocks stay in flight while one
+    // is consumed.  Steady state: blocks j .. j+3 exist, ka/va hold block j and kb/vb
+    // block j + 1, and every load in the loop is unconditional (see the vector kernel).
+    auto stage_kv = [&](int j, const u32x4 (&kr)[NLDS], const u32x4 (&vr)[NLDS]) {
+      stage(kt, kw_off, false, j, kr);
+      stage(vt, vw_off, true, j, vr);
+    };
     int j = j0;
-    while (j + 2 < j1) {
-      fetch(j + 1, kb, vb);
-      process(j, ka, va);
+    if (j + 1 < j1) fetch(j + 1, kb, vb);
+    while (j + 3 < j1) {
+      stage_kv(j, ka, va);
       fetch(j + 2, ka, va);
-      process(j + 1, kb, vb);
+      finish(j, logits());
+      stage_kv(j + 1, kb, vb);
+      fetch(j + 3, kb, vb);
+      finish(j + 1, logits());
       j += 2;
     }
+    // one to three blocks left: ka/va hold block j, kb/vb block j + 1 when it exists
+    stage_kv(j, ka, va);
+    if (j + 2 < j1) fetch(j + 2, ka, va);
+    finish(j, logits());
     if (j + 1 < j1) {
-      fetch(j + 1, kb, vb);
-      process(j, ka, va);
-      process(j + 1, kb, vb);
-    } else {
-      process(j, ka, va);
+      stage_kv(j + 1, kb, vb);
+      finish(j + 1, logits());
+    }
+    if (j + 2 < j1) {
+      stage_kv(j + 2, ka, va);
+      finish(j + 2, logits());
     }
   }
 
