@@ -59,7 +59,7 @@ def measured_traffic(workload: str, decode_path: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="opt13b_layer")
     ap.add_argument("--partition-size", type=int, default=-1,
