@@ -177,21 +177,15 @@ __device__ __forceinline__ float rows_sum(float x) {
 #endif
 
 // One 16-byte-per-lane load from global memory into LDS: lane l's 16 bytes land at LDS
-// byte lds + 16 l (the wave fills 1 KiB).  The LDS address travels in M0, which nothing
-// else in these kernels uses.  vmcnt drops once the bytes are in LDS (wait_vmcnt).  The
-// stage being refilled was read by the block before: lgkmcnt(0) first, so those reads have
-// returned before the new bytes can land.
+// byte lds + 16 l (the wave fills 1 KiB).  The compiler's builtin places the (wave-uniform)
+// LDS address in M0 itself.  vmcnt drops once the bytes are in LDS (wait_vmcnt).  The stage
+// being refilled was read by the block before: lgkmcnt(0) first, so those reads have
+// returned before the new bytes can land.  Cache policy 2 is the non-temporal hint.
+typedef __attribute__((address_space(3))) void lds_void;
 template <bool NT>
-__device__ __forceinline__ void load_lds_x4(const void* src, uint32_t lds) {
-  if constexpr (NT)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :: "v"(src), "s"(lds) : "memory");
-  else
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(lds) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+__device__ __forceinline__ void load_lds_x4(const void* src, uint8_t* lds) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, NT ? 2 : 0);
 }
 
 // Waves per SIMD the register allocation must allow.  e4m3 blocks carry half the bytes of
@@ -380,12 +374,12 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   }
   auto issue = [&](int jj, int st) {
     const size_t boff = (size_t)ts.get(jj) * blk_stride;
-    const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][st][0]));
-    const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][st][1]));
 #pragma unroll
-    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(kbase + boff + goffk[i], kl + 1024 * i);
+    for (int i = 0; i < NLDS; ++i)
+      load_lds_x4<NT>(kbase + boff + goffk[i], lds_buf[wave][st][0] + 1024 * i);
 #pragma unroll
-    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(vbase + boff + goffv[i], vl + 1024 * i);
+    for (int i = 0; i < NLDS; ++i)
+      load_lds_x4<NT>(vbase + boff + goffv[i], lds_buf[wave][st][1] + 1024 * i);
   };
   if constexpr (DMA) issue(j0, 0);
   else fetch(j0, ka, va);
@@ -581,21 +575,15 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     const uint32_t p01 = Ops::pack2(p[0], p[1], &rp[0], &rp[1]);
     const uint32_t p23 = Ops::pack2(p[2], p[3], &rp[2], &rp[3]);
     const u32x2 pop = u32x2{p01, p23};
-    // bf16 keeps 8 significant bits: a weight rounded to it can be off by 2^-9 of itself,
-    // which a few dominant tokens with distant values turn into output errors above the
-    // fp16/bf16 bar.  So P goes in as hi + lo (the second MFMA takes the rounding
-    // residual) and the denominator sums the unrounded weights.  fp16 P keeps 11 bits
-    // and goes in once, with the denominator of the rounded weights.
-    constexpr bool SPLIT = QK == KIND_BF16;
-    u32x2 plo = u32x2{0u, 0u};
-    if constexpr (SPLIT) {
-      float unused[4];
-      plo = u32x2{Ops::pack2(p[0] - rp[0], p[1] - rp[1], &unused[0], &unused[1]),
-                  Ops::pack2(p[2] - rp[2], p[3] - rp[3], &unused[2], &unused[3])};
-      l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    } else {
-      l_part += (rp[0] + rp[1]) + (rp[2] + rp[3]);
-    }
+    // A weight rounded to the operand type is off by up to 2^-9 (bf16) or 2^-12 (fp16) of
+    // itself, which a few dominant tokens with distant values turn into output errors of
+    // the order of the 2e-3 bar.  So P goes in as hi + lo (the second MFMA takes the
+    // rounding residual, exact to about 2^-17 / 2^-23) and the denominator sums the
+    // unrounded weights.
+    float unused[4];
+    const u32x2 plo = u32x2{Ops::pack2(p[0] - rp[0], p[1] - rp[1], &unused[0], &unused[1]),
+                            Ops::pack2(p[2] - rp[2], p[3] - rp[3], &unused[2], &unused[3])};
+    l_part += (p[0] + p[1]) + (p[2] + p[3]);
     // P . V over the 16 tokens, one 16-wide slice of the head dimension at a time
 #pragma unroll
     for (int t = 0; t < NTILES; ++t) {
@@ -603,7 +591,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
       const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(vt + trow * PITCH + chunk * 16 + 8 * (c % 2)));
       cacc[t] = Ops::pv(pop, vb, cacc[t]);
-      if constexpr (SPLIT) cacc[t] = Ops::pv(plo, vb, cacc[t]);
+      cacc[t] = Ops::pv(plo, vb, cacc[t]);
     }
   };
 

@@ -55,10 +55,10 @@ def compare(gpu_out_f64: np.ndarray, ref_f64: np.ndarray, atol: float, rtol_row:
             out_dtype: str | None = None):
     """Tolerance gates against the unrounded fp64 oracle.
 
-    Gate 1: |g - r| <= atol + half_ulp_out(r) for every element.  The bar of the operator
-    (2e-3 for fp16/bf16 caches, 2e-2 for e4m3) bounds the error of the kernel's fp32
-    result; the final conversion to the output dtype adds up to half an ulp on top, which
-    for bf16 alone exceeds 2e-3 once |o| > 1.
+    Gate 1: |g - r| <= atol for every element (2e-3 for fp16/bf16 caches, 2e-2 for
+    e4m3), with one allowance: a bf16 output also gets half an ulp of bf16 at |r|, since the
+    final round-to-nearest into bf16 alone moves a result by up to 2^-9 |r|, more than 2e-3
+    once |r| > 1.  fp16 outputs (half an ulp <= 4.9e-4 below |r| = 2) take the bar as is.
     Gate 2: per (s, h) row, ||g - r||_inf / ||r||_inf <= rtol_row.
     Returns (max_abs, max_row_rel)."""
     g = np.asarray(gpu_out_f64, np.float64)
@@ -67,14 +67,15 @@ def compare(gpu_out_f64: np.ndarray, ref_f64: np.ndarray, atol: float, rtol_row:
     assert np.isfinite(g).all(), "non-finite output"
     err = np.abs(g - r)
     max_abs = float(err.max()) if err.size else 0.0
-    bar = atol + half_ulp(r, out_dtype)
+    bar = atol + half_ulp(r, "bf16" if out_dtype == "bf16" else None)
     worst = float((err - bar).max()) if err.size else -1.0
     rn = np.abs(r).max(axis=-1)
     en = err.max(axis=-1)
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.where(rn > 0, en / np.where(rn > 0, rn, 1), en)
     max_rel = float(rel.max()) if rel.size else 0.0
-    assert worst <= 0, f"max abs err {max_abs} exceeds {atol} + half-ulp of {out_dtype}"
+    assert worst <= 0, (f"max abs err {max_abs} exceeds {atol}"
+                        + (" + half an ulp of bf16" if out_dtype == "bf16" else ""))
     if rtol_row is not None:
         assert max_rel <= rtol_row, f"max row rel err {max_rel} > {rtol_row}"
     return max_abs, max_rel

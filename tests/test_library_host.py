@@ -300,9 +300,12 @@ def test_hot_kernels_use_no_scratch():
             spilled[name] = scratch
     assert not spilled, spilled
     # the kernels the five workloads run, with their occupancy-setting register counts
-    # (four waves per SIMD need <= 128 VGPRs, three <= 168)
+    # (four waves per SIMD need <= 128 VGPRs, three <= 168, two <= 256).  The bf16 GQA
+    # register path fetches the block two ahead into the registers a staged block frees
+    # (two blocks in flight while one is consumed): 196 VGPRs, two waves per SIMD, measured
+    # 0.6 % faster per step on the GQA workload than one block ahead at three waves.
     hot = {"_ZN2pa19paged_decode_kernelILi128ELi16ELi0ELi0ELi1ELb1EEEvNS_10DecodeArgsE": 128,
-           "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0EEEvNS_10DecodeArgsE": 168,
+           "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0EEEvNS_10DecodeArgsE": 256,
            # the fp8 shared-prompt prefix units (4 members x 1 head, per-column masks)
            "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi2ELi4ELb1ELb1EEEvNS_10DecodeArgsE": 128}
     for name, vgpr_max in hot.items():
