@@ -301,6 +301,30 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     int32_t partition_size, uint32_t flags, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* No-allocation decode, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Computes exactly
+ * what pa_decode computes, with the same arguments minus the workspace, and launches the
+ * same kernels: the partition partials go to a fixed device array of
+ * PA_NOALLOC_SCRATCH_BYTES bytes inside the library (one copy per GPU, held until the
+ * process ends; its address on the current GPU is looked up on the first call there).  The
+ * call allocates nothing.  A plan whose partials need more than that array
+ * (pa_decode_workspace_size(...) > PA_NOALLOC_SCRATCH_BYTES, e.g. more than about 64,000
+ * (sequence, query head, partition) triples at head_dim 128) returns PA_ERR_UNSUPPORTED
+ * before anything is launched; call pa_decode with a workspace instead.  Every call on a
+ * GPU shares that GPU's array, which keeps whatever the last call left there (nothing in
+ * it needs to start at zero): calls that overlap on one GPU -- on several streams, or from
+ * several host threads -- race on it and must be serialised by the caller.  Errors and
+ * support as for pa_decode. */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+pa_status pa_decode_noalloc(void* out, const void* query, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t max_blocks_per_seq, int32_t num_blocks,
+                            int32_t max_context_len, float scale, pa_dtype q_dtype,
+                            pa_dtype kv_dtype, float k_scale, float v_scale,
+                            int32_t partition_size, uint32_t flags, void* stream);
+
 /* Decode step with the new token written in the same launch: pa_write_kv of one new token
  * per sequence followed by pa_decode ([P1] sec. 4 "Decoding Step": the new token's key and
  * value go to their slot, then every query attends the sequence including it).  The new

@@ -19,12 +19,14 @@ import numpy as np
 
 __all__ = [
     "F16", "BF16", "FP8_E4M3", "DECODE_SHARED_KV", "PagedAttnError", "LibraryNotBuilt", "lib", "library_path",
-    "BlockManager", "write_kv", "copy_blocks", "decode", "decode_plan", "decode_workspace_size",
+    "BlockManager", "write_kv", "copy_blocks", "decode", "decode_noalloc", "decode_plan",
+    "decode_workspace_size", "NOALLOC_SCRATCH_BYTES",
     "kv_bytes_per_token", "version",
 ]
 
 F16, BF16, FP8_E4M3 = 0, 1, 2
 DECODE_SHARED_KV = 1  # pa_decode flag: blocks are shared between sequences of the batch
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PA_NOALLOC_SCRATCH_BYTES: pa_decode_noalloc's fixed array
 _STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED",
            -3: "PA_ERR_NO_BLOCKS", -4: "PA_ERR_TABLE_OVERFLOW", -5: "PA_ERR_HIP"}
 
@@ -83,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_plan.argtypes = [i32] * 7 + [vp, vp]
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                             f32, c.c_int, c.c_int, f32, f32, i32, c.c_uint32, vp, sz, vp]
+    L.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    i32, f32, c.c_int, c.c_int, f32, f32, i32, c.c_uint32, vp]
     L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                    i32, i32, i32, f32, c.c_int, c.c_int, f32, f32, f32, f32,
                                    i32, c.c_uint32, vp, sz, vp]
@@ -371,6 +375,29 @@ def decode(query, k_cache, v_cache, block_tables, context_lens, max_context_len:
                            _dtype_code(k_cache), float(k_scale), float(v_scale),
                            int(partition_size), int(flags), ws_ptr, ws_bytes,
                            _stream(stream)))
+    return out
+
+
+def decode_noalloc(query, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                   scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                   partition_size: int = 0, flags: int = 0, out=None, stream=None):
+    """pa_decode_noalloc: pa_decode with its partials in the library's fixed device array
+    (no workspace; nothing allocated when `out` is given).  query [S, Hq, D]; returns out."""
+    torch = _torch()
+    S, Hq, D = query.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("decode_noalloc: shape mismatch")
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    _check(lib().pa_decode_noalloc(_dev(out, "out"), _dev(query, "query"),
+                                   _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                   _dev(block_tables, "block_tables"),
+                                   _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B, MB, NB,
+                                   int(max_context_len), float(scale), _dtype_code(query),
+                                   _dtype_code(k_cache), float(k_scale), float(v_scale),
+                                   int(partition_size), int(flags), _stream(stream)))
     return out
 
 

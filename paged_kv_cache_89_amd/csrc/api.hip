@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -279,6 +280,42 @@ static pa_status decode_impl(const char* who, void* out, const void* query, cons
   return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream), (std::string(who) + " merge launch").c_str());
 }
 
+// ---- scratch of pa_decode_noalloc --------------------------------------------------
+// A fixed device array for the partition partials of the no-allocation decode: the HIP
+// runtime gives every GPU the library runs on its own copy, at its own address, held until
+// the process ends.  Host code never uses the array's name as an address (on the host it
+// only names the symbol): the device address of each GPU's copy is looked up once, with that
+// GPU current, and kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch`.
+pa_status scratch_address(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, (std::string(who) + ": hipGetDevice").c_str());
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, std::string(who) + ": device ordinal " + std::to_string(dev) +
+                                        " beyond the " + std::to_string(kMaxDevices) + " supported");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, (std::string(who) + ": hipGetSymbolAddress").c_str());
+    if (!p) return fail(PA_ERR_HIP, std::string(who) + ": no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
@@ -456,6 +493,40 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                      num_blocks, max_context_len, scale, q_dtype, kv_dtype, k_scale, v_scale,
                      partition_size, flags, workspace, workspace_bytes_given, stream, nullptr,
                      nullptr, 1.0f, 1.0f);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* query, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t max_blocks_per_seq, int32_t num_blocks,
+                            int32_t max_context_len, float scale, pa_dtype q_dtype,
+                            pa_dtype kv_dtype, float k_scale, float v_scale,
+                            int32_t partition_size, uint32_t flags, void* stream) {
+  g_last_error.clear();
+  const char* who = "pa_decode_noalloc";
+  // The same plan pa_decode makes (and pa_decode_workspace_size sizes); refused before
+  // anything else when its partials do not fit the fixed array.
+  Plan plan;
+  pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, partition_size, &plan);
+  if (st != PA_OK) return st;
+  const size_t need = workspace_bytes(plan, num_seqs, num_heads, head_dim);
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_UNSUPPORTED, std::string(who) + ": the partition partials need " +
+                                        std::to_string(need) + " bytes, more than the " +
+                                        std::to_string((size_t)PA_NOALLOC_SCRATCH_BYTES) +
+                                        "-byte scratch array; call pa_decode with a workspace");
+  void* ws = nullptr;
+  if (need > 0 && num_seqs > 0) {
+    st = scratch_address(who, &ws);
+    if (st != PA_OK) return st;
+  }
+  return decode_impl(who, out, query, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                     partition_size, flags, ws, ws ? (size_t)PA_NOALLOC_SCRATCH_BYTES : 0,
+                     stream, nullptr, nullptr, 1.0f, 1.0f);
 }
 
 pa_status pa_decode_append(void* out, const void* query, const void* k_new, const void* v_new,
