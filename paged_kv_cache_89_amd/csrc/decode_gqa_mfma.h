@@ -175,17 +175,37 @@ __device__ __forceinline__ float rows_sum(float x) {
 #ifndef PA_FP8_LDS_DMA
 #define PA_FP8_LDS_DMA 1
 #endif
+// fp16/bf16 tiles: 1 = the same two-stage LDS ring (64 KiB per workgroup: two workgroups
+// per CU, two waves per SIMD, about 120 VGPRs); 0 = through registers, the block fetched two
+// ahead (196 VGPRs, also two waves per SIMD).  Measured on the GQA workload (three pairs on
+// one box): the ring 0.5 % faster per step, equal on four-token drafts.  A three-slot ring
+// per wave (K and V tiles in turn, 48 KiB per workgroup, three waves per SIMD, 8 KiB in
+// flight per wave) measured 0.5 % slower than the register path and was dropped.
+#ifndef PA_LDS_DMA_16
+#define PA_LDS_DMA_16 1
+#endif
 
 // One 16-byte-per-lane load from global memory into LDS: lane l's 16 bytes land at LDS
-// byte lds + 16 l (the wave fills 1 KiB).  The compiler's builtin places the (wave-uniform)
-// LDS address in M0 itself.  vmcnt drops once the bytes are in LDS (wait_vmcnt).  The stage
-// being refilled was read by the block before: lgkmcnt(0) first, so those reads have
-// returned before the new bytes can land.  Cache policy 2 is the non-temporal hint.
-typedef __attribute__((address_space(3))) void lds_void;
+// byte lds + 16 l (the wave fills 1 KiB).  The LDS address travels in M0; the statement
+// saves M0 first and restores it after, so whatever the compiler keeps there survives.
+// vmcnt drops once the bytes are in LDS (wait_vmcnt).  The stage being refilled was read by
+// the block before: lgkmcnt(0) first, so those reads have returned before the new bytes can
+// land.  (The compiler's global_load_lds builtin is not used: the compiler then waits for
+// every outstanding load, the next block's included, before the first LDS read after it.)
 template <bool NT>
-__device__ __forceinline__ void load_lds_x4(const void* src, uint8_t* lds) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, NT ? 2 : 0);
+__device__ __forceinline__ void load_lds_x4(const void* src, uint32_t lds) {
+  uint32_t saved;
+  if constexpr (NT)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Waves per SIMD the register allocation must allow.  e4m3 blocks carry half the bytes of
@@ -195,9 +215,10 @@ __device__ __forceinline__ void load_lds_x4(const void* src, uint8_t* lds) {
 // three without spilling.  The 16-bit instantiations are left to the compiler (they run at
 // the same speed with two or three).
 constexpr int gqa_min_waves(int kvk, bool lane, int g) {
-  return kvk == KIND_E4M3 ? (PA_FP8_NATIVE && PA_FP8_LDS_DMA ? 4 : (lane && g <= 8) ? 3
-                                                                                  : PA_GQA_MIN_WAVES)
-                          : PA_GQA_MIN_WAVES;
+  return kvk == KIND_E4M3 ? ((PA_FP8_NATIVE != 0 && PA_FP8_LDS_DMA != 0) ? 4
+                             : (lane && g <= 8)                        ? 3
+                                                                       : PA_GQA_MIN_WAVES)
+                          : (PA_LDS_DMA_16 != 0 ? 2 : PA_GQA_MIN_WAVES);
 }
 
 template <int D, int QK, int KVK, int G, bool NT, bool LANE>
@@ -224,9 +245,11 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   static_assert(G >= 2 && G <= 16, "group size");
   using Ops = MfmaOps<QK>;
   // per wave: NST stages of (K tile, V tile)
-  constexpr bool DMA = NATIVE && PA_FP8_LDS_DMA;
-  constexpr int NST = DMA ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_buf[4][NST][2][TILE];
+  constexpr bool DMA = NATIVE ? PA_FP8_LDS_DMA != 0 : (KVK != KIND_E4M3 && PA_LDS_DMA_16 != 0);
+  // LDS tiles of each wave: two-stage ring, slot 2 * stage + (0 = K, 1 = V); register
+  // path, slot 0 = K, 1 = V
+  constexpr int NSLOT = DMA ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_buf[4][NSLOT][TILE];
 
   // 16-byte chunk x of LDS row `row` holds chunk x ^ swz(row) of the V row: the two
   // chunks every ds_read_b64_tr_b16 takes from each of 16 rows then fall on distinct
@@ -236,12 +259,15 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
     if constexpr (NATIVE) return row % CPR;
     else return 2 * ((row / RPB) % (D / 16));
   };
-  // K tiles: chunk x of row t sits at x ^ kswz(t).  The logit operand reads of 16 lanes take
-  // one chunk from each of 16 rows; rows one 256-byte bank period apart share banks, so the
-  // e4m3 tiles (128- or 64-byte rows) rotate by the row's period index, which puts the 16
-  // reads on 16 different bank groups.  16-bit rows are a full period or more: t mod CPR.
+  // K tiles: chunk x of row t sits at x ^ kswz(t).  The logit operand reads (ds_read_b128)
+  // of lanes c = 0..15 take one 16-byte chunk from each of rows 0..15.  e4m3 rows are 128
+  // (64) bytes, so rows one 128-byte bank period apart start on the same bank: rotating by
+  // the row's index within its 8-row (4-row) run, xor its run, puts every 8 consecutive lanes
+  // on 8 different 16-byte bank groups of a 128-byte period and all 16 on different groups
+  // of a 256-byte period (conflict-free whether a pass serves 8 or 16 lanes).  16-bit rows
+  // are 256 bytes or more: t mod CPR.
   auto kswz = [](int row) {
-    if constexpr (NATIVE) return (row / RPB) % CPR;
+    if constexpr (NATIVE) return ((row / (128 / PITCH)) ^ (row / 8)) % CPR;
     else return row % CPR;
   };
 
@@ -374,12 +400,12 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   }
   auto issue = [&](int jj, int st) {
     const size_t boff = (size_t)ts.get(jj) * blk_stride;
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st]));
+    const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st + 1]));
 #pragma unroll
-    for (int i = 0; i < NLDS; ++i)
-      load_lds_x4<NT>(kbase + boff + goffk[i], lds_buf[wave][st][0] + 1024 * i);
+    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(kbase + boff + goffk[i], kl + 1024 * i);
 #pragma unroll
-    for (int i = 0; i < NLDS; ++i)
-      load_lds_x4<NT>(vbase + boff + goffv[i], lds_buf[wave][st][1] + 1024 * i);
+    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(vbase + boff + goffv[i], vl + 1024 * i);
   };
   if constexpr (DMA) issue(j0, 0);
   else fetch(j0, ka, va);
@@ -438,8 +464,8 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   float m_ref = -INFINITY;  // reference maximum of head c (log2 units), same in its 4 lanes
   float l_part = 0.f;       // this lane's share of head c's denominator
 
-  uint8_t* kt = lds_buf[wave][0][0];
-  uint8_t* vt = lds_buf[wave][0][1];
+  uint8_t* kt = lds_buf[wave][0];
+  uint8_t* vt = lds_buf[wave][1];
   const float qk_scale = a.qk_scale;
   // This lane's share of a tile: wave load i, token row i*TPLS + lane/LPTS, elements
   // (lane % LPTS) * EPLS .. +EPLS, i.e. LDS chunks (lane % LPTS) * CPL .. +CPL of that row.
@@ -610,8 +636,8 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
       } else {
         wait_vmcnt<0>();
       }
-      kt = lds_buf[wave][st][0];
-      vt = lds_buf[wave][st][1];
+      kt = lds_buf[wave][2 * st];
+      vt = lds_buf[wave][2 * st + 1];
       if (j * BS + BS > n) {  // V rows at or beyond n become zeros (their bytes may be NaN)
 #pragma unroll
         for (int x = lane; x < TILE / 16; x += 64)

@@ -1,6 +1,8 @@
 """Test-side helpers: build oracle inputs from a seeded case and compare results."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 import oracle
@@ -79,6 +81,15 @@ def compare(gpu_out_f64: np.ndarray, ref_f64: np.ndarray, atol: float, rtol_row:
     if rtol_row is not None:
         assert max_rel <= rtol_row, f"max row rel err {max_rel} > {rtol_row}"
     return max_abs, max_rel
+
+
+def host_threads() -> int:
+    """Oracle threads: the CPUs this process may run on, at most 16 (a GPU machine's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 # ------------------------------------------------------------------ GPU-side helpers

@@ -16,8 +16,8 @@ import torch
 import oracle
 import paged_kv_cache_89_amd as pa
 import workloads
-from helpers import DT, compare, dev_i32, oracle_caches, oracle_decode, oracle_tables, \
-    to_bits, to_dev, tolerance
+from helpers import DT, compare, dev_i32, host_threads, oracle_caches, oracle_decode, \
+    oracle_tables, to_bits, to_dev, tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -138,11 +138,11 @@ def test_prefix_bound_clamps_and_equals_plain_decode():
     assert np.array_equal(a, again)
 
 
-def test_full_size_fp8_shared_prompts_sampled_rows():
+def test_full_size_fp8_shared_prompts_all_rows():
     """The fp8 shared-prompt workload at full size (256 sequences in groups of 4 behind
     1024-token prompts, 32 heads, d 128, e4m3 K/V) launched as the benchmark launches it:
-    the oracle checks sampled (sequence, head) rows one by one; every row is finite and
-    within rounding of the plain library decode."""
+    the threaded oracle computes every (sequence, head) row; the output is also within
+    rounding of the plain library decode."""
     sp = workloads.SPECS["fp8_prefix"]
     seed = 8900 + list(workloads.SPECS).index("fp8_prefix")
     ctx, free = workloads.draw_lengths(sp, seed)
@@ -159,16 +159,11 @@ def test_full_size_fp8_shared_prompts_sampled_rows():
                       flags=pa.DECODE_SHARED_KV)
     torch.cuda.synchronize()
     got = _f64(out)
-    assert np.isfinite(got).all()
     atol, rrel = tolerance(sp)
     compare(got, _f64(plain), atol, None, None)
-    rng = np.random.default_rng(seed)
-    S, H = sp.num_seqs, sp.num_heads
-    rows = set(zip(rng.integers(0, S, 64).tolist(), rng.integers(0, H, 64).tolist()))
-    rows |= {(s, 0) for s in range(4)}      # one whole group
-    rows = np.array(sorted(rows), np.int32)
     qb, kb, vb = to_bits(q), to_bits(kd), to_bits(vd)
     del kd, vd
     ref = oracle.decode(qb, DT[sp.q_dtype], kb, vb, DT[sp.kv_dtype], tables, ctx,
-                        sp.num_kv_heads, sp.block_size, sp.scale, ks, vs, rows=rows)
-    compare(got[rows[:, 0], rows[:, 1]], ref[rows[:, 0], rows[:, 1]], atol, rrel, sp.q_dtype)
+                        sp.num_kv_heads, sp.block_size, sp.scale, ks, vs,
+                        threads=host_threads())
+    compare(got, ref, atol, rrel, sp.q_dtype)

@@ -300,12 +300,11 @@ def test_hot_kernels_use_no_scratch():
             spilled[name] = scratch
     assert not spilled, spilled
     # the kernels the five workloads run, with their occupancy-setting register counts
-    # (four waves per SIMD need <= 128 VGPRs, three <= 168, two <= 256).  The bf16 GQA
-    # register path fetches the block two ahead into the registers a staged block frees
-    # (two blocks in flight while one is consumed): 196 VGPRs, two waves per SIMD, measured
-    # 0.6 % faster per step on the GQA workload than one block ahead at three waves.
+    # (four waves per SIMD need <= 128 VGPRs, three <= 168).  The bf16 GQA kernel stages
+    # K/V through a two-stage LDS ring (64 KiB per workgroup), which holds it to two waves
+    # per SIMD; its registers stay within the four-wave budget.
     hot = {"_ZN2pa19paged_decode_kernelILi128ELi16ELi0ELi0ELi1ELb1EEEvNS_10DecodeArgsE": 128,
-           "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0EEEvNS_10DecodeArgsE": 256,
+           "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0EEEvNS_10DecodeArgsE": 128,
            # the fp8 shared-prompt prefix units (4 members x 1 head, per-column masks)
            "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi2ELi4ELb1ELb1EEEvNS_10DecodeArgsE": 128}
     for name, vgpr_max in hot.items():
