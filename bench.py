@@ -150,6 +150,7 @@ def main():
         pa.write_kv(k_new, v_new, lk, lv, tables_d, seq_ids, positions, k_inv, v_inv,
                     stream=stream)
 
+    cascade_plan = None
     path = args.decode_path
     if path == "auto":
         path = "shared_prefix" if sp.group_size else "plain"
@@ -188,6 +189,7 @@ def main():
         shared_tok = np.minimum(prefix_blocks * B, ctx.reshape(-1, sp.group_size).max(axis=1))
         own = ctx - np.minimum(np.repeat(prefix_blocks * B, sp.group_size), ctx)
         unique_bytes = workloads.kv_bytes(sp, np.concatenate([shared_tok, own]))
+        cascade_plan = pa.decode_shared_prefix_plan(S, Hq, Hkv, D, B, max_ctx, max_pb, P)
         kernels = ("paged_decode_gqa_mfma_kernel (group prefixes) + paged_decode_kernel "
                    "(own tokens) + merge_partitions_kernel")
 
@@ -291,8 +293,17 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, args.cpu_seconds)
+        # the output the oracle checks: one more decode of layer 0 (whose K/V it reads)
+        write(0)
+        decode(0)
+        torch.cuda.synchronize()
+        gpu_out = (outm if path == "multi" else out).double().cpu().numpy()
+        qsrc = qm if path == "multi" else q
+        cpu = cpu_baseline(sp, qsrc, kc, vc, tables, ctx, k_scale, v_scale, args.cpu_seconds,
+                           gpu_out, T if path == "multi" else 0)
 
+    block_bytes = workloads.kv_bytes(sp, -(-ctx // B) * B)  # whole blocks of every context
+    shared = unique_bytes != kv_bytes
     line = {
         "metric": "paged decode attention: achieved KV HBM GB/s (% of peak) + decode tokens/s",
         "value": round(value, 2),
@@ -307,18 +318,26 @@ def main():
         "dtype": sp.kv_dtype,
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "value_bytes": ("logical: every sequence's own context, shared prompt blocks counted "
+                        "once per sequence that reads them (above the HBM peak is possible; "
+                        "roofline.achieved uses the bytes the call must read)" if shared else
+                        "algorithmic: sum over sequences of n * num_kv_heads * head_dim * 2 * "
+                        "bytes per element, K and V read once"),
         "decode_tokens_per_s": round(S * T / (ms_per_step * 1e-3), 1),
         "config": {
             "workload": sp.name, "num_seqs": S, "num_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "block_size": B, "context_lens": f"U[{sp.ctx_lo},{sp.ctx_hi}]"
             + (f"+{sp.prompt_len}" if sp.prompt_len else ""), "num_blocks": sp.num_blocks,
-            "q_dtype": sp.q_dtype, "kv_dtype": sp.kv_dtype, "partition_size": used_P,
-            "num_partitions": nparts, "kv_bytes_per_step": kv_bytes,
+            "q_dtype": sp.q_dtype, "kv_dtype": sp.kv_dtype,
+            "partition_size": used_P if not cascade_plan else None,
+            "num_partitions": nparts if not cascade_plan else None, "kv_bytes_per_step": kv_bytes,
             "unique_kv_bytes_per_step": unique_bytes, "seed": seed,
             "decode_flags": flags, "decode_path": path,
             "step": ("fused: pa_decode_append stores the new tokens and decodes in one call"
                      if fused else "pa_write_kv, then the decode"),
-        } | ({"query_len": T} if path == "multi" else {}),
+            "block_granular_kv_bytes_per_step": block_bytes,
+        } | ({"query_len": T} if path == "multi" else {})
+          | ({"cascade_plan": cascade_plan} if cascade_plan else {}),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -330,6 +349,12 @@ def main():
         "decode_latency": latency,
         "cpu_baseline": cpu,
     }
+    if shared:
+        line["value_unique_GBps"] = round(unique_bytes / (ms_per_step * 1e-3) / 1e9, 2)
+        line["pct_of_hbm_peak_unique"] = round(100.0 * line["value_unique_GBps"] / HBM_PEAK_GBS, 2)
+    if sp.name == "opt13b_layer":
+        # the 40 layers of OPT-13B, attention only: one token per sequence through all of them
+        line["opt13b_40_layer_tokens_per_s"] = round(S * T / (40 * ms_per_step * 1e-3), 1)
     if swap is not None:
         line["swap"] = swap
     if copy is not None:
@@ -415,16 +440,29 @@ def swap_leg(sp, kc, vc, tables, nseq):
             "out_ms": round(t_out, 4), "in_ms": round(t_in, 4)}
 
 
-def cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, target_s):
-    """The oracle (plain fp64 C++) on the host cores, over a bounded sample of sequences
-    (all heads of the first few), scaled to the same GB/s metric."""
+def host_cpus():
+    """(CPUs this process may run on, CPUs the host reports)."""
+    try:
+        mine = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        mine = os.cpu_count() or 1
+    return mine, os.cpu_count() or mine
+
+
+def cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, target_s, gpu_out, query_len):
+    """The oracle (plain fp64 C++, unmodified) on the host cores, over a bounded sample of
+    sequences (all heads of the first few) scaled to the same GB/s metric: wall time, median
+    of 3 runs, with one thread per CPU this process may use (at most 16, a GPU machine's share)
+    and with one thread.  The sample's oracle output also checks the GPU output of the same
+    rows (parity at the benchmark's own launch configuration)."""
     import torch
 
     import oracle
     import workloads
 
     dt = {"f16": oracle.F16, "bf16": oracle.BF16, "e4m3": oracle.E4M3}
-    threads = min(os.cpu_count() or 1, 16)
+    mine, host = host_cpus()
+    threads = max(1, min(mine, 16))
 
     def sample(nseq):
         rows = tables[:nseq]
@@ -441,31 +479,58 @@ def cpu_baseline(sp, q, kc, vc, tables, ctx, k_scale, v_scale, target_s):
         qb = q[:nseq].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
         return qb, bits(kc), bits(vc), t, ctx[:nseq].copy()
 
-    def run(nseq, nthreads=threads):
-        qb, kb, vb, t, c = sample(nseq)
+    def once(inputs, nthreads):
+        qb, kb, vb, t, c = inputs
         t0 = time.perf_counter()
-        oracle.decode(qb, dt[sp.q_dtype], kb, vb, dt[sp.kv_dtype], t, c, sp.num_kv_heads,
-                      sp.block_size, sp.scale, k_scale, v_scale, threads=nthreads)
-        return time.perf_counter() - t0, workloads.kv_bytes(sp, c)
+        if query_len:
+            ref = oracle.decode_multi(qb, dt[sp.q_dtype], kb, vb, dt[sp.kv_dtype], t, c,
+                                      sp.num_kv_heads, sp.block_size, sp.scale, k_scale,
+                                      v_scale, threads=nthreads)
+        else:
+            ref = oracle.decode(qb, dt[sp.q_dtype], kb, vb, dt[sp.kv_dtype], t, c,
+                                sp.num_kv_heads, sp.block_size, sp.scale, k_scale, v_scale,
+                                threads=nthreads)
+        return time.perf_counter() - t0, ref
 
-    dt1, _ = run(1)  # probe: one sequence
-    nseq = int(max(1, min(sp.num_seqs, target_s / max(dt1, 1e-3))))
-    secs, nbytes = run(nseq)
-    # one thread, on a sample of about a second of work
-    n1 = int(max(1, min(nseq, 1.0 / max(dt1 * threads, 1e-3))))
-    secs1, nbytes1 = run(n1, 1)
+    def median3(inputs, nthreads):
+        runs = [once(inputs, nthreads) for _ in range(3)]
+        return float(np.median([r[0] for r in runs])), runs[0][1]
+
+    probe, _ = once(sample(1), threads)
+    nseq = int(max(1, min(sp.num_seqs, target_s / 3 / max(probe, 1e-3))))
+    inputs = sample(nseq)
+    secs, ref = median3(inputs, threads)
+    # the GPU metric's bytes: each sequence's K/V once per pass (all its query tokens)
+    nbytes = workloads.kv_bytes(sp, inputs[4])
+    # one thread, on a sample of about a second of work per run
+    n1 = int(max(1, min(nseq, 1.0 / max(probe * threads, 1e-3))))
+    inputs1 = inputs if n1 == nseq else sample(n1)
+    secs1, _ = median3(inputs1, 1)
+    nbytes1 = workloads.kv_bytes(sp, inputs1[4])
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
     except OSError:
         pass
+    # parity of the GPU rows the sample covers (fp64 oracle, unrounded)
+    got = gpu_out[:nseq]
+    err = np.abs(got - ref)
+    rn = np.abs(ref).max(axis=-1)
+    row_rel = np.where(rn > 0, err.max(axis=-1) / np.where(rn > 0, rn, 1), err.max(axis=-1))
+    atol = 2e-2 if sp.kv_dtype == "e4m3" else 2e-3
     return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds": round(secs, 2),
-            "single_thread_value": round(nbytes1 / secs1 / 1e9, 4), "cpu": model,
-            "sample": f"{nseq} of {sp.num_seqs} sequences, all {sp.num_heads} heads "
-                      f"({nbytes} KV bytes), fp64 C++ oracle with {threads} threads; "
-                      f"single thread: {n1} sequences"}
+            "kind": "oracle", "seconds_median_of_3": round(secs, 3),
+            "single_thread_value": round(nbytes1 / secs1 / 1e9, 4),
+            "single_thread_seconds_median_of_3": round(secs1, 3),
+            "host_cpus": host, "cpus_available": mine, "cpu": model,
+            "sample": f"{nseq} of {sp.num_seqs} sequences, all {sp.num_heads} heads"
+                      + (f", {query_len} query tokens each" if query_len else "")
+                      + f" ({nbytes} KV bytes per pass), fp64 C++ oracle with "
+                      f"{threads} threads, median of 3 runs; single thread: {n1} sequences",
+            "parity": {"rows": int(got.shape[0] * int(np.prod(got.shape[1:-1]))),
+                       "max_abs_err": float(err.max()), "max_row_rel_err": float(row_rel.max()),
+                       "bar_abs": atol, "bar_row_rel": None if sp.kv_dtype == "e4m3" else 1e-2}}
 
 
 if __name__ == "__main__":

@@ -389,6 +389,19 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_head
                                               int32_t max_prefix_blocks,
                                               int32_t partition_size);
 
+/* The plan pa_decode_shared_prefix makes for these arguments (host only, nothing launched):
+ * the partition length of the prefix launch (tokens), the partial slots per row that the
+ * prefix launch and the per-sequence launch own (prefix_slots + suffix_slots in all, the
+ * merge's input), and the shortest share of a row's own blocks in the per-sequence launch
+ * (0 = fixed partitions of prefix_partition_size tokens instead of equal shares).  Any
+ * output pointer may be NULL. */
+pa_status pa_decode_shared_prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t max_context_len, int32_t max_prefix_blocks,
+                                       int32_t partition_size, int32_t* prefix_partition_size,
+                                       int32_t* prefix_slots, int32_t* suffix_slots,
+                                       int32_t* suffix_min_blocks);
+
 pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
                                   const void* v_cache, const int32_t* block_tables,
                                   const int32_t* context_lens, const int32_t* prefix_blocks,

@@ -560,6 +560,24 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_head
   return cascade_workspace_bytes(cp, num_seqs, num_heads, head_dim);
 }
 
+pa_status pa_decode_shared_prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       int32_t max_context_len, int32_t max_prefix_blocks,
+                                       int32_t partition_size, int32_t* prefix_partition_size,
+                                       int32_t* prefix_slots, int32_t* suffix_slots,
+                                       int32_t* suffix_min_blocks) {
+  g_last_error.clear();
+  CascadePlan cp;
+  const pa_status st = make_cascade_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                         max_context_len, max_prefix_blocks, partition_size, &cp);
+  if (st != PA_OK) return st;
+  if (prefix_partition_size) *prefix_partition_size = cp.partition_size;
+  if (prefix_slots) *prefix_slots = cp.pre_parts;
+  if (suffix_slots) *suffix_slots = cp.suf_parts;
+  if (suffix_min_blocks) *suffix_min_blocks = cp.suf_min_blocks;
+  return PA_OK;
+}
+
 pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
                                   const void* v_cache, const int32_t* block_tables,
                                   const int32_t* context_lens, const int32_t* prefix_blocks,

@@ -201,6 +201,17 @@ def test_shared_prefix_workspace_and_errors_without_gpu():
     # no prefix bound: per-sequence slots only
     assert pa.decode_shared_prefix_workspace_size(4, 8, 8, 64, 16, 100, 0) == 4 * 8 * 1 * 66 * 4
     assert pa.decode_shared_prefix_workspace_size(4, 8, 8, 64, 16, 100, -1) == 0  # bad bound
+    # the plan query reports the same slot counts the workspace is sized from
+    for args in ((256, 32, 32, 128, 16, 1536, 64, 0), (256, 32, 32, 128, 16, 1536, 64, 512),
+                 (256, 32, 32, 128, 16, 4096, 64, 0), (4, 8, 8, 64, 16, 100, 2, 0)):
+        plan = pa.decode_shared_prefix_plan(*args)
+        S, Hq, d = args[0], args[1], args[3]
+        slots = plan["prefix_slots"] + plan["suffix_slots"]
+        assert pa.decode_shared_prefix_workspace_size(*args) == S * Hq * slots * (d + 2) * 4
+    assert pa.decode_shared_prefix_plan(256, 32, 32, 128, 16, 1536, 64) == {
+        "prefix_partition_size": 512, "prefix_slots": 2, "suffix_slots": 2,
+        "suffix_min_blocks": 8}
+    assert pa.decode_shared_prefix_plan(256, 32, 32, 128, 16, 1536, 64, 512)["suffix_min_blocks"] == 0
     L = pa.lib()
 
     def call(S=8, K=4, Hq=8, Hkv=8, d=128, B=16, q=1, kv=2, flags=0):
