@@ -61,6 +61,15 @@ struct Plan {
 // 0.5-1 % on the OPT-13B one; the shared-prefix decode keeps 512, which splits its
 // block-aligned prompts evenly (768 measured 4 % slower there).
 constexpr int32_t kAutoPartition = 768;
+// 1: matrix-core decodes (grouped queries, multi-token) of at most kBalancedMaxSeqs rows
+// spread the row-partitions over the XCDs by their blocks (balanced_coords); compile-time
+// switch for measurements.  Measured against contiguous ranges of rows, three pairs on one
+// box: GQA workload 1.1 % faster per step, four-token drafts over it 2.1 %; the vector
+// kernel's OPT-13B layer 5.7 % slower and the long-context workload 0.5 % slower, so the
+// vector kernel keeps contiguous ranges.
+#ifndef PA_BALANCED_XCD
+#define PA_BALANCED_XCD 1
+#endif
 constexpr int32_t kCascadePartition = 512;
 // Partials are stored and merged with 8- and 16-byte vector accesses.
 constexpr uintptr_t kWorkspaceAlign = 16;
@@ -257,7 +266,8 @@ static pa_status decode_impl(const char* who, void* out, const void* query, cons
   a.qk_scale = scale * kLog2e * (f8 ? k_scale : 1.0f);
   a.v_scale = f8 ? v_scale : 1.0f;
   a.seq_fastest = shared ? 1 : 0;
-  a.xcd_remap = 1;
+  a.xcd_remap = (PA_BALANCED_XCD && gqa_mfma_supported(shape) && !shared &&
+                 num_seqs <= kBalancedMaxSeqs) ? 2 : 1;
   a.num_slots = plan.num_parts > 1 ? plan.num_parts : 0;
   a.slot_base = 0;
   a.mode = MODE_PLAIN;
@@ -784,7 +794,7 @@ pa_status pa_decode_multi(void* out, const void* query, const void* k_cache, con
   a.qk_scale = scale * kLog2e * (f8 ? k_scale : 1.0f);
   a.v_scale = f8 ? v_scale : 1.0f;
   a.seq_fastest = shared ? 1 : 0;
-  a.xcd_remap = 1;
+  a.xcd_remap = (PA_BALANCED_XCD && !shared && num_seqs <= kBalancedMaxSeqs) ? 2 : 1;
   a.mode = MODE_MULTI;
   a.seq_group = 1; a.num_groups = num_seqs; a.max_prefix_blocks = 0; a.prefix_blocks = nullptr;
   a.query_len = query_len; a.tree_masks = tree_masks;

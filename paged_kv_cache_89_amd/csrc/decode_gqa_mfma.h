@@ -49,6 +49,10 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 #ifndef PA_GQA_MIN_WAVES
 #define PA_GQA_MIN_WAVES 1
 #endif
+// Wavefronts (independent work units) per workgroup (compile-time tuning knob).
+#ifndef PA_GQA_WAVES
+#define PA_GQA_WAVES 4
+#endif
 
 // e4m3 caches: 1 = contract the codes on the fp8 matrix cores (no widening); 0 = widen
 // them to the query's 16-bit type while staging (compile-time switch for measurements).
@@ -222,7 +226,7 @@ constexpr int gqa_min_waves(int kvk, bool lane, int g) {
 }
 
 template <int D, int QK, int KVK, int G, bool NT, bool LANE>
-__global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode_gqa_mfma_kernel(
+__global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) void paged_decode_gqa_mfma_kernel(
     const DecodeArgs a) {
   constexpr int BS = 16;
   constexpr int KSTEPS = D / 32;             // 16x16x32 steps over the head dimension
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   // LDS tiles of each wave: two-stage ring, slot 2 * stage + (0 = K, 1 = V); register
   // path, slot 0 = K, 1 = V
   constexpr int NSLOT = DMA ? 4 : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_buf[4][NSLOT][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_buf[PA_GQA_WAVES][NSLOT][TILE];
 
   // 16-byte chunk x of LDS row `row` holds chunk x ^ swz(row) of the V row: the two
   // chunks every ds_read_b64_tr_b16 takes from each of 16 rows then fall on distinct
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
   const bool prefix = LANE && a.mode == MODE_PREFIX;
   const bool multi = LANE && a.mode == MODE_MULTI;
   const int rows = prefix ? a.num_groups : a.num_seqs;
-  const UnitCoords uc = unit_coords(a, 4, wave, rows);
+  const UnitCoords uc = unit_coords(a, PA_GQA_WAVES, wave, rows, BS);
   if (!uc.ok) return;
   const int s = uc.s, kvh = uc.kvh, part = uc.part;  // s: the sequence, or in prefix mode the group
   const int r = lane >> 4;
@@ -711,12 +715,12 @@ __global__ __launch_bounds__(256, gqa_min_waves(KVK, LANE, G)) void paged_decode
 
 template <int D, int QK, int KVK, int G, bool NT>
 hipError_t launch_gqa_mfma_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid = decode_grid(a, 4);
+  const dim3 grid = decode_grid(a, PA_GQA_WAVES);
   if (a.mode == MODE_PREFIX || a.mode == MODE_MULTI)
-    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true>), grid, dim3(64 * PA_GQA_WAVES), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, false>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, false>), grid, dim3(64 * PA_GQA_WAVES), 0,
                        stream, a);
   return hipGetLastError();
 }

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const UnitCoords uc = unit_coords(a, PA_DECODE_WAVES, wave, a.num_seqs);
+  const UnitCoords uc = unit_coords(a, PA_DECODE_WAVES, wave, a.num_seqs, BS);
   if (!uc.ok) return;
   const int s = uc.s, kvh = uc.kvh, part = uc.part;
   const int h0 = kvh * G;

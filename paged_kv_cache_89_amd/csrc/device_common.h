@@ -183,7 +183,7 @@ struct TableSlice {
 // workgroup (`waves` per workgroup); false when the wavefront has no unit.
 //   xcd_remap 1: the hardware deals workgroups to the 8 XCDs round-robin; they are
 //     renumbered so that XCD x runs a contiguous range of logical workgroups (a bijection
-//     for any grid size).  0: launch order.
+//     for any grid size).  0: launch order.  2: work-balanced ranges (balanced_coords).
 //   seq_fastest 0: units in (row, partition, KV head) order, neighbouring heads of the
 //     same blocks side by side; 1: (partition, KV head, row), the rows that share blocks
 //     side by side.
@@ -191,10 +191,11 @@ struct UnitCoords {
   int s, kvh, part;
   bool ok;
 };
-__device__ __forceinline__ UnitCoords unit_coords(const DecodeArgs& a, int waves, int wave,
-                                                  int rows) {
+
+__device__ __forceinline__ UnitCoords remapped_coords(const DecodeArgs& a, int waves, int wave,
+                                                      int rows) {
   int wg = blockIdx.x;
-  if (a.xcd_remap == 1) {
+  if (a.xcd_remap != 0) {
     const int G8 = gridDim.x, x = wg % 8, loc = wg / 8, per = G8 / 8, rem = G8 % 8;
     wg = (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
   }
@@ -213,6 +214,107 @@ __device__ __forceinline__ UnitCoords unit_coords(const DecodeArgs& a, int waves
     u.part = rest / a.num_kv_heads;
   }
   return u;
+}
+
+// Work-balanced XCD ranges (xcd_remap 2; units in (row, partition, KV head) order; at most
+// kBalancedMaxSeqs rows).  The row-partitions that hold blocks are laid out in row order;
+// XCD x takes those whose first block lies in the x-th eighth of all the rows' blocks, KV
+// heads fastest, so every XCD reads the same amount of K/V (to within one partition) and
+// still works through a few neighbouring rows at a time; partitions past a row's end get
+// no unit at all.  Workgroup i runs on XCD i % 8 (round-robin dealing); the grid has
+// rows * num_parts * num_kv_heads units, and the workgroups of an XCD beyond its range's
+// units find none and exit.  If some XCD's range has more units than the XCD has
+// wavefronts, every wavefront falls back to the contiguous mapping (the decision is the
+// same in all of them: it depends only on the lengths).  Every cross-lane chain below is
+// independent of the others, so they overlap.
+__device__ __forceinline__ UnitCoords balanced_coords(const DecodeArgs& a, int waves, int wave,
+                                                      int block_size) {
+  const int lane = threadIdx.x & 63;
+  const int S = a.num_seqs, bpp = a.blocks_per_part, H = a.num_kv_heads;
+  constexpr int K = kBalancedMaxSeqs / 64;
+  // lane's rows s = lane + 64 k: blocks and non-empty partitions
+  int nb[K], np[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int s = lane + 64 * k;
+    int n = s < S ? a.ctx[s] : 0;
+    n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+    nb[k] = (n + block_size - 1) / block_size;
+    np[k] = (nb[k] + bpp - 1) / bpp;
+  }
+  // exclusive prefix sums in row order: wb = blocks before the row, wp = row-partitions
+  int ib[K], ip[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) { ib[k] = nb[k]; ip[k] = np[k]; }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int yb = __shfl_up(ib[k], off), yp = __shfl_up(ip[k], off);
+      if (lane >= off) { ib[k] += yb; ip[k] += yp; }
+    }
+  }
+  int wb[K], wp[K], cb = 0, cp = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    wb[k] = cb + ib[k] - nb[k];
+    wp[k] = cp + ip[k] - np[k];
+    cb += __builtin_amdgcn_readlane(ib[k], 63);
+    cp += __builtin_amdgcn_readlane(ip[k], 63);
+  }
+  // row-partitions whose first block lies before block y * total / 8, y = 1..7
+  int c[7];
+#pragma unroll
+  for (int y = 0; y < 7; ++y) {
+    const int t = (int)(((long long)cb * (y + 1)) / 8);
+    c[y] = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int d = t - wb[k];
+      const int m = d <= 0 ? 0 : (d + bpp - 1) / bpp;
+      c[y] += m < np[k] ? m : np[k];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int y = 0; y < 7; ++y) c[y] += __shfl_xor(c[y], off);
+  const int G8 = gridDim.x, x = blockIdx.x % 8, loc = blockIdx.x / 8;
+  const int per_lo = G8 / 8, rem = G8 % 8;
+  bool fits = true;
+  int r_lo = 0, r_hi = 0, prev = 0;
+#pragma unroll
+  for (int y = 0; y < 8; ++y) {
+    const int r = y == 7 ? cp : __builtin_amdgcn_readfirstlane(c[y]);
+    fits = fits && (r - prev) * H <= (per_lo + (y < rem ? 1 : 0)) * waves;
+    if (y == x) { r_lo = prev; r_hi = r; }
+    prev = r;
+  }
+  if (!fits) return remapped_coords(a, waves, wave, S);
+  UnitCoords u;
+  const int unit = r_lo * H + loc * waves + wave;
+  const int rp = unit / H;
+  u.kvh = unit % H;
+  u.s = 0;
+  u.part = 0;
+  // the row holding row-partition rp
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const uint64_t hit = __ballot(np[k] > 0 && rp >= wp[k] && rp < wp[k] + np[k]);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      u.s = 64 * k + l;
+      u.part = rp - __builtin_amdgcn_readlane(wp[k], l);
+    }
+  }
+  u.ok = unit < r_hi * H;
+  return u;
+}
+
+__device__ __forceinline__ UnitCoords unit_coords(const DecodeArgs& a, int waves, int wave,
+                                                  int rows, int block_size) {
+  if (a.xcd_remap == 2) return balanced_coords(a, waves, wave, block_size);
+  return remapped_coords(a, waves, wave, rows);
 }
 
 // Blocks per unit of a row whose units walk blocks [jb, nblk): the fixed partition, or

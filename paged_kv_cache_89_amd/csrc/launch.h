@@ -12,6 +12,7 @@ enum Kind : int { KIND_F16 = 0, KIND_BF16 = 1, KIND_E4M3 = 2 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxUnitBlocks = 64;  // blocks one work unit (wavefront) walks at most
+constexpr int kBalancedMaxSeqs = 128;  // rows the work-balanced XCD ranges handle (xcd_remap 2)
 
 // Decode over work units (sequence, KV head, partition).  A unit walks blocks
 // [part * blocks_per_part, min(ceil(n / B), (part + 1) * blocks_per_part)) of its
@@ -52,7 +53,8 @@ struct DecodeArgs {
   float qk_scale;            // scale * log2(e) * k_scale
   float v_scale;
   int32_t seq_fastest;       // unit order: 0 = (seq, part, kv head), 1 = (part, kv head, seq)
-  int32_t xcd_remap;         // 1 = each XCD runs a contiguous range of workgroups
+  int32_t xcd_remap;         // 1 = each XCD runs a contiguous range of workgroups; 2 = of
+                             // row-partitions, balanced by blocks (balanced_coords)
   int32_t mode;              // DecodeMode
   int32_t seq_group, num_groups, max_prefix_blocks;
   const int32_t* prefix_blocks;  // [num_groups] shared leading blocks of each group

@@ -455,3 +455,26 @@ def test_pools_beyond_4_gib(kv, q, G):
     finally:
         del kd, vd
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("S", [128, 129])
+def test_grouped_queries_skewed_rows_over_xcds(S):
+    """Matrix-core decodes spread row-partitions over the XCDs by their blocks (at most 128
+    rows; 129 take contiguous ranges): a few long rows among many short or empty ones, so
+    the ranges cut rows apart; every row must still be decoded once and only once."""
+    rng = np.random.default_rng(S)
+    lens = rng.integers(0, 40, S)
+    lens[rng.choice(S, 5, replace=False)] = [3000, 2047, 1500, 777, 3001]
+    lens[rng.choice(S, 10, replace=False)] = 0
+    B, d, G = 16, 128, 4
+    sp = workloads.Spec("skew", S, 2 * G, 2, d, B, 1, 1,
+                        int(sum(math.ceil(n / B) for n in lens)) + 5,
+                        math.ceil(int(lens.max()) / B) + 1, "bf16", "bf16", 1 / math.sqrt(d))
+    case = workloads.generate(sp, 5200 + S, context_lens=lens.tolist())
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    ref = oracle_decode(case, tables, k, v)
+    for P in (0, 256):
+        out = _f64(_gpu_decode(case, tables, k, v, partition_size=P))
+        assert (out[lens == 0] == 0).all()
+        compare(out, ref, 2e-3, 1e-2, "bf16")
