@@ -372,13 +372,38 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
   };
   TableSlice ts;
   ts.init(table_row, j0, j1, a.num_blocks, lane);
-  // appending decode: the unit that walks the sequence's last block stores the new token's
-  // row there first (a table entry outside the pool is skipped, as the KV write does)
-  if (a.append && a.mode == MODE_PLAIN && n > 0 && j1 == (n + BS - 1) / BS) {
-    const int raw = __builtin_amdgcn_readlane(ts.ids, (n - 1) / BS - ts.j0);
-    if ((unsigned)raw < (unsigned)a.num_blocks)
-      append_new_row<D, BS, QK, KVK>(a, s, kvh, raw, (n - 1) % BS, lane,
-                                     (n - 1) / BS - j0 < 2);
+  // Appending decode (the unit that walks the sequence's last block, whose table entry lies
+  // in the pool -- an entry outside it skips the write, as the KV write does).  LDS-ring
+  // path: once block jn has landed, lane x < CPR writes 16-byte chunk x of the new K and V
+  // rows (in the cache's type: e4m3 codes of x * inv_scale, the KV write's conversion)
+  // into slot tn of the staged tiles, and the rows go to the cache after the epilogue, so
+  // no load waits for the store.  Register path: the rows are stored first.
+  const int jn = (n - 1) / BS, tn = (n - 1) % BS;
+  bool app = a.append && a.mode == MODE_PLAIN && n > 0 && j1 == (n + BS - 1) / BS;
+  int app_phys = 0;
+  u32x4 nk = u32x4{0, 0, 0, 0}, nv = u32x4{0, 0, 0, 0};
+  if constexpr (DMA) {
+    if (app && lane < CPR) {  // loaded whatever the table entry says (checked below)
+      const size_t src = ((size_t)s * a.num_kv_heads + kvh) * D + (size_t)lane * (16 / LE);
+      const u32x4* ks = (const u32x4*)((const uint16_t*)a.k_new + src);
+      const u32x4* vs = (const u32x4*)((const uint16_t*)a.v_new + src);
+      if constexpr (LE == 1) {
+        const u32x2 k0 = src8_to_e4m3<QK>(ks[0], a.k_inv_scale), k1 = src8_to_e4m3<QK>(ks[1], a.k_inv_scale);
+        const u32x2 v0 = src8_to_e4m3<QK>(vs[0], a.v_inv_scale), v1 = src8_to_e4m3<QK>(vs[1], a.v_inv_scale);
+        nk = u32x4{k0[0], k0[1], k1[0], k1[1]};
+        nv = u32x4{v0[0], v0[1], v1[0], v1[1]};
+      } else {
+        nk = ks[0];
+        nv = vs[0];
+      }
+    }
+  }
+  if (app) {
+    app_phys = __builtin_amdgcn_readlane(ts.ids, jn - ts.j0);
+    app = (unsigned)app_phys < (unsigned)a.num_blocks;
+  }
+  if constexpr (!DMA) {
+    if (app) append_new_row<D, BS, QK, KVK>(a, s, kvh, app_phys, tn, lane, jn - j0 < 2);
   }
   u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
   // The barrier keeps the scheduler from hoisting the next block's LDS staging (and its
@@ -642,6 +667,10 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
       }
       kt = lds_buf[wave][2 * st];
       vt = lds_buf[wave][2 * st + 1];
+      if (app && j == jn && lane < CPR) {  // the new token's rows into slot tn
+        *(u32x4*)(kt + tn * PITCH + ((lane ^ kswz(tn)) * 16)) = nk;
+        *(u32x4*)(vt + tn * PITCH + ((lane ^ swz(tn)) * 16)) = nv;
+      }
       if (j * BS + BS > n) {  // V rows at or beyond n become zeros (their bytes may be NaN)
 #pragma unroll
         for (int x = lane; x < TILE / 16; x += 64)
@@ -710,6 +739,14 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
         }
       }
     }
+  }
+  // appending decode, LDS-ring path: the new rows into the cache, after everything that
+  // read the block
+  if (DMA && app && lane < CPR) {
+    const size_t dst = (((size_t)app_phys * a.num_kv_heads + kvh) * BS + tn) * (D * E) +
+                       (size_t)lane * 16;
+    *(u32x4*)((char*)a.k + dst) = nk;
+    *(u32x4*)((char*)a.v + dst) = nv;
   }
 }
 

@@ -267,7 +267,49 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
     }
   };
 
-  auto process = [&](int j, const LT (&kr)[NLD], const LT (&vr)[NLD]) {
+  // Appending decode (the unit that walks the sequence's last block, whose table entry lies
+  // in the pool -- an entry outside it skips the write, as the KV write does): the new
+  // token's rows take slot tn of block jn in place of the loaded bytes, and are stored into
+  // the cache after the unit's epilogue, so no load waits for the store.  Lanes of token
+  // row tn % TPL hold its slice c in load tn / TPL, in the cache's type (e4m3: the code of
+  // x * inv_scale, the conversion the KV write uses).
+  // (The rows are loaded whatever the table entry says; whether the entry lies in the pool
+  // is read from the unit's table slice once it is there, so nothing waits for it here.)
+  const int jn = (n - 1) / BS, tn = (n - 1) % BS;
+  bool app = a.append && a.mode == MODE_PLAIN && n > 0 && j1 == nblk;
+  int app_phys = 0;
+  LT nk{}, nv{};
+  if (app) {
+    const size_t src = ((size_t)s * a.num_kv_heads + kvh) * D + (size_t)c * EPL;
+    const uint16_t* ks = (const uint16_t*)a.k_new + src;
+    const uint16_t* vs = (const uint16_t*)a.v_new + src;
+    if constexpr (F8) {
+      if constexpr (W == 4) {  // 16 codes from 16 source elements
+        const u32x2 k0 = src8_to_e4m3<QK>(((const u32x4*)ks)[0], a.k_inv_scale);
+        const u32x2 k1 = src8_to_e4m3<QK>(((const u32x4*)ks)[1], a.k_inv_scale);
+        const u32x2 v0 = src8_to_e4m3<QK>(((const u32x4*)vs)[0], a.v_inv_scale);
+        const u32x2 v1 = src8_to_e4m3<QK>(((const u32x4*)vs)[1], a.v_inv_scale);
+        nk = LT{k0[0], k0[1], k1[0], k1[1]};
+        nv = LT{v0[0], v0[1], v1[0], v1[1]};
+      } else {  // 8 codes from 8 source elements
+        nk = src8_to_e4m3<QK>(*(const u32x4*)ks, a.k_inv_scale);
+        nv = src8_to_e4m3<QK>(*(const u32x4*)vs, a.v_inv_scale);
+      }
+    } else {
+      nk = *(const LT*)ks;
+      nv = *(const LT*)vs;
+    }
+  }
+
+  auto process = [&](int j, LT (&kr)[NLD], LT (&vr)[NLD]) {
+    if (app && j == jn && r == tn % TPL) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        if (i == tn / TPL) {
+          kr[i] = nk;
+          vr[i] = nv;
+        }
+    }
     if ((j + 1) * BS <= n) consume(std::false_type{}, j, kr, vr);
     else consume(std::true_type{}, j, kr, vr);
   };
@@ -278,13 +320,9 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
   // the block being consumed; the last one or two blocks are peeled off the loop.
   TableSlice ts;
   ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
-  // appending decode: the unit that walks the sequence's last block stores the new token's
-  // row there first (a table entry outside the pool is skipped, as the KV write does)
-  if (a.append && a.mode == MODE_PLAIN && n > 0 && j1 == nblk) {
-    const int raw = __builtin_amdgcn_readlane(ts.ids, (n - 1) / BS - ts.j0);
-    if ((unsigned)raw < (unsigned)a.num_blocks)
-      append_new_row<D, BS, QK, KVK>(a, s, kvh, raw, (n - 1) % BS, lane,
-                                     (n - 1) / BS - j0 < 2);
+  if (app) {
+    app_phys = __builtin_amdgcn_readlane(ts.ids, jn - ts.j0);
+    app = (unsigned)app_phys < (unsigned)a.num_blocks;
   }
   LT ka[NLD], va[NLD], kb[NLD], vb[NLD];
   issue(ts.get(j0), ka, va);
@@ -355,6 +393,13 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
         a.part_ml[pi * 2 + 1] = L;
       }
     }
+  }
+  // appending decode: the new rows into the cache, after everything that read the block
+  if (app && r == tn % TPL) {
+    const size_t dst = (((size_t)app_phys * a.num_kv_heads + kvh) * BS + tn) * (Geo::TILE / BS) +
+                       (size_t)c * Geo::LB;
+    *(LT*)((char*)a.k + dst) = nk;
+    *(LT*)((char*)a.v + dst) = nv;
   }
 }
 
