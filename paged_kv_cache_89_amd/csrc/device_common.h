@@ -231,6 +231,7 @@ __device__ __forceinline__ UnitCoords balanced_coords(const DecodeArgs& a, int w
                                                       int block_size) {
   const int lane = threadIdx.x & 63;
   const int S = a.num_seqs, bpp = a.blocks_per_part, H = a.num_kv_heads;
+  if (S > kBalancedMaxSeqs) return remapped_coords(a, waves, wave, S);
   constexpr int K = kBalancedMaxSeqs / 64;
   // lane's rows s = lane + 64 k: blocks and non-empty partitions
   int nb[K], np[K];
