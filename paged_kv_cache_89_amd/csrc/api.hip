@@ -57,10 +57,14 @@ struct Plan {
 // partitions of `base` tokens keep units long enough to stream efficiently while cutting
 // ragged batches into near-uniform pieces; when that leaves too few units to fill the
 // chip's wave slots (256 CUs), the partition is halved while it stays at least 128 tokens.
-// Measured on MI355X: 768-token partitions beat 512 by 3 % on the GQA workload and
-// 0.5-1 % on the OPT-13B one; the shared-prefix decode keeps 512, which splits its
-// block-aligned prompts evenly (768 measured 4 % slower there).
+// Measured on MI355X: 768-token partitions beat 512 by 0.5-1 % on the OPT-13B workload
+// (and 1024 by 3.5-5 %); grouped queries take 1024 (below); the shared-prefix decode keeps
+// 512, which splits its block-aligned prompts evenly (768 measured 4 % slower there).
 constexpr int32_t kAutoPartition = 768;
+// Grouped queries over 16-token blocks run on the matrix-core kernel, whose row-partitions
+// are spread over the XCDs by their blocks: there 64-block partitions measured 0.55 % faster
+// per GQA step than 768 tokens (0.2 % for four draft tokens; 512 tokens 3-4 % slower).
+constexpr int32_t kAutoPartitionMfma = 1024;
 // 1: matrix-core decodes (grouped queries, multi-token) of at most kBalancedMaxSeqs rows
 // spread the row-partitions over the XCDs by their blocks (balanced_coords); compile-time
 // switch for measurements.  Measured against contiguous ranges of rows, three pairs on one
@@ -104,6 +108,10 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
     return fail(PA_ERR_INVALID_ARG, "decode plan: negative or zero size");
   if (partition_size % block_size != 0)
     return fail(PA_ERR_INVALID_ARG, "decode plan: partition_size must be a multiple of block_size");
+  const int32_t G = num_heads / num_kv_heads;
+  if (base_partition == kAutoPartition && block_size == 16 && (G == 2 || G == 4 || G == 8) &&
+      (head_dim == 64 || head_dim == 128))
+    base_partition = kAutoPartitionMfma;
   int32_t P = partition_size > 0 ? partition_size
                                   : auto_partition(num_seqs, num_kv_heads, max_context_len,
                                                    base_partition, block_size);

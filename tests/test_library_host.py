@@ -139,7 +139,9 @@ def test_decode_plan_and_workspace():
     assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0) == (768, 3)
     assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (2048, 16)
     assert pa.decode_plan(4, 32, 32, 128, 32, 32768, 0) == (768, 43)   # 2048 units only
-    assert pa.decode_plan(128, 32, 8, 128, 16, 8192, 0) == (768, 11)  # below 16 x 768
+    # grouped queries over 16-token blocks (the matrix-core kernel) start from 1024 tokens
+    assert pa.decode_plan(128, 32, 8, 128, 16, 8192, 0) == (1024, 8)
+    assert pa.decode_plan(128, 32, 8, 128, 32, 8192, 0) == (768, 11)  # 32-token blocks: vector
     assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (0, 1)
     assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0) == (192, 11)
     assert pa.decode_plan(16, 8, 8, 64, 16, 8192, 0) == (192, 43)
