@@ -67,8 +67,9 @@ template <> struct LoadVec<4> { using T = u32x4; };
 template <> struct LoadVec<2> { using T = u32x2; };
 
 
-// NT: K/V loads carry the non-temporal hint (data read once per step).
-template <int D, int BS, int QK, int KVK, int G, bool NT>
+// NT: K/V loads carry the non-temporal hint (data read once per step).  APP: the appending
+// decode (a separate instantiation, so the plain decode carries none of its registers).
+template <int D, int BS, int QK, int KVK, int G, bool NT, bool APP>
 __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(const DecodeArgs a) {
   using Geo = TileGeometry<D, BS, KVK>;
   using LT = typename LoadVec<Geo::W>::T;
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
   // (The rows are loaded whatever the table entry says; whether the entry lies in the pool
   // is read from the unit's table slice once it is there, so nothing waits for it here.)
   const int jn = (n - 1) / BS, tn = (n - 1) % BS;
-  bool app = a.append && a.mode == MODE_PLAIN && n > 0 && j1 == nblk;
+  bool app = APP && a.mode == MODE_PLAIN && n > 0 && j1 == nblk;
   int app_phys = 0;
   LT nk{}, nv{};
   if (app) {
@@ -405,8 +406,12 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
 
 template <int D, int BS, int QK, int KVK, int G, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT>), decode_grid(a, PA_DECODE_WAVES), dim3(64 * PA_DECODE_WAVES),
-                     0, stream, a);
+  if (a.append)
+    hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT, true>), decode_grid(a, PA_DECODE_WAVES),
+                       dim3(64 * PA_DECODE_WAVES), 0, stream, a);
+  else
+    hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT, false>), decode_grid(a, PA_DECODE_WAVES),
+                       dim3(64 * PA_DECODE_WAVES), 0, stream, a);
   return hipGetLastError();
 }
 

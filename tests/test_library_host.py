@@ -316,7 +316,9 @@ def test_hot_kernels_use_no_scratch():
     # (four waves per SIMD need <= 128 VGPRs, three <= 168).  The bf16 GQA kernel stages
     # K/V through a two-stage LDS ring (64 KiB per workgroup), which holds it to two waves
     # per SIMD; its registers stay within the four-wave budget.
-    hot = {"_ZN2pa19paged_decode_kernelILi128ELi16ELi0ELi0ELi1ELb1EEEvNS_10DecodeArgsE": 128,
+    hot = {"_ZN2pa19paged_decode_kernelILi128ELi16ELi0ELi0ELi1ELb1ELb0EEEvNS_10DecodeArgsE": 128,
+           # the fp8 shared-prompt per-sequence units (e4m3 cache, bf16 queries)
+           "_ZN2pa19paged_decode_kernelILi128ELi16ELi1ELi2ELi1ELb1ELb0EEEvNS_10DecodeArgsE": 128,
            "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0EEEvNS_10DecodeArgsE": 128,
            # the fp8 shared-prompt prefix units (4 members x 1 head, per-column masks)
            "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi2ELi4ELb1ELb1EEEvNS_10DecodeArgsE": 128}
