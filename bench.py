@@ -138,7 +138,8 @@ def main():
                  + torch.arange(T, dtype=torch.int32, device="cuda").repeat(S)).to(torch.int32)
     max_ctx = int(ctx.max())
     out = torch.empty_like(q)
-    used_P, nparts = pa.decode_plan(S, Hq, Hkv, D, B, max_ctx, P)
+    # the plain and multi-token decodes' split (the flat split for fp16/bf16 caches)
+    used_P, nparts, flat_min = pa.decode_plan(S, Hq, Hkv, D, B, max_ctx, P, kc.dtype)
     ws_bytes = pa.decode_workspace_size(S, Hq, Hkv, D, B, max_ctx, P)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
@@ -251,6 +252,15 @@ def main():
     dec_ms = [a.elapsed_time(b) for a, b in ev]
     dec_ms_mean = float(np.mean(dec_ms))
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    # the flat split's chunk length, as the last decode chose it on the device (the word
+    # after the partials in the workspace)
+    flat_split = None
+    if flat_min and path in ("plain", "multi") and not flags:
+        rows = S * T * Hq
+        off = rows * nparts * (D + 2) * 4
+        chunk, waves = ws[off:off + 8].view(torch.int32).tolist()
+        flat_split = {"min_chunk_blocks": flat_min, "chunk_blocks": chunk, "grid_waves": waves,
+                      "max_partials_per_row": nparts}
     achieved = unique_bytes / (dec_ms_mean * 1e-3) / 1e9
 
     if args.copy_calibration:
@@ -329,15 +339,17 @@ def main():
             "head_dim": D, "block_size": B, "context_lens": f"U[{sp.ctx_lo},{sp.ctx_hi}]"
             + (f"+{sp.prompt_len}" if sp.prompt_len else ""), "num_blocks": sp.num_blocks,
             "q_dtype": sp.q_dtype, "kv_dtype": sp.kv_dtype,
-            "partition_size": used_P if not cascade_plan else None,
-            "num_partitions": nparts if not cascade_plan else None, "kv_bytes_per_step": kv_bytes,
+            "partition_size": used_P if not cascade_plan and not flat_min else None,
+            "num_partitions": nparts if not cascade_plan and not flat_min else None,
+            "kv_bytes_per_step": kv_bytes,
             "unique_kv_bytes_per_step": unique_bytes, "seed": seed,
             "decode_flags": flags, "decode_path": path,
             "step": ("fused: pa_decode_append stores the new tokens and decodes in one call"
                      if fused else "pa_write_kv, then the decode"),
             "block_granular_kv_bytes_per_step": block_bytes,
         } | ({"query_len": T} if path == "multi" else {})
-          | ({"cascade_plan": cascade_plan} if cascade_plan else {}),
+          | ({"cascade_plan": cascade_plan} if cascade_plan else {})
+          | ({"flat_split": flat_split} if flat_split else {}),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),

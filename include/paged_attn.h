@@ -257,7 +257,8 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void
  * The kernel walks the table block by block with the online rescaling of [P1] sec. 7,
  * one pass over K and V ([P3] sec. 3), accumulating in fp32.  Long contexts are cut into
  * partitions of partition_size tokens whose partial (max, sum, output) triples are
- * combined by a second, log-sum-exp merge kernel.
+ * combined by a second, log-sum-exp merge kernel; with partition_size 0, fp16/bf16 caches
+ * and at most 256 sequences the split is instead the flat one pa_decode_plan describes.
  *   out           [num_seqs, num_heads, head_dim] in q_dtype (round to nearest even)
  *   query         [num_seqs, num_heads, head_dim] in q_dtype
  *   k/v_cache     [num_blocks, num_kv_heads, block_size, head_dim] in kv_dtype
@@ -273,7 +274,10 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void
  *                 several sequences of the batch (shared prompts, [P1] sec. 5): K/V loads
  *                 then stay cacheable and sequences are visited together so that a shared
  *                 block is fetched from HBM once; without it K/V loads are streamed with
- *                 the non-temporal hint.  Results are identical either way.
+ *                 the non-temporal hint.  At a given partition_size results are identical
+ *                 either way; under the library's choice the flag keeps fixed partitions
+ *                 (the flat split does not visit sharing sequences together), so results
+ *                 then agree to rounding.
  *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes, 16-byte
  *                 aligned (hipMalloc gives 256); may be NULL when that size is 0.  The
  *                 same holds for every workspace argument below.
@@ -285,12 +289,20 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                 int32_t partition_size);
 
-/* The partition size pa_decode will use for these arguments (0 = no split) and the
- * resulting number of partitions per sequence. */
+/* The split pa_decode (flags 0) will use for these arguments and cache type.  Fixed partitions:
+ * used_partition_size tokens each (0 = no split) and num_partitions of them per sequence;
+ * *flat_min_blocks = 0.  Flat split (the library's choice for fp16/bf16 caches and at most
+ * 256 sequences whose contexts it splits): the blocks of all sequences, one sequence after another, are cut
+ * into equal chunks of at least *flat_min_blocks blocks (the length itself is chosen on the
+ * device from context_lens, so that every wavefront walks the same number of blocks), and
+ * a chunk crossing into the next sequence leaves one partial per sequence; then
+ * used_partition_size = 0 and num_partitions is the most partials a row can have.  Any
+ * output pointer may be NULL. */
 pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t max_context_len,
-                         int32_t partition_size, int32_t* used_partition_size,
-                         int32_t* num_partitions);
+                         int32_t partition_size, pa_dtype kv_dtype,
+                         int32_t* used_partition_size, int32_t* num_partitions,
+                         int32_t* flat_min_blocks);
 
 pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens,
@@ -302,15 +314,17 @@ pa_status pa_decode(void* out, const void* query, const void* k_cache, const voi
                     size_t workspace_bytes, void* stream);
 
 /* No-allocation decode, for callers that cannot allocate device memory (code under HIP
- * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Computes exactly
- * what pa_decode computes, with the same arguments minus the workspace, and launches the
- * same kernels: the partition partials go to a fixed device array of
- * PA_NOALLOC_SCRATCH_BYTES bytes inside the library (one copy per GPU, held until the
- * process ends; its address on the current GPU is looked up on the first call there).  The
- * call allocates nothing.  A plan whose partials need more than that array
- * (pa_decode_workspace_size(...) > PA_NOALLOC_SCRATCH_BYTES, e.g. more than about 64,000
- * (sequence, query head, partition) triples at head_dim 128) returns PA_ERR_UNSUPPORTED
- * before anything is launched; call pa_decode with a workspace instead.  Every call on a
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Computes what
+ * pa_decode computes, with the same arguments minus the workspace, and launches the same
+ * kernels: the partition partials go to a fixed device array of PA_NOALLOC_SCRATCH_BYTES
+ * bytes inside the library (one copy per GPU, held until the process ends; its address on
+ * the current GPU is looked up on the first call there).  The call allocates nothing.  It
+ * takes pa_decode's split, bit for bit the same output, except where the flat split's
+ * partials would not fit the array: then it takes fixed partitions (the same result to
+ * within the decode's tolerance).  A plan whose fixed partitions do not fit either (more
+ * than about 64,000 (sequence, query head, partition) triples at head_dim 128) returns
+ * PA_ERR_UNSUPPORTED before anything is launched; call pa_decode with a workspace
+ * instead.  Every call on a
  * GPU shares that GPU's array, which keeps whatever the last call left there (nothing in
  * it needs to start at zero): calls that overlap on one GPU -- on several streams, or from
  * several host threads -- race on it and must be serialised by the caller.  Errors and

@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
                               c.c_int, c.c_int, f32, f32, vp]
     L.pa_decode_workspace_size.argtypes = [i32] * 7
     L.pa_decode_workspace_size.restype = sz
-    L.pa_decode_plan.argtypes = [i32] * 7 + [vp, vp]
+    L.pa_decode_plan.argtypes = [i32] * 7 + [c.c_int, vp, vp, vp]
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                             f32, c.c_int, c.c_int, f32, f32, i32, c.c_uint32, vp, sz, vp]
     L.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -336,13 +336,19 @@ def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
 
 
 def decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
-                partition_size=0):
-    """(partition size pa_decode will use (0 = no split), partitions per sequence)."""
+                partition_size=0, kv_dtype=F16):
+    """pa_decode_plan: (partition size (0 = no split or the flat split), partial slots per
+    row, shortest chunk of the flat split in blocks (0 = fixed partitions)).  kv_dtype: a
+    dtype code (F16, BF16, FP8_E4M3) or a torch dtype."""
+    if not isinstance(kv_dtype, int):
+        kv_dtype = _dtype_code(_torch().empty(0, dtype=kv_dtype))
     p = np.zeros(1, np.int32)
     n = np.zeros(1, np.int32)
+    f = np.zeros(1, np.int32)
     _check(lib().pa_decode_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                int(max_context_len), int(partition_size), _ptr(p), _ptr(n)))
-    return int(p[0]), int(n[0])
+                                int(max_context_len), int(partition_size), int(kv_dtype),
+                                _ptr(p), _ptr(n), _ptr(f)))
+    return int(p[0]), int(n[0]), int(f[0])
 
 
 def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,

@@ -48,8 +48,9 @@ bool log_enabled() {
 }
 
 struct Plan {
-  int32_t partition_size;  // 0 = whole context in one unit
-  int32_t num_parts;
+  int32_t partition_size;  // 0 = whole context in one unit (or the flat split)
+  int32_t num_parts;       // partial slots per row
+  int32_t flat_min_blocks = 0;  // > 0: flat split with chunks of at least this many blocks
 };
 
 // Library choice of the partition length.  A unit is one wavefront.  Contexts of at most
@@ -100,9 +101,19 @@ int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx, 
   return P;
 }
 
+// Flat split (see launch.h): the library's choice for plain and multi-token decodes of at
+// most kFlatMaxSeqs sequences whose contexts it would split, when the caller leaves the
+// partition size to it.  Every unit then reads the same number of blocks whatever the
+// lengths: measured on MI355X, partitions of unequal length (each sequence's last one
+// short) cost 6-7 % against equal ones on the same bytes.  Chunks are at least
+// kFlatMinBlocks long, which bounds a row's slots at ceil(blocks / kFlatMinBlocks) + 1.
+// 32-token blocks keep fixed partitions: the flat walk would take their vector kernel from
+// three waves per SIMD to two (and their one workload has equal lengths).
+constexpr int32_t kFlatMinBlocks = 16;
+
 pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t max_context_len, int32_t partition_size,
-                    Plan* plan, int32_t base_partition = kAutoPartition) {
+                    Plan* plan, int32_t base_partition = kAutoPartition, bool flat_ok = false) {
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
       max_context_len < 0 || partition_size < 0)
     return fail(PA_ERR_INVALID_ARG, "decode plan: negative or zero size");
@@ -120,9 +131,17 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
   const int64_t cap = (int64_t)kMaxUnitBlocks * block_size;
   if (P == 0 && max_context_len > cap) P = (int32_t)cap;
   if (P > cap) P = (int32_t)cap;
+  plan->flat_min_blocks = 0;
   if (P == 0 || P >= max_context_len) {
     plan->partition_size = 0;
     plan->num_parts = 1;
+  } else if (flat_ok && partition_size == 0 && num_seqs <= kFlatMaxSeqs && block_size <= 16 &&
+             (int64_t)num_seqs * (((int64_t)max_context_len + block_size - 1) / block_size) <
+                 ((int64_t)1 << 26)) {  // the walk's scan keeps block ends in 26 bits
+    const int64_t max_blk = ((int64_t)max_context_len + block_size - 1) / block_size;
+    plan->partition_size = 0;
+    plan->num_parts = (int32_t)((max_blk + kFlatMinBlocks - 1) / kFlatMinBlocks + 1);
+    plan->flat_min_blocks = kFlatMinBlocks;
   } else {
     plan->partition_size = P;
     plan->num_parts = (max_context_len + P - 1) / P;
@@ -130,10 +149,20 @@ pa_status make_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
   return PA_OK;
 }
 
+// Partials: acc [rows, num_parts, D] then (m, l) [rows, num_parts, 2] (fp32); the flat
+// split adds one 16-byte word after them for the chunk length the decode chose.
 size_t workspace_bytes(const Plan& p, int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
-  if (p.num_parts <= 1) return 0;
+  if (p.num_parts <= 1 && p.flat_min_blocks == 0) return 0;
   const size_t rows = (size_t)num_seqs * num_heads * p.num_parts;
-  return rows * head_dim * sizeof(float) + rows * 2 * sizeof(float);
+  return rows * head_dim * sizeof(float) + rows * 2 * sizeof(float) +
+         (p.flat_min_blocks > 0 ? 16 : 0);
+}
+
+// Where the flat split's chunk length sits in a workspace laid out as above.
+int32_t* flat_meta_ptr(const Plan& p, void* workspace, int32_t num_seqs, int32_t num_heads,
+                       int32_t head_dim) {
+  const size_t rows = (size_t)num_seqs * num_heads * p.num_parts;
+  return (int32_t*)((char*)workspace + rows * head_dim * sizeof(float) + rows * 2 * sizeof(float));
 }
 
 // Shared-prefix decode: one partition length P for both launches (pa_decode's choice,
@@ -199,7 +228,8 @@ static pa_status decode_impl(const char* who, void* out, const void* query, cons
                     pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
                     int32_t partition_size, uint32_t flags, void* workspace,
                     size_t workspace_bytes_given, void* stream, const void* k_new,
-                    const void* v_new, float k_inv_scale, float v_inv_scale) {
+                    const void* v_new, float k_inv_scale, float v_inv_scale,
+                    bool flat_ok = true) {
   g_last_error.clear();
   int qk, kk;
   if (!dtype_kind(q_dtype, &qk) || !dtype_kind(kv_dtype, &kk))
@@ -236,7 +266,8 @@ static pa_status decode_impl(const char* who, void* out, const void* query, cons
   // the table's reach find no blocks and exit.
   Plan plan;
   pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, partition_size, &plan);
+                           max_context_len, partition_size, &plan, kAutoPartition,
+                           flat_ok && !shared && kk != KIND_E4M3);
   if (st != PA_OK) return st;
   const size_t need = workspace_bytes(plan, num_seqs, num_heads, head_dim);
   if (need > 0 && (!workspace || workspace_bytes_given < need))
@@ -284,17 +315,22 @@ static pa_status decode_impl(const char* who, void* out, const void* query, cons
   a.append = append ? 1 : 0;
   a.k_new = k_new; a.v_new = v_new;
   a.k_inv_scale = k_inv_scale; a.v_inv_scale = v_inv_scale;
+  a.flat_min_blocks = plan.flat_min_blocks;
+  a.flat_meta = plan.flat_min_blocks > 0
+                    ? flat_meta_ptr(plan, workspace, num_seqs, num_heads, head_dim) : nullptr;
+  if (plan.flat_min_blocks > 0) a.num_slots = plan.num_parts;
   if (log_enabled())
-    std::fprintf(stderr, "[paged_attn] decode S=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d P=%d parts=%d units=%lld\n",
+    std::fprintf(stderr, "[paged_attn] decode S=%d Hq=%d Hkv=%d D=%d B=%d max_ctx=%d P=%d parts=%d units=%lld flat=%d\n",
                  num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
-                 plan.partition_size, plan.num_parts, (long long)units);
+                 plan.partition_size, plan.num_parts, (long long)units, plan.flat_min_blocks);
   st = hip_status(launch_decode(shape, a, (hipStream_t)stream), (std::string(who) + " launch").c_str());
-  if (st != PA_OK || plan.num_parts <= 1) return st;
+  if (st != PA_OK || a.num_slots == 0) return st;
   MergeArgs m;
   m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
   m.num_seqs = num_seqs; m.num_heads = num_heads; m.num_parts = plan.num_parts;
   m.partition_size = plan.partition_size; m.max_ctx = max_ctx;
   m.v_scale = a.v_scale; m.all_slots = 0;
+  m.flat = plan.flat_min_blocks > 0 ? 1 : 0; m.block_size = block_size; m.flat_meta = a.flat_meta;
   return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream), (std::string(who) + " merge launch").c_str());
 }
 
@@ -476,26 +512,36 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, void* dst_k, void
 
 pa_status pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t max_context_len,
-                         int32_t partition_size, int32_t* used_partition_size,
-                         int32_t* num_partitions) {
+                         int32_t partition_size, pa_dtype kv_dtype,
+                         int32_t* used_partition_size, int32_t* num_partitions,
+                         int32_t* flat_min_blocks) {
   g_last_error.clear();
+  int kk;
+  if (!dtype_kind(kv_dtype, &kk)) return fail(PA_ERR_INVALID_ARG, "pa_decode_plan: unknown dtype");
   Plan p;
   const pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                 max_context_len, partition_size, &p);
+                                 max_context_len, partition_size, &p, kAutoPartition,
+                                 kk != KIND_E4M3);
   if (st != PA_OK) return st;
   if (used_partition_size) *used_partition_size = p.partition_size;
   if (num_partitions) *num_partitions = p.num_parts;
+  if (flat_min_blocks) *flat_min_blocks = p.flat_min_blocks;
   return PA_OK;
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                 int32_t partition_size) {
-  Plan p;
+  // Enough for either split pa_decode may take: the flat split, or fixed partitions
+  // (PA_DECODE_SHARED_KV, e4m3 caches).
+  Plan flat, fixed;
   if (make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
-                partition_size, &p) != PA_OK)
+                partition_size, &flat, kAutoPartition, true) != PA_OK ||
+      make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                partition_size, &fixed) != PA_OK)
     return 0;
-  return workspace_bytes(p, num_seqs, num_heads, head_dim);
+  return std::max(workspace_bytes(flat, num_seqs, num_heads, head_dim),
+                  workspace_bytes(fixed, num_seqs, num_heads, head_dim));
 }
 
 pa_status pa_decode(void* out, const void* query, const void* k_cache, const void* v_cache,
@@ -525,10 +571,22 @@ pa_status pa_decode_noalloc(void* out, const void* query, const void* k_cache,
   const char* who = "pa_decode_noalloc";
   // The same plan pa_decode makes (and pa_decode_workspace_size sizes); refused before
   // anything else when its partials do not fit the fixed array.
+  // The flat split where its partials fit the array, else fixed partitions.
+  int kk;
+  if (!dtype_kind(kv_dtype, &kk)) return fail(PA_ERR_INVALID_ARG, std::string(who) + ": unknown dtype");
+  const bool shared = (flags & PA_DECODE_SHARED_KV) != 0;
+  bool flat_ok = !shared && kk != KIND_E4M3;
   Plan plan;
   pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, partition_size, &plan);
+                           max_context_len, partition_size, &plan, kAutoPartition, flat_ok);
   if (st != PA_OK) return st;
+  if (plan.flat_min_blocks > 0 &&
+      workspace_bytes(plan, num_seqs, num_heads, head_dim) > (size_t)PA_NOALLOC_SCRATCH_BYTES) {
+    flat_ok = false;
+    st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                   partition_size, &plan);
+    if (st != PA_OK) return st;
+  }
   const size_t need = workspace_bytes(plan, num_seqs, num_heads, head_dim);
   if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
     return fail(PA_ERR_UNSUPPORTED, std::string(who) + ": the partition partials need " +
@@ -544,7 +602,7 @@ pa_status pa_decode_noalloc(void* out, const void* query, const void* k_cache,
                      num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, scale, q_dtype, kv_dtype, k_scale, v_scale,
                      partition_size, flags, ws, ws ? (size_t)PA_NOALLOC_SCRATCH_BYTES : 0,
-                     stream, nullptr, nullptr, 1.0f, 1.0f);
+                     stream, nullptr, nullptr, 1.0f, 1.0f, flat_ok);
 }
 
 pa_status pa_decode_append(void* out, const void* query, const void* k_new, const void* v_new,
@@ -719,11 +777,16 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
 size_t pa_decode_multi_workspace_size(int32_t num_seqs, int32_t query_len, int32_t num_heads,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                       int32_t max_context_len, int32_t partition_size) {
-  Plan p;
-  if (query_len < 1 || make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                 max_context_len, partition_size, &p) != PA_OK)
+  // Enough for either split pa_decode_multi may take (see pa_decode_workspace_size).
+  Plan flat, fixed;
+  if (query_len < 1 ||
+      make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                partition_size, &flat, kAutoPartition, true) != PA_OK ||
+      make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                partition_size, &fixed) != PA_OK)
     return 0;
-  return workspace_bytes(p, num_seqs * query_len, num_heads, head_dim);
+  return std::max(workspace_bytes(flat, num_seqs * query_len, num_heads, head_dim),
+                  workspace_bytes(fixed, num_seqs * query_len, num_heads, head_dim));
 }
 
 pa_status pa_decode_multi(void* out, const void* query, const void* k_cache, const void* v_cache,
@@ -766,7 +829,8 @@ pa_status pa_decode_multi(void* out, const void* query, const void* k_cache, con
   const int32_t max_ctx = (int32_t)(max_context_len < reach ? max_context_len : reach);
   Plan plan;
   pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                           max_context_len, partition_size, &plan);
+                           max_context_len, partition_size, &plan, kAutoPartition,
+                           !shared && kk != KIND_E4M3);
   if (st != PA_OK) return st;
   const int32_t qrows = num_seqs * query_len;  // rows of [S, T] query tokens
   const size_t need = workspace_bytes(plan, qrows, num_heads, head_dim);
@@ -806,13 +870,18 @@ pa_status pa_decode_multi(void* out, const void* query, const void* k_cache, con
   a.mode = MODE_MULTI;
   a.seq_group = 1; a.num_groups = num_seqs; a.max_prefix_blocks = 0; a.prefix_blocks = nullptr;
   a.query_len = query_len; a.tree_masks = tree_masks;
+  a.flat_min_blocks = plan.flat_min_blocks;
+  a.flat_meta = plan.flat_min_blocks > 0
+                    ? flat_meta_ptr(plan, workspace, qrows, num_heads, head_dim) : nullptr;
+  if (plan.flat_min_blocks > 0) a.num_slots = plan.num_parts;
   st = hip_status(launch_decode_gqa_mfma(shape, a, (hipStream_t)stream), "pa_decode_multi launch");
-  if (st != PA_OK || plan.num_parts <= 1) return st;
+  if (st != PA_OK || a.num_slots == 0) return st;
   MergeArgs m;
   m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
   m.num_seqs = num_seqs; m.num_heads = query_len * num_heads; m.num_parts = plan.num_parts;
   m.partition_size = plan.partition_size; m.max_ctx = max_ctx;
   m.v_scale = a.v_scale; m.all_slots = 0;
+  m.flat = plan.flat_min_blocks > 0 ? 1 : 0; m.block_size = block_size; m.flat_meta = a.flat_meta;
   return hip_status(launch_merge(head_dim, qk, m, (hipStream_t)stream), "pa_decode_multi merge launch");
 }
 
@@ -833,6 +902,28 @@ bool decode_supported(const DecodeShape& s) {
   return s.kv_kind == s.q_kind || s.kv_kind == KIND_E4M3;
 }
 
+
+int resident_workgroups(const void* kernel, int threads, std::atomic<int>* cache) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const bool cached = dev >= 0 && dev < kMaxCachedDevices && cache;
+  if (cached) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) {
+    (void)hipGetLastError();  // a failed query must not surface as the launch's error
+    per_cu = 1;
+  }
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    cus = 1;
+  }
+  const int r = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  if (cached) cache[dev].store(r, std::memory_order_relaxed);
+  return r;
+}
 
 // Grouped-query shapes with 16-token blocks run the matrix-core kernel (fp16/bf16 caches on
 // the 16-bit MFMA, e4m3 caches on the fp8 MFMA); every other shape runs the vector kernel.

@@ -225,7 +225,7 @@ constexpr int gqa_min_waves(int kvk, bool lane, int g) {
                           : (PA_LDS_DMA_16 != 0 ? 2 : PA_GQA_MIN_WAVES);
 }
 
-template <int D, int QK, int KVK, int G, bool NT, bool LANE>
+template <int D, int QK, int KVK, int G, bool NT, bool LANE, bool FLAT>
 __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) void paged_decode_gqa_mfma_kernel(
     const DecodeArgs a) {
   constexpr int BS = 16;
@@ -280,484 +280,580 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
   const bool prefix = LANE && a.mode == MODE_PREFIX;
   const bool multi = LANE && a.mode == MODE_MULTI;
   const int rows = prefix ? a.num_groups : a.num_seqs;
-  const UnitCoords uc = unit_coords(a, PA_GQA_WAVES, wave, rows, BS);
-  if (!uc.ok) return;
-  const int s = uc.s, kvh = uc.kvh, part = uc.part;  // s: the sequence, or in prefix mode the group
   const int r = lane >> 4;
   const int c = lane & 15;
-  // Query column cc < G of the unit reads and writes row row_of(cc) of the [rows, D]
-  // query / output arrays.  Plain and suffix units: the G heads of sequence s that share
-  // KV head kvh.  Prefix units: head cc % Gr of member cc / Gr of group s; multi-token
-  // units: head cc % Gr of query token cc / Gr of sequence s (Gr = query heads per KV
-  // head; G = Gr * members or Gr * query tokens).
+  // Query column cc < G of a unit of sequence (or group) s and KV head kvh reads and writes
+  // row row_at(s, kvh, cc) of the [rows, D] query / output arrays.  Plain and suffix units:
+  // the G heads of sequence s that share KV head kvh.  Prefix units: head cc % Gr of member
+  // cc / Gr of group s; multi-token units: head cc % Gr of query token cc / Gr of sequence
+  // s (Gr = query heads per KV head; G = Gr * members or Gr * query tokens).
   const int Gr = a.num_heads / a.num_kv_heads;
   const int outer_n = prefix ? a.seq_group : a.query_len;
-  auto row_of = [&](int cc) -> size_t {
+  auto row_at = [&](int s_, int kvh_, int cc) -> size_t {
     if (LANE && (prefix || multi))
-      return ((size_t)s * outer_n + cc / Gr) * a.num_heads + kvh * Gr + cc % Gr;
-    return (size_t)s * a.num_heads + kvh * G + cc;
+      return ((size_t)s_ * outer_n + cc / Gr) * a.num_heads + kvh_ * Gr + cc % Gr;
+    return (size_t)s_ * a.num_heads + kvh_ * G + cc;
   };
   auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > a.max_ctx ? a.max_ctx : v); };
-  // n: tokens the unit's block range covers; jb: first block of the walk.  Column c
-  // sees token t iff t < lo or (t < hi and bit t - lo of tm is set).
-  int n, jb = 0, lo = 0, hi = 0;
-  uint32_t tm = 0;
-  const int32_t* table_row;
-  if (prefix) {
-    n = 0;
-    for (int k = 0; k < a.seq_group; ++k)
-      n = max(n, prefix_tokens(a, s, BS, clamp_len(a.ctx[s * a.seq_group + k])));
-    lo = hi = (c < G) ? prefix_tokens(a, s, BS, clamp_len(a.ctx[s * a.seq_group + c / Gr])) : 0;
-    table_row = a.tables + (size_t)s * a.seq_group * a.max_blocks;  // the group's first member
-  } else {
-    n = clamp_len(a.ctx[s]);
-    if (multi) {
-      const int t = c / Gr;
-      lo = (c < G) ? n - a.query_len : 0;
-      hi = (c < G) ? n : 0;
-      tm = (c >= G) ? 0u
-           : a.tree_masks ? a.tree_masks[(size_t)s * a.query_len + t]
-                          : (uint32_t)((2ull << t) - 1);
-    } else {
-      lo = hi = (c < G) ? n : 0;
-    }
-    if (a.mode == MODE_SUFFIX) jb = (prefix_tokens(a, s / a.seq_group, BS, n) + BS - 1) / BS;
-    table_row = a.tables + (size_t)s * a.max_blocks;
-  }
-  const int nblk = (n + BS - 1) / BS;
-  const int bpp = part_share_blocks(a, jb, nblk);
-  const int j0 = jb + part * bpp;
-  const int j1 = min(nblk, j0 + bpp);
-
-  if (j0 >= j1) {
-    if (a.num_slots == 0) {  // direct output of an n == 0 sequence: zero rows
-      for (int cc = 0; cc < G; ++cc) {
-        uint16_t* o = (uint16_t*)a.out + row_of(cc) * D;
-        for (int e = lane; e < D; e += 64) o[e] = 0;
-      }
-    } else if (a.mode != MODE_PLAIN && r == 0 && c < G) {  // empty slot of a cascade row
-      const size_t pi = row_of(c) * a.num_slots + a.slot_base + part;
-      a.part_ml[pi * 2] = -INFINITY;
-      a.part_ml[pi * 2 + 1] = 0.f;
-    }
-    return;
-  }
-
-  // The query's loads go out together with the table-slice load (neither depends on the
-  // other), and the first block's loads before the query is converted: those latencies
-  // hide the unit's set-up.  Lane (r, c) loads head c's elements (zeros for c >= G):
-  // dims QD*r .. +QD for the e4m3 contraction, dims 32kk + 8r .. +8 otherwise.
+  // Lane (r, c) loads head c's query elements (zeros for c >= G): dims QD*r .. +QD for the
+  // e4m3 contraction, dims 32kk + 8r .. +8 otherwise.
   constexpr int QL = NATIVE ? QD / 8 : KSTEPS;  // 16-byte query loads per lane
-  u32x4 qraw[QL];
-  if (c < G) {
-    const uint16_t* qrow = (const uint16_t*)a.q + row_of(c) * D;
+  auto load_query = [&](int s_, int kvh_, u32x4 (&qr)[QL]) {
+    if (c < G) {
+      const uint16_t* qrow = (const uint16_t*)a.q + row_at(s_, kvh_, c) * D;
 #pragma unroll
-    for (int k = 0; k < QL; ++k)
-      qraw[k] = *(const u32x4*)(qrow + (NATIVE ? QD * r + 8 * k : 32 * k + 8 * r));
-  } else {
-#pragma unroll
-    for (int k = 0; k < QL; ++k) qraw[k] = u32x4{0, 0, 0, 0};
-  }
-  const size_t blk_stride = (size_t)a.num_kv_heads * STILE;
-  const char* kbase = (const char*)a.k + (size_t)kvh * STILE;
-  const char* vbase = (const char*)a.v + (size_t)kvh * STILE;
-  const uint32_t voff = (uint32_t)lane * 16;  // natural 1 KiB wave loads (K and V)
-  auto load_tile = [&](const char* base, int phys, u32x4 (&t)[NLDS]) {
-    const char* p = base + (size_t)phys * blk_stride;
-#pragma unroll
-    for (int i = 0; i < NLDS; ++i) {
-      if constexpr (NT) t[i] = __builtin_nontemporal_load((const u32x4*)(p + voff + 1024 * i));
-      else t[i] = *(const u32x4*)(p + voff + 1024 * i);
-    }
-  };
-  TableSlice ts;
-  ts.init(table_row, j0, j1, a.num_blocks, lane);
-  // Appending decode (the unit that walks the sequence's last block, whose table entry lies
-  // in the pool -- an entry outside it skips the write, as the KV write does).  LDS-ring
-  // path: once block jn has landed, lane x < CPR writes 16-byte chunk x of the new K and V
-  // rows (in the cache's type: e4m3 codes of x * inv_scale, the KV write's conversion)
-  // into slot tn of the staged tiles, and the rows go to the cache after the epilogue, so
-  // no load waits for the store.  Register path: the rows are stored first.
-  const int jn = (n - 1) / BS, tn = (n - 1) % BS;
-  bool app = a.append && a.mode == MODE_PLAIN && n > 0 && j1 == (n + BS - 1) / BS;
-  int app_phys = 0;
-  u32x4 nk = u32x4{0, 0, 0, 0}, nv = u32x4{0, 0, 0, 0};
-  if constexpr (DMA) {
-    if (app && lane < CPR) {  // loaded whatever the table entry says (checked below)
-      const size_t src = ((size_t)s * a.num_kv_heads + kvh) * D + (size_t)lane * (16 / LE);
-      const u32x4* ks = (const u32x4*)((const uint16_t*)a.k_new + src);
-      const u32x4* vs = (const u32x4*)((const uint16_t*)a.v_new + src);
-      if constexpr (LE == 1) {
-        const u32x2 k0 = src8_to_e4m3<QK>(ks[0], a.k_inv_scale), k1 = src8_to_e4m3<QK>(ks[1], a.k_inv_scale);
-        const u32x2 v0 = src8_to_e4m3<QK>(vs[0], a.v_inv_scale), v1 = src8_to_e4m3<QK>(vs[1], a.v_inv_scale);
-        nk = u32x4{k0[0], k0[1], k1[0], k1[1]};
-        nv = u32x4{v0[0], v0[1], v1[0], v1[1]};
-      } else {
-        nk = ks[0];
-        nv = vs[0];
-      }
-    }
-  }
-  if (app) {
-    app_phys = __builtin_amdgcn_readlane(ts.ids, jn - ts.j0);
-    app = (unsigned)app_phys < (unsigned)a.num_blocks;
-  }
-  if constexpr (!DMA) {
-    if (app) append_new_row<D, BS, QK, KVK>(a, s, kvh, app_phys, tn, lane, jn - j0 < 2);
-  }
-  u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
-  // The barrier keeps the scheduler from hoisting the next block's LDS staging (and its
-  // wait for that block's loads) above these loads: the loads of block j+1 must be in
-  // flight before the wave waits for block j.
-  auto fetch = [&](int jj, u32x4 (&kr)[NLDS], u32x4 (&vr)[NLDS]) {
-    const int p = ts.get(jj);
-    load_tile(kbase, p, kr);
-    load_tile(vbase, p, vr);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // LDS-ring path: block j sits in stage (j - j0) mod 2.  Byte 16 * lane of 1 KiB piece i
-  // of a tile is row i * TPLS + lane / LPTS, chunk lane % LPTS, which must hold the row's
-  // chunk (lane % LPTS) ^ kswz(row) (K) or ^ swz(row) (V) of the swizzled layouts: that is
-  // what the lane fetches, so the wave still reads whole 1 KiB pieces.
-  uint32_t goffk[NLDS], goffv[NLDS];
-#pragma unroll
-  for (int i = 0; i < NLDS; ++i) {
-    const int row = i * TPLS + lane / LPTS;
-    const uint32_t base = i * 1024 + (lane / LPTS) * (D * E);
-    goffk[i] = base + (((lane % LPTS) ^ kswz(row)) * 16);
-    goffv[i] = base + (((lane % LPTS) ^ swz(row)) * 16);
-  }
-  auto issue = [&](int jj, int st) {
-    const size_t boff = (size_t)ts.get(jj) * blk_stride;
-    const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st]));
-    const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st + 1]));
-#pragma unroll
-    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(kbase + boff + goffk[i], kl + 1024 * i);
-#pragma unroll
-    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>(vbase + boff + goffv[i], vl + 1024 * i);
-  };
-  if constexpr (DMA) issue(j0, 0);
-  else fetch(j0, ka, va);
-
-  // Q^T operand: lane (r, c) holds head c's dims 32kk + 8r .. +8 (zero for padding heads)
-  u32x4 qop[NATIVE ? 1 : KSTEPS];
-  // native: head c's dims QD*r .. +QD as three e4m3 terms (zero for padding heads), and
-  // the E8M0 exponent 127 - e of the operand scale 2^-e that undoes the head's 2^e
-  v8i qn[NATIVE ? 3 : 1];
-  int q_exp = 127;
-  if constexpr (NATIVE) {
-    float qv[QD];
-#pragma unroll
-    for (int k = 0; k < QD / 8; ++k) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        qv[8 * k + 2 * w] = (QK == KIND_BF16) ? bf16_lo(qraw[k][w]) : f16_lo(qraw[k][w]);
-        qv[8 * k + 2 * w + 1] = (QK == KIND_BF16) ? bf16_hi(qraw[k][w]) : f16_hi(qraw[k][w]);
-      }
-    }
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < QD; ++i) mx = fmaxf(mx, fabsf(qv[i]));
-    mx = rows_max(mx);
-    // mx in [2^(x-1), 2^x) -> scale by 2^(8-x): the largest element lands in [128, 256)
-    int e = (mx > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(mx) : 0;
-    e = e > 127 ? 127 : e;
-    q_exp = 127 - e;
-#pragma unroll
-    for (int t = 0; t < 3; ++t) qn[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int w = 0; w < QD / 4; ++w) {
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = __builtin_amdgcn_ldexpf(qv[4 * w + i], e);
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {  // each term takes the rounding residual of the last
-        const uint32_t code = e4m3x4_pack(x[0], x[1], x[2], x[3]);
-        qn[t][w] = (int)code;
-        float back[4];
-        e4m3x4_to_f32(code, back);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] -= back[i];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) qop[kk] = qraw[kk];
-  }
-
-  // Output accumulators (matrix-core C operands) hold P . V relative to the reference
-  // maximum; they are rescaled only when the reference moves.
-  f32x4 cacc[NTILES];
-#pragma unroll
-  for (int t = 0; t < NTILES; ++t) cacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // reference maximum of head c (log2 units), same in its 4 lanes
-  float l_part = 0.f;       // this lane's share of head c's denominator
-
-  uint8_t* kt = lds_buf[wave][0];
-  uint8_t* vt = lds_buf[wave][1];
-  const float qk_scale = a.qk_scale;
-  // This lane's share of a tile: wave load i, token row i*TPLS + lane/LPTS, elements
-  // (lane % LPTS) * EPLS .. +EPLS, i.e. LDS chunks (lane % LPTS) * CPL .. +CPL of that row.
-  // K's chunk x of row t sits at x ^ kswz(t): the operand reads (row c, one chunk) of 16
-  // lanes hit 16 different bank groups.  V's chunk x sits at x ^ swz(t).
-  uint32_t kw_off[NLDS][CPL], vw_off[NLDS][CPL];
-#pragma unroll
-  for (int i = 0; i < NLDS; ++i) {
-    const int row = i * TPLS + lane / LPTS;
-#pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-      const int chunk = (lane % LPTS) * CPL + q;
-      kw_off[i][q] = row * PITCH + ((chunk ^ kswz(row)) * 16);
-      vw_off[i][q] = row * PITCH + ((chunk ^ swz(row)) * 16);
-    }
-  }
-  const int trow = 4 * r + c / 4;
-
-  // widen (e4m3) and write one tile into LDS; rows at or beyond n become zeros when
-  // `mask` (their bytes may be NaN and the matrix core would turn 0 * NaN into NaN)
-  auto stage = [&](uint8_t* dst, const uint32_t (&off)[NLDS][CPL], bool mask, int j,
-                   const u32x4 (&t)[NLDS]) {
-#pragma unroll
-    for (int i = 0; i < NLDS; ++i) {
-      u32x4 w[CPL];
-      if constexpr (NATIVE) {
-        w[0] = t[i];
-      } else if constexpr (KVK == KIND_E4M3) {
-        u32x4 two[2];
-        e4m3x16_widen<QK>(t[i], two);
-        w[0] = two[0];
-        w[CPL - 1] = two[1];
-      } else {
-        w[0] = t[i];
-      }
-      const bool dead = mask && j * BS + i * TPLS + lane / LPTS >= n;
-#pragma unroll
-      for (int q = 0; q < CPL; ++q) *(u32x4*)(dst + off[i][q]) = dead ? u32x4{0, 0, 0, 0} : w[q];
-    }
-  };
-
-  // logits of block j: C[token 4r+i][head c]
-  auto logits = [&]() {
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (NATIVE) {
-      // K's operand: token c, the same dims QD*r .. +QD that lane (r, c) holds of Q
-      const uint8_t* row = kt + c * PITCH;
-      const u32x4 lo = *(const u32x4*)(row + ((((QD / 16) * r) ^ kswz(c)) * 16));
-      u32x4 hi = u32x4{0, 0, 0, 0};
-      if constexpr (QD == 32) hi = *(const u32x4*)(row + (((2 * r + 1) ^ kswz(c)) * 16));
-      const v8i kop = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-#pragma unroll
-      for (int t = 0; t < 3; ++t) sc = mfma_e4m3(kop, qn[t], sc, 127, q_exp);
+      for (int k = 0; k < QL; ++k)
+        qr[k] = *(const u32x4*)(qrow + (NATIVE ? QD * r + 8 * k : 32 * k + 8 * r));
     } else {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int chunk = (4 * kk + r) ^ kswz(c);
-        const u32x4 kop = *(const u32x4*)(kt + c * PITCH + chunk * 16);
-        sc = Ops::qk(kop, qop[kk], sc);
-      }
-    }
-    return sc;
-  };
-
-  // online-softmax weights and P . V for block j (MASK: the block holds slots >= n)
-  auto finish = [&](int j, f32x4 sv) {
-    float z[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = j * BS + 4 * r + i;
-      const bool ok = LANE ? (t < lo || (t < hi && ((tm >> ((t - lo) & 31)) & 1u)))
-                           : (c < G && t < n);
-      z[i] = ok ? sv[i] * qk_scale : -INFINITY;
-    }
-    float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    bm = rows_max(bm);
-    const bool move = bm > m_ref + kLazyRescaleLog2;  // false for padding heads (bm = -inf)
-    if (__builtin_amdgcn_ballot_w64(move)) {
-      const float mn = move ? bm : m_ref;
-      const float f = move ? ((m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - mn)) : 1.f;
-      l_part *= f;
-      m_ref = mn;
-      // accumulator row 4r + i belongs to head 4r + i, whose factor sits in lane 4r + i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float fi = __shfl(f, 4 * r + i);
-#pragma unroll
-        for (int t = 0; t < NTILES; ++t) cacc[t][i] *= fi;
-      }
-    }
-    const float ms = (m_ref == -INFINITY) ? 0.f : m_ref;
-    if constexpr (NATIVE) {
-      // weights 2^(z - ms) <= 2^8, lifted by 2^kb so the block's largest is in [2^7, 2^8)
-      const float rel = bm - ms;
-      int kb = 0;
-      if (rel > -INFINITY) {
-        kb = 7 - (int)floorf(rel);
-        kb = kb > 126 ? 126 : kb;
-      }
-      float p[4], pp[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(z[i] - ms);
-        pp[i] = __builtin_amdgcn_ldexpf(p[i], kb);  // exact
-      }
-      const uint32_t hi = e4m3x4_pack(pp[0], pp[1], pp[2], pp[3]);
-      float back[4];
-      e4m3x4_to_f32(hi, back);
-      const uint32_t lo = e4m3x4_pack(pp[0] - back[0], pp[1] - back[1], pp[2] - back[2],
-                                      pp[3] - back[3]);
-      // P's operand: head c, tokens 4r .. 4r+3 as hi then lo; V's operand repeats those
-      // four tokens so both halves meet the same values; the A-operand scale 2^-kb undoes
-      // the lift.  The operands carry 8 codes of the 32 the instruction takes (the rest
-      // zero); issuing one tile at a time keeps a single zero-padded V operand live (about
-      // 30 fewer VGPRs at D = 128 than letting the compiler build all eight up front).
-      const v8i pop8 = v8i{(int)hi, (int)lo, 0, 0, 0, 0, 0, 0};
-      l_part += (p[0] + p[1]) + (p[2] + p[3]);
-      const int rho = 4 * r + ((c >> 1) & 3);
-#pragma unroll
-      for (int t = 0; t < NTILES; ++t) {
-        const v2i vv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_v2i*)(vt + rho * PITCH + ((t ^ swz(rho)) * 16) + 8 * (c & 1)));
-        const v8i vop = v8i{vv[0], vv[1], 0, 0, 0, 0, 0, 0};
-        cacc[t] = mfma_e4m3(pop8, vop, cacc[t], 127 - kb, 127);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      return;
-    }
-    float p[4], rp[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - ms);
-    const uint32_t p01 = Ops::pack2(p[0], p[1], &rp[0], &rp[1]);
-    const uint32_t p23 = Ops::pack2(p[2], p[3], &rp[2], &rp[3]);
-    const u32x2 pop = u32x2{p01, p23};
-    // A weight rounded to the operand type is off by up to 2^-9 (bf16) or 2^-12 (fp16) of
-    // itself, which a few dominant tokens with distant values turn into output errors of
-    // the order of the 2e-3 bar.  So P goes in as hi + lo (the second MFMA takes the
-    // rounding residual, exact to about 2^-17 / 2^-23) and the denominator sums the
-    // unrounded weights.
-    float unused[4];
-    const u32x2 plo = u32x2{Ops::pack2(p[0] - rp[0], p[1] - rp[1], &unused[0], &unused[1]),
-                            Ops::pack2(p[2] - rp[2], p[3] - rp[3], &unused[2], &unused[3])};
-    l_part += (p[0] + p[1]) + (p[2] + p[3]);
-    // P . V over the 16 tokens, one 16-wide slice of the head dimension at a time
-#pragma unroll
-    for (int t = 0; t < NTILES; ++t) {
-      const uint32_t chunk = (2 * t + (c % 4) / 2) ^ swz(trow);
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(vt + trow * PITCH + chunk * 16 + 8 * (c % 2)));
-      cacc[t] = Ops::pv(pop, vb, cacc[t]);
-      cacc[t] = Ops::pv(plo, vb, cacc[t]);
+      for (int k = 0; k < QL; ++k) qr[k] = u32x4{0, 0, 0, 0};
     }
   };
+  // multi-token units: the draft positions query column c sees
+  auto load_mask = [&](int s_) -> uint32_t {
+    const int t = c / Gr;
+    return (c >= G) ? 0u
+           : a.tree_masks ? a.tree_masks[(size_t)s_ * a.query_len + t]
+                          : (uint32_t)((2ull << t) - 1);
+  };
 
-  // Pipeline (register path): two register sets of K and V tiles, as in the vector kernel;
-  // consuming block j moves K(j) and V(j) into the LDS tiles, runs the logit contraction,
-  // the softmax update and P . V.  The mask of slots >= n is applied branch-free (it only
-  // bites in a unit's last block).
-  if constexpr (DMA) {
-    constexpr int PER = 2 * NLDS;  // vector-memory operations per block
-    int st = 0;
-    for (int j = j0; j < j1; ++j) {
-      // fill the other stage (read by block j - 1) with block j + 1, then wait for block j
-      if (j + 1 < j1) {
-        issue(j + 1, st ^ 1);
-        wait_vmcnt<PER>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      kt = lds_buf[wave][2 * st];
-      vt = lds_buf[wave][2 * st + 1];
-      if (app && j == jn && lane < CPR) {  // the new token's rows into slot tn
-        *(u32x4*)(kt + tn * PITCH + ((lane ^ kswz(tn)) * 16)) = nk;
-        *(u32x4*)(vt + tn * PITCH + ((lane ^ swz(tn)) * 16)) = nv;
-      }
-      if (j * BS + BS > n) {  // V rows at or beyond n become zeros (their bytes may be NaN)
-#pragma unroll
-        for (int x = lane; x < TILE / 16; x += 64)
-          if (j * BS + x / CPR >= n) *(u32x4*)(vt + x * 16) = u32x4{0, 0, 0, 0};
-      }
-      finish(j, logits());
-      st ^= 1;
-    }
+  // Work: the one unit of unit_coords, or under the flat split (plain and multi-token
+  // decodes) this wavefront's walk.  The walk loads the next segment's set-up (table slice,
+  // query, draft masks) while the current segment streams, right behind the
+  // current segment's first block, so a segment starts by requesting its first block.
+  constexpr bool flat = FLAT;  // plain and multi-token decodes only (never prefix units)
+  FlatWalk walk;
+  FlatSeg nx{0, 0, 0, 0, 0, 0};
+  bool nx_ok = false;
+  using Slice = std::conditional_t<FLAT, TableSlice2, TableSlice>;
+  Slice nx_ts;
+  u32x4 nx_q[QL];
+  uint32_t nx_tm = 0;
+  auto prefetch = [&]() {
+    nx_ok = walk.next(nx);
+    if (!nx_ok) return;
+    nx_ts.init(a.tables + (size_t)nx.s * a.max_blocks, nx.j0, nx.j1, a.num_blocks, lane);
+    load_query(nx.s, nx.kvh, nx_q);
+    if (multi) nx_tm = load_mask(nx.s);
+  };
+  bool pre_issued = false;  // the segment's first block went out before the last one's partials
+  UnitCoords uc{0, 0, 0, true};
+  if constexpr (flat) {
+    walk.init(a, BS, PA_GQA_WAVES, wave, lane);
+    prefetch();
   } else {
-    // A block's registers are free once it sits in LDS, so the block two ahead is fetched
-    // into them before the block's contractions run: two blocks stay in flight while one
-    // is consumed.  Steady state: blocks j .. j+3 exist, ka/va hold block j and kb/vb
-    // block j + 1, and every load in the loop is unconditional (see the vector kernel).
-    auto stage_kv = [&](int j, const u32x4 (&kr)[NLDS], const u32x4 (&vr)[NLDS]) {
-      stage(kt, kw_off, false, j, kr);
-      stage(vt, vw_off, true, j, vr);
-    };
-    int j = j0;
-    if (j + 1 < j1) fetch(j + 1, kb, vb);
-    while (j + 3 < j1) {
-      stage_kv(j, ka, va);
-      fetch(j + 2, ka, va);
-      finish(j, logits());
-      stage_kv(j + 1, kb, vb);
-      fetch(j + 3, kb, vb);
-      finish(j + 1, logits());
-      j += 2;
-    }
-    // one to three blocks left: ka/va hold block j, kb/vb block j + 1 when it exists
-    stage_kv(j, ka, va);
-    if (j + 2 < j1) fetch(j + 2, ka, va);
-    finish(j, logits());
-    if (j + 1 < j1) {
-      stage_kv(j + 1, kb, vb);
-      finish(j + 1, logits());
-    }
-    if (j + 2 < j1) {
-      stage_kv(j + 2, ka, va);
-      finish(j + 2, logits());
-    }
+    uc = unit_coords(a, PA_GQA_WAVES, wave, rows, BS);
+    if (!uc.ok) return;
   }
-
-  // head c's denominator: sum of its four lanes' shares
-  const float L = rows_sum(l_part);
-  // accumulator row 4r + i (lane c holds dim 16t + c of slice t) belongs to head 4r + i
+  // (one pass over the unit without the flat split: the trip count stays in the loop
+  // condition, where the compiler sees it)
+  for (int iter = 0; flat || iter < 1; ++iter) {
+    int s, kvh, j0, j1, slot;  // s: the sequence, or in prefix mode the group
+    // n: tokens the unit's block range covers; jb: first block of the walk.  Column c
+    // sees token t iff t < lo or (t < hi and bit t - lo of tm is set).
+    int n, jb = 0, lo = 0, hi = 0;
+    uint32_t tm = 0;
+    Slice ts;
+    u32x4 qraw[QL];
+    if constexpr (flat) {
+      if (!nx_ok) break;
+      s = nx.s;
+      kvh = nx.kvh;
+      j0 = nx.j0;
+      j1 = nx.j1;
+      slot = nx.slot;
+      n = nx.n;
+      tm = nx_tm;
+      ts = nx_ts;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * r + i;
-    const float Li = __shfl(L, hh);
-    const float Mi = __shfl(m_ref, hh);
-    if (hh < G) {
-      if (a.num_slots == 0) {
-        uint16_t* o = (uint16_t*)a.out + row_of(hh) * D + c;
-        // a column that sees no token (possible under a draft mask) gives a zero row
-        const float inv = (Li > 0.f) ? a.v_scale / Li : 0.f;
-#pragma unroll
-        for (int t = 0; t < NTILES; ++t) o[16 * t] = f32_to_store<QK>(cacc[t][i] * inv);
+      for (int k = 0; k < QL; ++k) qraw[k] = nx_q[k];
+    } else {
+      s = uc.s;
+      kvh = uc.kvh;
+      slot = a.slot_base + uc.part;
+      const int32_t* table_row;
+      if (prefix) {
+        n = 0;
+        for (int k = 0; k < a.seq_group; ++k)
+          n = max(n, prefix_tokens(a, s, BS, clamp_len(a.ctx[s * a.seq_group + k])));
+        lo = hi = (c < G) ? prefix_tokens(a, s, BS, clamp_len(a.ctx[s * a.seq_group + c / Gr])) : 0;
+        table_row = a.tables + (size_t)s * a.seq_group * a.max_blocks;  // the group's first member
       } else {
-        const size_t pi = row_of(hh) * a.num_slots + a.slot_base + part;
-        float* pa_ = a.part_acc + pi * D + c;
+        n = clamp_len(a.ctx[s]);
+        if (multi) tm = load_mask(s);
+        if (a.mode == MODE_SUFFIX) jb = (prefix_tokens(a, s / a.seq_group, BS, n) + BS - 1) / BS;
+        table_row = a.tables + (size_t)s * a.max_blocks;
+      }
+      const int nblk = (n + BS - 1) / BS;
+      const int bpp = part_share_blocks(a, jb, nblk);
+      j0 = jb + uc.part * bpp;
+      j1 = min(nblk, j0 + bpp);
+      if (j0 >= j1) {
+        if (a.num_slots == 0) {  // direct output of an n == 0 sequence: zero rows
+          for (int cc = 0; cc < G; ++cc) {
+            uint16_t* o = (uint16_t*)a.out + row_at(s, kvh, cc) * D;
+            for (int e = lane; e < D; e += 64) o[e] = 0;
+          }
+        } else if (a.mode != MODE_PLAIN && r == 0 && c < G) {  // empty slot of a cascade row
+          const size_t pi = row_at(s, kvh, c) * a.num_slots + slot;
+          a.part_ml[pi * 2] = -INFINITY;
+          a.part_ml[pi * 2 + 1] = 0.f;
+        }
+        continue;
+      }
+      // the query's loads go out together with the table-slice load (neither depends on
+      // the other), and the first block's loads before the query is converted
+      load_query(s, kvh, qraw);
+      ts.init(table_row, j0, j1, a.num_blocks, lane);
+    }
+    if (!prefix) {
+      if (multi) {
+        lo = (c < G) ? n - a.query_len : 0;
+        hi = (c < G) ? n : 0;
+      } else {
+        lo = hi = (c < G) ? n : 0;
+      }
+    }
+    auto row_of = [&](int cc) -> size_t { return row_at(s, kvh, cc); };
+    const size_t blk_stride = (size_t)a.num_kv_heads * STILE;
+    const char* kbase = (const char*)a.k + (size_t)kvh * STILE;
+    const char* vbase = (const char*)a.v + (size_t)kvh * STILE;
+    const uint32_t voff = (uint32_t)lane * 16;  // natural 1 KiB wave loads (K and V)
+    auto load_tile = [&](const char* base, int phys, u32x4 (&t)[NLDS]) {
+      const char* p = base + (size_t)phys * blk_stride;
 #pragma unroll
-        for (int t = 0; t < NTILES; ++t) pa_[16 * t] = cacc[t][i];
-        if (c == 0) {
-          a.part_ml[pi * 2] = Mi;
-          a.part_ml[pi * 2 + 1] = Li;
+      for (int i = 0; i < NLDS; ++i) {
+        if constexpr (NT) t[i] = __builtin_nontemporal_load((const u32x4*)(p + voff + 1024 * i));
+        else t[i] = *(const u32x4*)(p + voff + 1024 * i);
+      }
+    };
+    // Appending decode (the unit that walks the sequence's last block, whose table entry lies
+    // in the pool -- an entry outside it skips the write, as the KV write does).  LDS-ring
+    // path: once block jn has landed, lane x < CPR writes 16-byte chunk x of the new K and V
+    // rows (in the cache's type: e4m3 codes of x * inv_scale, the KV write's conversion)
+    // into slot tn of the staged tiles, and the rows go to the cache after the epilogue, so
+    // no load waits for the store.  Register path: the rows are stored first.
+    const int jn = (n - 1) / BS, tn = (n - 1) % BS;
+    bool app = a.append && a.mode == MODE_PLAIN && n > 0 && j1 == (n + BS - 1) / BS;
+    int app_phys = 0;
+    u32x4 nk = u32x4{0, 0, 0, 0}, nv = u32x4{0, 0, 0, 0};
+    if constexpr (DMA) {
+      if (app && lane < CPR) {  // loaded whatever the table entry says (checked below)
+        const size_t src = ((size_t)s * a.num_kv_heads + kvh) * D + (size_t)lane * (16 / LE);
+        const u32x4* ks = (const u32x4*)((const uint16_t*)a.k_new + src);
+        const u32x4* vs = (const u32x4*)((const uint16_t*)a.v_new + src);
+        if constexpr (LE == 1) {
+          const u32x2 k0 = src8_to_e4m3<QK>(ks[0], a.k_inv_scale), k1 = src8_to_e4m3<QK>(ks[1], a.k_inv_scale);
+          const u32x2 v0 = src8_to_e4m3<QK>(vs[0], a.v_inv_scale), v1 = src8_to_e4m3<QK>(vs[1], a.v_inv_scale);
+          nk = u32x4{k0[0], k0[1], k1[0], k1[1]};
+          nv = u32x4{v0[0], v0[1], v1[0], v1[1]};
+        } else {
+          nk = ks[0];
+          nv = vs[0];
         }
       }
     }
-  }
-  // appending decode, LDS-ring path: the new rows into the cache, after everything that
-  // read the block
-  if (DMA && app && lane < CPR) {
-    const size_t dst = (((size_t)app_phys * a.num_kv_heads + kvh) * BS + tn) * (D * E) +
-                       (size_t)lane * 16;
-    *(u32x4*)((char*)a.k + dst) = nk;
-    *(u32x4*)((char*)a.v + dst) = nv;
+    if (app) {
+      app_phys = ts.raw(jn);
+      app = (unsigned)app_phys < (unsigned)a.num_blocks;
+    }
+    if constexpr (!DMA) {
+      if (app) append_new_row<D, BS, QK, KVK>(a, s, kvh, app_phys, tn, lane, jn - j0 < 2);
+    }
+    u32x4 ka[NLDS], va[NLDS], kb[NLDS], vb[NLDS];
+    // The barrier keeps the scheduler from hoisting the next block's LDS staging (and its
+    // wait for that block's loads) above these loads: the loads of block j+1 must be in
+    // flight before the wave waits for block j.
+    auto fetch = [&](int jj, u32x4 (&kr)[NLDS], u32x4 (&vr)[NLDS]) {
+      const int p = ts.get(jj);
+      load_tile(kbase, p, kr);
+      load_tile(vbase, p, vr);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // LDS-ring path: block j sits in stage (j - j0) mod 2.  Byte 16 * lane of 1 KiB piece i
+    // of a tile is row i * TPLS + lane / LPTS, chunk lane % LPTS, which must hold the row's
+    // chunk (lane % LPTS) ^ kswz(row) (K) or ^ swz(row) (V) of the swizzled layouts: that is
+    // what the lane fetches, so the wave still reads whole 1 KiB pieces.
+    uint32_t goffk[NLDS], goffv[NLDS];
+#pragma unroll
+    for (int i = 0; i < NLDS; ++i) {
+      const int row = i * TPLS + lane / LPTS;
+      const uint32_t base = i * 1024 + (lane / LPTS) * (D * E);
+      goffk[i] = base + (((lane % LPTS) ^ kswz(row)) * 16);
+      goffv[i] = base + (((lane % LPTS) ^ swz(row)) * 16);
+    }
+    // block jj of the table slice t, KV head kvh_, into stage st of the ring
+    auto issue_at = [&](const Slice& t, int kvh_, int jj, int st) {
+      const size_t boff = (size_t)t.get(jj) * blk_stride + (size_t)kvh_ * STILE;
+      const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st]));
+      const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st + 1]));
+#pragma unroll
+      for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>((const char*)a.k + boff + goffk[i], kl + 1024 * i);
+#pragma unroll
+      for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>((const char*)a.v + boff + goffv[i], vl + 1024 * i);
+    };
+    auto issue = [&](int jj, int st) { issue_at(ts, kvh, jj, st); };
+    if constexpr (DMA) {
+      if (!pre_issued) issue(j0, 0);
+    } else {
+      fetch(j0, ka, va);
+    }
+    pre_issued = false;
+    if constexpr (flat) prefetch();  // the next segment's set-up, behind this first block
+
+    // Q^T operand: lane (r, c) holds head c's dims 32kk + 8r .. +8 (zero for padding heads)
+    u32x4 qop[NATIVE ? 1 : KSTEPS];
+    // native: head c's dims QD*r .. +QD as three e4m3 terms (zero for padding heads), and
+    // the E8M0 exponent 127 - e of the operand scale 2^-e that undoes the head's 2^e
+    v8i qn[NATIVE ? 3 : 1];
+    int q_exp = 127;
+    if constexpr (NATIVE) {
+      float qv[QD];
+#pragma unroll
+      for (int k = 0; k < QD / 8; ++k) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          qv[8 * k + 2 * w] = (QK == KIND_BF16) ? bf16_lo(qraw[k][w]) : f16_lo(qraw[k][w]);
+          qv[8 * k + 2 * w + 1] = (QK == KIND_BF16) ? bf16_hi(qraw[k][w]) : f16_hi(qraw[k][w]);
+        }
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < QD; ++i) mx = fmaxf(mx, fabsf(qv[i]));
+      mx = rows_max(mx);
+      // mx in [2^(x-1), 2^x) -> scale by 2^(8-x): the largest element lands in [128, 256)
+      int e = (mx > 0.f) ? 8 - __builtin_amdgcn_frexp_expf(mx) : 0;
+      e = e > 127 ? 127 : e;
+      q_exp = 127 - e;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) qn[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < QD / 4; ++w) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __builtin_amdgcn_ldexpf(qv[4 * w + i], e);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {  // each term takes the rounding residual of the last
+          const uint32_t code = e4m3x4_pack(x[0], x[1], x[2], x[3]);
+          qn[t][w] = (int)code;
+          float back[4];
+          e4m3x4_to_f32(code, back);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] -= back[i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qop[kk] = qraw[kk];
+    }
+
+    // Output accumulators (matrix-core C operands) hold P . V relative to the reference
+    // maximum; they are rescaled only when the reference moves.
+    f32x4 cacc[NTILES];
+#pragma unroll
+    for (int t = 0; t < NTILES; ++t) cacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY;  // reference maximum of head c (log2 units), same in its 4 lanes
+    float l_part = 0.f;       // this lane's share of head c's denominator
+
+    uint8_t* kt = lds_buf[wave][0];
+    uint8_t* vt = lds_buf[wave][1];
+    const float qk_scale = a.qk_scale;
+    // This lane's share of a tile: wave load i, token row i*TPLS + lane/LPTS, elements
+    // (lane % LPTS) * EPLS .. +EPLS, i.e. LDS chunks (lane % LPTS) * CPL .. +CPL of that row.
+    // K's chunk x of row t sits at x ^ kswz(t): the operand reads (row c, one chunk) of 16
+    // lanes hit 16 different bank groups.  V's chunk x sits at x ^ swz(t).
+    uint32_t kw_off[NLDS][CPL], vw_off[NLDS][CPL];
+#pragma unroll
+    for (int i = 0; i < NLDS; ++i) {
+      const int row = i * TPLS + lane / LPTS;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) {
+        const int chunk = (lane % LPTS) * CPL + q;
+        kw_off[i][q] = row * PITCH + ((chunk ^ kswz(row)) * 16);
+        vw_off[i][q] = row * PITCH + ((chunk ^ swz(row)) * 16);
+      }
+    }
+    const int trow = 4 * r + c / 4;
+
+    // widen (e4m3) and write one tile into LDS; rows at or beyond n become zeros when
+    // `mask` (their bytes may be NaN and the matrix core would turn 0 * NaN into NaN)
+    auto stage = [&](uint8_t* dst, const uint32_t (&off)[NLDS][CPL], bool mask, int j,
+                     const u32x4 (&t)[NLDS]) {
+#pragma unroll
+      for (int i = 0; i < NLDS; ++i) {
+        u32x4 w[CPL];
+        if constexpr (NATIVE) {
+          w[0] = t[i];
+        } else if constexpr (KVK == KIND_E4M3) {
+          u32x4 two[2];
+          e4m3x16_widen<QK>(t[i], two);
+          w[0] = two[0];
+          w[CPL - 1] = two[1];
+        } else {
+          w[0] = t[i];
+        }
+        const bool dead = mask && j * BS + i * TPLS + lane / LPTS >= n;
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) *(u32x4*)(dst + off[i][q]) = dead ? u32x4{0, 0, 0, 0} : w[q];
+      }
+    };
+
+    // logits of block j: C[token 4r+i][head c]
+    auto logits = [&]() {
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (NATIVE) {
+        // K's operand: token c, the same dims QD*r .. +QD that lane (r, c) holds of Q
+        const uint8_t* row = kt + c * PITCH;
+        const u32x4 lo = *(const u32x4*)(row + ((((QD / 16) * r) ^ kswz(c)) * 16));
+        u32x4 hi = u32x4{0, 0, 0, 0};
+        if constexpr (QD == 32) hi = *(const u32x4*)(row + (((2 * r + 1) ^ kswz(c)) * 16));
+        const v8i kop = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+        for (int t = 0; t < 3; ++t) sc = mfma_e4m3(kop, qn[t], sc, 127, q_exp);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const int chunk = (4 * kk + r) ^ kswz(c);
+          const u32x4 kop = *(const u32x4*)(kt + c * PITCH + chunk * 16);
+          sc = Ops::qk(kop, qop[kk], sc);
+        }
+      }
+      return sc;
+    };
+
+    // online-softmax weights and P . V for block j (MASK: the block holds slots >= n)
+    auto finish = [&](int j, f32x4 sv) {
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = j * BS + 4 * r + i;
+        const bool ok = LANE ? (t < lo || (t < hi && ((tm >> ((t - lo) & 31)) & 1u)))
+                             : (c < G && t < n);
+        z[i] = ok ? sv[i] * qk_scale : -INFINITY;
+      }
+      float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      bm = rows_max(bm);
+      const bool move = bm > m_ref + kLazyRescaleLog2;  // false for padding heads (bm = -inf)
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float mn = move ? bm : m_ref;
+        const float f = move ? ((m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - mn)) : 1.f;
+        l_part *= f;
+        m_ref = mn;
+        // accumulator row 4r + i belongs to head 4r + i, whose factor sits in lane 4r + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float fi = __shfl(f, 4 * r + i);
+#pragma unroll
+          for (int t = 0; t < NTILES; ++t) cacc[t][i] *= fi;
+        }
+      }
+      const float ms = (m_ref == -INFINITY) ? 0.f : m_ref;
+      if constexpr (NATIVE) {
+        // weights 2^(z - ms) <= 2^8, lifted by 2^kb so the block's largest is in [2^7, 2^8)
+        const float rel = bm - ms;
+        int kb = 0;
+        if (rel > -INFINITY) {
+          kb = 7 - (int)floorf(rel);
+          kb = kb > 126 ? 126 : kb;
+        }
+        float p[4], pp[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = fast_exp2(z[i] - ms);
+          pp[i] = __builtin_amdgcn_ldexpf(p[i], kb);  // exact
+        }
+        const uint32_t hi = e4m3x4_pack(pp[0], pp[1], pp[2], pp[3]);
+        float back[4];
+        e4m3x4_to_f32(hi, back);
+        const uint32_t lo = e4m3x4_pack(pp[0] - back[0], pp[1] - back[1], pp[2] - back[2],
+                                        pp[3] - back[3]);
+        // P's operand: head c, tokens 4r .. 4r+3 as hi then lo; V's operand repeats those
+        // four tokens so both halves meet the same values; the A-operand scale 2^-kb undoes
+        // the lift.  The operands carry 8 codes of the 32 the instruction takes (the rest
+        // zero); issuing one tile at a time keeps a single zero-padded V operand live (about
+        // 30 fewer VGPRs at D = 128 than letting the compiler build all eight up front).
+        const v8i pop8 = v8i{(int)hi, (int)lo, 0, 0, 0, 0, 0, 0};
+        l_part += (p[0] + p[1]) + (p[2] + p[3]);
+        const int rho = 4 * r + ((c >> 1) & 3);
+#pragma unroll
+        for (int t = 0; t < NTILES; ++t) {
+          const v2i vv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_v2i*)(vt + rho * PITCH + ((t ^ swz(rho)) * 16) + 8 * (c & 1)));
+          const v8i vop = v8i{vv[0], vv[1], 0, 0, 0, 0, 0, 0};
+          cacc[t] = mfma_e4m3(pop8, vop, cacc[t], 127 - kb, 127);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
+      float p[4], rp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(z[i] - ms);
+      const uint32_t p01 = Ops::pack2(p[0], p[1], &rp[0], &rp[1]);
+      const uint32_t p23 = Ops::pack2(p[2], p[3], &rp[2], &rp[3]);
+      const u32x2 pop = u32x2{p01, p23};
+      // A weight rounded to the operand type is off by up to 2^-9 (bf16) or 2^-12 (fp16) of
+      // itself, which a few dominant tokens with distant values turn into output errors of
+      // the order of the 2e-3 bar.  So P goes in as hi + lo (the second MFMA takes the
+      // rounding residual, exact to about 2^-17 / 2^-23) and the denominator sums the
+      // unrounded weights.
+      float unused[4];
+      const u32x2 plo = u32x2{Ops::pack2(p[0] - rp[0], p[1] - rp[1], &unused[0], &unused[1]),
+                              Ops::pack2(p[2] - rp[2], p[3] - rp[3], &unused[2], &unused[3])};
+      l_part += (p[0] + p[1]) + (p[2] + p[3]);
+      // P . V over the 16 tokens, one 16-wide slice of the head dimension at a time
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) {
+        const uint32_t chunk = (2 * t + (c % 4) / 2) ^ swz(trow);
+        const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vt + trow * PITCH + chunk * 16 + 8 * (c % 2)));
+        cacc[t] = Ops::pv(pop, vb, cacc[t]);
+        cacc[t] = Ops::pv(plo, vb, cacc[t]);
+      }
+    };
+
+    // Pipeline (register path): two register sets of K and V tiles, as in the vector kernel;
+    // consuming block j moves K(j) and V(j) into the LDS tiles, runs the logit contraction,
+    // the softmax update and P . V.  The mask of slots >= n is applied branch-free (it only
+    // bites in a unit's last block).
+    if constexpr (DMA) {
+      constexpr int PER = 2 * NLDS;  // vector-memory operations per block
+      int st = 0;
+      for (int j = j0; j < j1; ++j) {
+        // fill the other stage (read by block j - 1) with block j + 1, then wait for block j
+        if (j + 1 < j1) {
+          issue(j + 1, st ^ 1);
+          wait_vmcnt<PER>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        kt = lds_buf[wave][2 * st];
+        vt = lds_buf[wave][2 * st + 1];
+        if (app && j == jn && lane < CPR) {  // the new token's rows into slot tn
+          *(u32x4*)(kt + tn * PITCH + ((lane ^ kswz(tn)) * 16)) = nk;
+          *(u32x4*)(vt + tn * PITCH + ((lane ^ swz(tn)) * 16)) = nv;
+        }
+        if (j * BS + BS > n) {  // V rows at or beyond n become zeros (their bytes may be NaN)
+#pragma unroll
+          for (int x = lane; x < TILE / 16; x += 64)
+            if (j * BS + x / CPR >= n) *(u32x4*)(vt + x * 16) = u32x4{0, 0, 0, 0};
+        }
+        finish(j, logits());
+        st ^= 1;
+      }
+    } else {
+      // A block's registers are free once it sits in LDS, so the block two ahead is fetched
+      // into them before the block's contractions run: two blocks stay in flight while one
+      // is consumed.  Steady state: blocks j .. j+3 exist, ka/va hold block j and kb/vb
+      // block j + 1, and every load in the loop is unconditional (see the vector kernel).
+      auto stage_kv = [&](int j, const u32x4 (&kr)[NLDS], const u32x4 (&vr)[NLDS]) {
+        stage(kt, kw_off, false, j, kr);
+        stage(vt, vw_off, true, j, vr);
+      };
+      int j = j0;
+      if (j + 1 < j1) fetch(j + 1, kb, vb);
+      while (j + 3 < j1) {
+        stage_kv(j, ka, va);
+        fetch(j + 2, ka, va);
+        finish(j, logits());
+        stage_kv(j + 1, kb, vb);
+        fetch(j + 3, kb, vb);
+        finish(j + 1, logits());
+        j += 2;
+      }
+      // one to three blocks left: ka/va hold block j, kb/vb block j + 1 when it exists
+      stage_kv(j, ka, va);
+      if (j + 2 < j1) fetch(j + 2, ka, va);
+      finish(j, logits());
+      if (j + 1 < j1) {
+        stage_kv(j + 1, kb, vb);
+        finish(j + 1, logits());
+      }
+      if (j + 2 < j1) {
+        stage_kv(j + 2, ka, va);
+        finish(j + 2, logits());
+      }
+    }
+
+    // flat walk: the next segment's first block goes out before this segment's partials
+    // (its table slice is already here), into stage 0, where that segment starts
+    if constexpr (flat && DMA) {
+      if (nx_ok) {
+        issue_at(nx_ts, nx.kvh, nx.j0, 0);
+        pre_issued = true;
+      }
+    }
+    // head c's denominator: sum of its four lanes' shares
+    const float L = rows_sum(l_part);
+    // accumulator row 4r + i (lane c holds dim 16t + c of slice t) belongs to head 4r + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * r + i;
+      const float Li = __shfl(L, hh);
+      const float Mi = __shfl(m_ref, hh);
+      if (hh < G) {
+        if (a.num_slots == 0) {
+          uint16_t* o = (uint16_t*)a.out + row_of(hh) * D + c;
+          // a column that sees no token (possible under a draft mask) gives a zero row
+          const float inv = (Li > 0.f) ? a.v_scale / Li : 0.f;
+#pragma unroll
+          for (int t = 0; t < NTILES; ++t) o[16 * t] = f32_to_store<QK>(cacc[t][i] * inv);
+        } else {
+          const size_t pi = row_of(hh) * a.num_slots + slot;
+          float* pa_ = a.part_acc + pi * D + c;
+#pragma unroll
+          for (int t = 0; t < NTILES; ++t) pa_[16 * t] = cacc[t][i];
+          if (c == 0) {
+            a.part_ml[pi * 2] = Mi;
+            a.part_ml[pi * 2 + 1] = Li;
+          }
+        }
+      }
+    }
+    // appending decode, LDS-ring path: the new rows into the cache, after everything that
+    // read the block
+    if (DMA && app && lane < CPR) {
+      const size_t dst = (((size_t)app_phys * a.num_kv_heads + kvh) * BS + tn) * (D * E) +
+                         (size_t)lane * 16;
+      *(u32x4*)((char*)a.k + dst) = nk;
+      *(u32x4*)((char*)a.v + dst) = nv;
+    }
   }
 }
 
 template <int D, int QK, int KVK, int G, bool NT>
 hipError_t launch_gqa_mfma_t(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 block(64 * PA_GQA_WAVES);
+  const bool lane_masks = a.mode == MODE_PREFIX || a.mode == MODE_MULTI;
+  if (a.flat_min_blocks > 0) {
+    // the flat split: plain and multi-token decodes over 16-bit caches only (the host never
+    // asks it otherwise)
+    if (a.mode != MODE_PLAIN && a.mode != MODE_MULTI) return hipErrorInvalidValue;
+    if constexpr (KVK == KIND_E4M3) {
+      return hipErrorInvalidValue;
+    } else {
+      static std::atomic<int> resident[2][kMaxCachedDevices];
+      if (lane_masks)
+        hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true, true>),
+                           decode_grid(a, PA_GQA_WAVES,
+                                       (const void*)paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true, true>,
+                                       resident[1]),
+                           block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, false, true>),
+                           decode_grid(a, PA_GQA_WAVES,
+                                       (const void*)paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, false, true>,
+                                       resident[0]),
+                           block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid = decode_grid(a, PA_GQA_WAVES);
-  if (a.mode == MODE_PREFIX || a.mode == MODE_MULTI)
-    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true>), grid, dim3(64 * PA_GQA_WAVES), 0,
+  if (lane_masks)
+    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, true, false>), grid, block, 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, false>), grid, dim3(64 * PA_GQA_WAVES), 0,
+    hipLaunchKernelGGL((paged_decode_gqa_mfma_kernel<D, QK, KVK, G, NT, false, false>), grid, block, 0,
                        stream, a);
   return hipGetLastError();
 }

@@ -68,8 +68,9 @@ template <> struct LoadVec<2> { using T = u32x2; };
 
 
 // NT: K/V loads carry the non-temporal hint (data read once per step).  APP: the appending
-// decode (a separate instantiation, so the plain decode carries none of its registers).
-template <int D, int BS, int QK, int KVK, int G, bool NT, bool APP>
+// decode, FLAT: the flat split (separate instantiations, so the plain decode over fixed
+// partitions carries none of their registers).
+template <int D, int BS, int QK, int KVK, int G, bool NT, bool APP, bool FLAT>
 __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(const DecodeArgs a) {
   using Geo = TileGeometry<D, BS, KVK>;
   using LT = typename LoadVec<Geo::W>::T;
@@ -79,339 +80,432 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const UnitCoords uc = unit_coords(a, PA_DECODE_WAVES, wave, a.num_seqs, BS);
-  if (!uc.ok) return;
-  const int s = uc.s, kvh = uc.kvh, part = uc.part;
-  const int h0 = kvh * G;
-
-  int n = a.ctx[s];
-  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  const int nblk = (n + BS - 1) / BS;
-  // suffix of a shared-prefix group: start after the blocks the prefix units cover
-  const int jb = (a.mode == MODE_SUFFIX)
-                     ? (prefix_tokens(a, s / a.seq_group, BS, n) + BS - 1) / BS : 0;
-  const int bpp = part_share_blocks(a, jb, nblk);
-  const int j0 = jb + part * bpp;
-  const int j1 = min(nblk, j0 + bpp);
   const int r = lane / LPT;   // token row of this lane inside a load
   const int c = lane % LPT;   // element slice [c*EPL, c*EPL + EPL) of the head dimension
-
-  if (j0 >= j1) {
-    // Nothing to read.  Direct output: this is the n == 0 row, write zeros.  Cascade
-    // partials: mark the slot empty (the merge skips it).
-    if (a.num_slots == 0 && lane < LPT) {
-      for (int g = 0; g < G; ++g) {
-        uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + h0 + g) * D + c * EPL;
-        for (int e = 0; e < EPL; ++e) o[e] = 0;
-      }
-    } else if (a.mode != MODE_PLAIN && lane < G) {
-      const size_t pi = ((size_t)s * a.num_heads + h0 + lane) * a.num_slots + a.slot_base + part;
-      a.part_ml[pi * 2] = -INFINITY;
-      a.part_ml[pi * 2 + 1] = 0.f;
-    }
-    return;
-  }
-
-  // ---- query slice, kept packed (fp16/bf16 caches) or widened to fp32 (e4m3 caches)
-  uint32_t qw[G][EPL / 2];
-  float qf[F8 ? G : 1][F8 ? EPL : 1];
-  for (int g = 0; g < G; ++g) {
-    const u32x4* qp = (const u32x4*)((const uint16_t*)a.q +
-                                     ((size_t)s * a.num_heads + h0 + g) * D + c * EPL);
+  // the query slices of the G heads that share KV head kvh, as loaded
+  auto load_query = [&](int s_, int kvh_, u32x4 (&qr)[G][EPL / 8]) {
 #pragma unroll
-    for (int k = 0; k < EPL / 8; ++k) {
-      u32x4 t = qp[k];
+    for (int g = 0; g < G; ++g) {
+      const u32x4* qp = (const u32x4*)((const uint16_t*)a.q +
+                                       ((size_t)s_ * a.num_heads + kvh_ * G + g) * D + c * EPL);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) qw[g][4 * k + w] = t[w];
-    }
-    if constexpr (F8) {
-#pragma unroll
-      for (int w = 0; w < EPL / 2; ++w) {
-        if constexpr (QK == KIND_BF16) {
-          qf[g][2 * w] = bf16_lo(qw[g][w]);
-          qf[g][2 * w + 1] = bf16_hi(qw[g][w]);
-        } else {
-          qf[g][2 * w] = f16_lo(qw[g][w]);
-          qf[g][2 * w + 1] = f16_hi(qw[g][w]);
-        }
-      }
-    }
-  }
-
-  float m[G], l[G], acc[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  }
-
-  const size_t blk_stride = (size_t)a.num_kv_heads * Geo::TILE;
-  const char* kbase = (const char*)a.k + (size_t)kvh * Geo::TILE;
-  const char* vbase = (const char*)a.v + (size_t)kvh * Geo::TILE;
-  const uint32_t loff = (uint32_t)lane * Geo::LB;
-  const float qk_scale = a.qk_scale;
-
-  auto issue = [&](int phys, LT (&kr)[NLD], LT (&vr)[NLD]) {
-    const char* kp = kbase + (size_t)phys * blk_stride;
-    const char* vp = vbase + (size_t)phys * blk_stride;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      if constexpr (NT) kr[i] = __builtin_nontemporal_load((const LT*)(kp + loff + i * Geo::SPAN));
-      else kr[i] = *(const LT*)(kp + loff + i * Geo::SPAN);
-    }
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      if constexpr (NT) vr[i] = __builtin_nontemporal_load((const LT*)(vp + loff + i * Geo::SPAN));
-      else vr[i] = *(const LT*)(vp + loff + i * Geo::SPAN);
+      for (int k = 0; k < EPL / 8; ++k) qr[g][k] = qp[k];
     }
   };
 
-  // Fold one block into the running state.  MASK: the block holds slots >= n.
-  auto consume = [&](auto mask_tag, int j, const LT (&kr)[NLD], const LT (&vr)[NLD]) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    float sc[G][NLD];
-    // q.k partial sums over this lane's slice
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      if constexpr (F8) {
-        float kf[EPL];
-#pragma unroll
-        for (int w = 0; w < W; ++w) e4m3x4_to_f32(kr[i][w], &kf[4 * w]);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPL; e += 2) {
-            d0 = fmaf(qf[g][e], kf[e], d0);
-            d1 = fmaf(qf[g][e + 1], kf[e + 1], d1);
-          }
-          sc[g][i] = d0 + d1;
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.f;
-#pragma unroll
-          for (int w = 0; w < W; ++w) {
-            if constexpr (KVK == KIND_F16)
-              d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw[g][w]),
-                                         __builtin_bit_cast(f16x2, (uint32_t)kr[i][w]), d, false);
-            else
-              d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[g][w]),
-                                                  __builtin_bit_cast(bf16x2, (uint32_t)kr[i][w]),
-                                                  d, false);
-          }
-          sc[g][i] = d;
-        }
-      }
-    }
-    // finish the dot products inside each token's lane group; scale into log2 units
-    bool valid[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      valid[i] = !MASK || (j * BS + i * TPL + r < n);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float z = group_sum<LPT>(sc[g][i]) * qk_scale;
-        sc[g][i] = valid[i] ? z : -INFINITY;
-      }
-    }
-    // online softmax update per head
-    float p[G][NLD];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float bm = sc[g][0];
-#pragma unroll
-      for (int i = 1; i < NLD; ++i) bm = fmaxf(bm, sc[g][i]);
-      const float mn = fmaxf(m[g], bm);
-      const float ms = (mn == -INFINITY) ? 0.f : mn;  // row has seen no valid token yet
-      const float rs = fast_exp2(m[g] - ms);
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        p[g][i] = fast_exp2(sc[g][i] - ms);
-        ps += p[g][i];
-      }
-      l[g] = l[g] * rs + ps;
-      m[g] = mn;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= rs;
-    }
-    // weighted value rows
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      float vf[EPL];
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const uint32_t x = vr[i][w];
-        if constexpr (F8) {
-          e4m3x4_to_f32(x, &vf[4 * w]);
-        } else if constexpr (KVK == KIND_BF16) {
-          vf[2 * w] = bf16_lo(x);
-          vf[2 * w + 1] = bf16_hi(x);
-        } else {
-          vf[2 * w] = f16_lo(x);
-          vf[2 * w + 1] = f16_hi(x);
-        }
-      }
-      if constexpr (MASK) {
-        // never let an unused slot's bytes (possibly NaN) reach the FMA: 0 * NaN = NaN
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[e] = valid[i] ? vf[e] : 0.f;
-      }
+  // Work: the one unit of unit_coords, or under the flat split this wavefront's walk.  The
+  // walk loads the next segment's set-up (table slice, query) while the current
+  // segment streams, right behind the current segment's first block, so a segment starts
+  // by requesting its first block.
+  constexpr bool flat = FLAT;
+  FlatWalk walk;
+  FlatSeg nx{0, 0, 0, 0, 0, 0};
+  bool nx_ok = false;
+  using Slice = std::conditional_t<FLAT, TableSlice2, TableSlice>;
+  Slice nx_ts;
+  u32x4 nx_q[G][EPL / 8];
+  auto prefetch = [&]() {
+    nx_ok = walk.next(nx);
+    if (!nx_ok) return;
+    nx_ts.init(a.tables + (size_t)nx.s * a.max_blocks, nx.j0, nx.j1, a.num_blocks, lane);
+    load_query(nx.s, nx.kvh, nx_q);
+  };
+  // the pipeline's first register set: under the flat split it can already hold the next
+  // segment's first block, requested before the last segment's epilogue
+  LT ka[NLD], va[NLD];
+  bool pre_issued = false;
+  UnitCoords uc{0, 0, 0, true};
+  if constexpr (flat) {
+    walk.init(a, BS, PA_DECODE_WAVES, wave, lane);
+    prefetch();
+  } else {
+    uc = unit_coords(a, PA_DECODE_WAVES, wave, a.num_seqs, BS);
+    if (!uc.ok) return;
+  }
+  // (one pass over the unit without the flat split: the trip count stays in the loop
+  // condition, where the compiler sees it)
+  for (int iter = 0; flat || iter < 1; ++iter) {
+    int s, kvh, j0, j1, slot, n;
+    Slice ts;
+    u32x4 qraw[G][EPL / 8];
+    if constexpr (flat) {
+      if (!nx_ok) break;
+      s = nx.s;
+      kvh = nx.kvh;
+      j0 = nx.j0;
+      j1 = nx.j1;
+      slot = nx.slot;
+      n = nx.n;
+      ts = nx_ts;
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g][i], vf[e], acc[g][e]);
-    }
-  };
-
-  // Appending decode (the unit that walks the sequence's last block, whose table entry lies
-  // in the pool -- an entry outside it skips the write, as the KV write does): the new
-  // token's rows take slot tn of block jn in place of the loaded bytes, and are stored into
-  // the cache after the unit's epilogue, so no load waits for the store.  Lanes of token
-  // row tn % TPL hold its slice c in load tn / TPL, in the cache's type (e4m3: the code of
-  // x * inv_scale, the conversion the KV write uses).
-  // (The rows are loaded whatever the table entry says; whether the entry lies in the pool
-  // is read from the unit's table slice once it is there, so nothing waits for it here.)
-  const int jn = (n - 1) / BS, tn = (n - 1) % BS;
-  bool app = APP && a.mode == MODE_PLAIN && n > 0 && j1 == nblk;
-  int app_phys = 0;
-  LT nk{}, nv{};
-  if (app) {
-    const size_t src = ((size_t)s * a.num_kv_heads + kvh) * D + (size_t)c * EPL;
-    const uint16_t* ks = (const uint16_t*)a.k_new + src;
-    const uint16_t* vs = (const uint16_t*)a.v_new + src;
-    if constexpr (F8) {
-      if constexpr (W == 4) {  // 16 codes from 16 source elements
-        const u32x2 k0 = src8_to_e4m3<QK>(((const u32x4*)ks)[0], a.k_inv_scale);
-        const u32x2 k1 = src8_to_e4m3<QK>(((const u32x4*)ks)[1], a.k_inv_scale);
-        const u32x2 v0 = src8_to_e4m3<QK>(((const u32x4*)vs)[0], a.v_inv_scale);
-        const u32x2 v1 = src8_to_e4m3<QK>(((const u32x4*)vs)[1], a.v_inv_scale);
-        nk = LT{k0[0], k0[1], k1[0], k1[1]};
-        nv = LT{v0[0], v0[1], v1[0], v1[1]};
-      } else {  // 8 codes from 8 source elements
-        nk = src8_to_e4m3<QK>(*(const u32x4*)ks, a.k_inv_scale);
-        nv = src8_to_e4m3<QK>(*(const u32x4*)vs, a.v_inv_scale);
-      }
+        for (int k = 0; k < EPL / 8; ++k) qraw[g][k] = nx_q[g][k];
     } else {
-      nk = *(const LT*)ks;
-      nv = *(const LT*)vs;
+      s = uc.s;
+      kvh = uc.kvh;
+      slot = a.slot_base + uc.part;
+      n = a.ctx[s];
     }
-  }
+    n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+    const int h0 = kvh * G;
+    const int nblk = (n + BS - 1) / BS;
+    if constexpr (!flat) {
+      // suffix of a shared-prefix group: start after the blocks the prefix units cover
+      const int jb = (a.mode == MODE_SUFFIX)
+                         ? (prefix_tokens(a, s / a.seq_group, BS, n) + BS - 1) / BS : 0;
+      const int bpp = part_share_blocks(a, jb, nblk);
+      j0 = jb + uc.part * bpp;
+      j1 = min(nblk, j0 + bpp);
+    }
 
-  auto process = [&](int j, LT (&kr)[NLD], LT (&vr)[NLD]) {
-    if (app && j == jn && r == tn % TPL) {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i)
-        if (i == tn / TPL) {
-          kr[i] = nk;
-          vr[i] = nv;
+    if (j0 >= j1) {
+      // Nothing to read.  Direct output: this is the n == 0 row, write zeros.  Cascade
+      // partials: mark the slot empty (the merge skips it).
+      if (a.num_slots == 0 && lane < LPT) {
+        for (int g = 0; g < G; ++g) {
+          uint16_t* o = (uint16_t*)a.out + ((size_t)s * a.num_heads + h0 + g) * D + c * EPL;
+          for (int e = 0; e < EPL; ++e) o[e] = 0;
         }
+      } else if (a.mode != MODE_PLAIN && lane < G) {
+        const size_t pi = ((size_t)s * a.num_heads + h0 + lane) * a.num_slots + slot;
+        a.part_ml[pi * 2] = -INFINITY;
+        a.part_ml[pi * 2 + 1] = 0.f;
+      }
+      continue;
     }
-    if ((j + 1) * BS <= n) consume(std::false_type{}, j, kr, vr);
-    else consume(std::true_type{}, j, kr, vr);
-  };
 
-  // Software pipeline: the K/V loads of block j+1 are issued before block j is consumed
-  // (two register sets).  The steady-state loop always has a next block to request, so every
-  // load in it is unconditional and the compiler's in-order load counter waits for exactly
-  // the block being consumed; the last one or two blocks are peeled off the loop.
-  TableSlice ts;
-  ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
-  if (app) {
-    app_phys = __builtin_amdgcn_readlane(ts.ids, jn - ts.j0);
-    app = (unsigned)app_phys < (unsigned)a.num_blocks;
-  }
-  LT ka[NLD], va[NLD], kb[NLD], vb[NLD];
-  issue(ts.get(j0), ka, va);
-  int j = j0;
-  while (j + 2 < j1) {
-    issue(ts.get(j + 1), kb, vb);
-    process(j, ka, va);
-    issue(ts.get(j + 2), ka, va);
-    process(j + 1, kb, vb);
-    j += 2;
-  }
-  if (j + 1 < j1) {
-    issue(ts.get(j + 1), kb, vb);
-    process(j, ka, va);
-    process(j + 1, kb, vb);
-  } else {
-    process(j, ka, va);
-  }
-
-  // ---- merge the TPL lane-group states of the wave (same rescaling rule)
+    // ---- query slice, kept packed (fp16/bf16 caches) or widened to fp32 (e4m3 caches)
+    if constexpr (!flat) load_query(s, kvh, qraw);
+    uint32_t qw[G][EPL / 2];
+    float qf[F8 ? G : 1][F8 ? EPL : 1];
+    for (int g = 0; g < G; ++g) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float M = m[g];
+      for (int k = 0; k < EPL / 8; ++k) {
+        const u32x4 t = qraw[g][k];
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float f = (m[g] == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
-    float L = l[g] * f;
+        for (int w = 0; w < 4; ++w) qw[g][4 * k + w] = t[w];
+      }
+      if constexpr (F8) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
-      L += __shfl_xor(L, off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
-    }
-    const int h = h0 + g;
-    if (a.num_slots == 0) {
-      if (lane < LPT) {
-        uint16_t ob[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          float o = acc[g][e] / L;
-          if constexpr (F8) o = o * a.v_scale;
-          ob[e] = f32_to_store<QK>(o);
-        }
-        u32x4* op = (u32x4*)((uint16_t*)a.out + ((size_t)s * a.num_heads + h) * D + c * EPL);
-#pragma unroll
-        for (int k = 0; k < EPL / 8; ++k) {
-          u32x4 t;
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            t[w] = (uint32_t)ob[8 * k + 2 * w] | ((uint32_t)ob[8 * k + 2 * w + 1] << 16);
-          op[k] = t;
+        for (int w = 0; w < EPL / 2; ++w) {
+          if constexpr (QK == KIND_BF16) {
+            qf[g][2 * w] = bf16_lo(qw[g][w]);
+            qf[g][2 * w + 1] = bf16_hi(qw[g][w]);
+          } else {
+            qf[g][2 * w] = f16_lo(qw[g][w]);
+            qf[g][2 * w + 1] = f16_hi(qw[g][w]);
+          }
         }
       }
+    }
+
+    float m[G], l[G], acc[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    }
+
+    const size_t blk_stride = (size_t)a.num_kv_heads * Geo::TILE;
+    const uint32_t loff = (uint32_t)lane * Geo::LB;
+    const float qk_scale = a.qk_scale;
+
+    // block `phys` of KV head kvh_ into (kr, vr)
+    auto issue_at = [&](int phys, int kvh_, LT (&kr)[NLD], LT (&vr)[NLD]) {
+      const size_t off = (size_t)phys * blk_stride + (size_t)kvh_ * Geo::TILE;
+      const char* kp = (const char*)a.k + off;
+      const char* vp = (const char*)a.v + off;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        if constexpr (NT) kr[i] = __builtin_nontemporal_load((const LT*)(kp + loff + i * Geo::SPAN));
+        else kr[i] = *(const LT*)(kp + loff + i * Geo::SPAN);
+      }
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        if constexpr (NT) vr[i] = __builtin_nontemporal_load((const LT*)(vp + loff + i * Geo::SPAN));
+        else vr[i] = *(const LT*)(vp + loff + i * Geo::SPAN);
+      }
+    };
+    auto issue = [&](int phys, LT (&kr)[NLD], LT (&vr)[NLD]) { issue_at(phys, kvh, kr, vr); };
+
+    // Fold one block into the running state.  MASK: the block holds slots >= n.
+    auto consume = [&](auto mask_tag, int j, const LT (&kr)[NLD], const LT (&vr)[NLD]) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      float sc[G][NLD];
+      // q.k partial sums over this lane's slice
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        if constexpr (F8) {
+          float kf[EPL];
+#pragma unroll
+          for (int w = 0; w < W; ++w) e4m3x4_to_f32(kr[i][w], &kf[4 * w]);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; e += 2) {
+              d0 = fmaf(qf[g][e], kf[e], d0);
+              d1 = fmaf(qf[g][e + 1], kf[e + 1], d1);
+            }
+            sc[g][i] = d0 + d1;
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float d = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+              if constexpr (KVK == KIND_F16)
+                d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw[g][w]),
+                                           __builtin_bit_cast(f16x2, (uint32_t)kr[i][w]), d, false);
+              else
+                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[g][w]),
+                                                    __builtin_bit_cast(bf16x2, (uint32_t)kr[i][w]),
+                                                    d, false);
+            }
+            sc[g][i] = d;
+          }
+        }
+      }
+      // finish the dot products inside each token's lane group; scale into log2 units
+      bool valid[NLD];
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        valid[i] = !MASK || (j * BS + i * TPL + r < n);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float z = group_sum<LPT>(sc[g][i]) * qk_scale;
+          sc[g][i] = valid[i] ? z : -INFINITY;
+        }
+      }
+      // online softmax update per head
+      float p[G][NLD];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float bm = sc[g][0];
+#pragma unroll
+        for (int i = 1; i < NLD; ++i) bm = fmaxf(bm, sc[g][i]);
+        const float mn = fmaxf(m[g], bm);
+        const float ms = (mn == -INFINITY) ? 0.f : mn;  // row has seen no valid token yet
+        const float rs = fast_exp2(m[g] - ms);
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          p[g][i] = fast_exp2(sc[g][i] - ms);
+          ps += p[g][i];
+        }
+        l[g] = l[g] * rs + ps;
+        m[g] = mn;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] *= rs;
+      }
+      // weighted value rows
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        float vf[EPL];
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          const uint32_t x = vr[i][w];
+          if constexpr (F8) {
+            e4m3x4_to_f32(x, &vf[4 * w]);
+          } else if constexpr (KVK == KIND_BF16) {
+            vf[2 * w] = bf16_lo(x);
+            vf[2 * w + 1] = bf16_hi(x);
+          } else {
+            vf[2 * w] = f16_lo(x);
+            vf[2 * w + 1] = f16_hi(x);
+          }
+        }
+        if constexpr (MASK) {
+          // never let an unused slot's bytes (possibly NaN) reach the FMA: 0 * NaN = NaN
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) vf[e] = valid[i] ? vf[e] : 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p[g][i], vf[e], acc[g][e]);
+      }
+    };
+
+    // Appending decode (the unit that walks the sequence's last block, whose table entry lies
+    // in the pool -- an entry outside it skips the write, as the KV write does): the new
+    // token's rows take slot tn of block jn in place of the loaded bytes, and are stored into
+    // the cache after the unit's epilogue, so no load waits for the store.  Lanes of token
+    // row tn % TPL hold its slice c in load tn / TPL, in the cache's type (e4m3: the code of
+    // x * inv_scale, the conversion the KV write uses).
+    // (The rows are loaded whatever the table entry says; whether the entry lies in the pool
+    // is read from the unit's table slice once it is there, so nothing waits for it here.)
+    const int jn = (n - 1) / BS, tn = (n - 1) % BS;
+    bool app = APP && a.mode == MODE_PLAIN && n > 0 && j1 == nblk;
+    int app_phys = 0;
+    LT nk{}, nv{};
+    if (app) {
+      const size_t src = ((size_t)s * a.num_kv_heads + kvh) * D + (size_t)c * EPL;
+      const uint16_t* ks = (const uint16_t*)a.k_new + src;
+      const uint16_t* vs = (const uint16_t*)a.v_new + src;
+      if constexpr (F8) {
+        if constexpr (W == 4) {  // 16 codes from 16 source elements
+          const u32x2 k0 = src8_to_e4m3<QK>(((const u32x4*)ks)[0], a.k_inv_scale);
+          const u32x2 k1 = src8_to_e4m3<QK>(((const u32x4*)ks)[1], a.k_inv_scale);
+          const u32x2 v0 = src8_to_e4m3<QK>(((const u32x4*)vs)[0], a.v_inv_scale);
+          const u32x2 v1 = src8_to_e4m3<QK>(((const u32x4*)vs)[1], a.v_inv_scale);
+          nk = LT{k0[0], k0[1], k1[0], k1[1]};
+          nv = LT{v0[0], v0[1], v1[0], v1[1]};
+        } else {  // 8 codes from 8 source elements
+          nk = src8_to_e4m3<QK>(*(const u32x4*)ks, a.k_inv_scale);
+          nv = src8_to_e4m3<QK>(*(const u32x4*)vs, a.v_inv_scale);
+        }
+      } else {
+        nk = *(const LT*)ks;
+        nv = *(const LT*)vs;
+      }
+    }
+
+    auto process = [&](int j, LT (&kr)[NLD], LT (&vr)[NLD]) {
+      if (app && j == jn && r == tn % TPL) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          if (i == tn / TPL) {
+            kr[i] = nk;
+            vr[i] = nv;
+          }
+      }
+      if ((j + 1) * BS <= n) consume(std::false_type{}, j, kr, vr);
+      else consume(std::true_type{}, j, kr, vr);
+    };
+
+    // Software pipeline: the K/V loads of block j+1 are issued before block j is consumed
+    // (two register sets).  The steady-state loop always has a next block to request, so every
+    // load in it is unconditional and the compiler's in-order load counter waits for exactly
+    // the block being consumed; the last one or two blocks are peeled off the loop.
+    if constexpr (!flat) ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
+    if (app) {
+      app_phys = ts.raw(jn);
+      app = (unsigned)app_phys < (unsigned)a.num_blocks;
+    }
+    LT kb[NLD], vb[NLD];
+    if (!pre_issued) issue(ts.get(j0), ka, va);
+    pre_issued = false;
+    if constexpr (flat) prefetch();  // the next segment's set-up, behind this first block
+    int j = j0;
+    while (j + 2 < j1) {
+      issue(ts.get(j + 1), kb, vb);
+      process(j, ka, va);
+      issue(ts.get(j + 2), ka, va);
+      process(j + 1, kb, vb);
+      j += 2;
+    }
+    if (j + 1 < j1) {
+      issue(ts.get(j + 1), kb, vb);
+      process(j, ka, va);
+      process(j + 1, kb, vb);
     } else {
-      const size_t pi = ((size_t)s * a.num_heads + h) * a.num_slots + a.slot_base + part;
-      if (lane < LPT) {
-        float* pa_ = a.part_acc + pi * D + c * EPL;
-#pragma unroll
-        for (int e = 0; e < EPL; e += 4) {
-          float4 t = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
-          *(float4*)(pa_ + e) = t;
-        }
-      }
-      if (lane == 0) {
-        a.part_ml[pi * 2] = M;
-        a.part_ml[pi * 2 + 1] = L;
+      process(j, ka, va);
+    }
+    // flat walk: the next segment's first block goes out before this segment's epilogue
+    // (its table slice is already here)
+    if constexpr (flat) {
+      if (nx_ok) {
+        issue_at(nx_ts.get(nx.j0), nx.kvh, ka, va);
+        pre_issued = true;
       }
     }
-  }
-  // appending decode: the new rows into the cache, after everything that read the block
-  if (app && r == tn % TPL) {
-    const size_t dst = (((size_t)app_phys * a.num_kv_heads + kvh) * BS + tn) * (Geo::TILE / BS) +
-                       (size_t)c * Geo::LB;
-    *(LT*)((char*)a.k + dst) = nk;
-    *(LT*)((char*)a.v + dst) = nv;
+
+    // ---- merge the TPL lane-group states of the wave (same rescaling rule)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float M = m[g];
+#pragma unroll
+      for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float f = (m[g] == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
+      float L = l[g] * f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
+#pragma unroll
+      for (int off = LPT; off < 64; off <<= 1) {
+        L += __shfl_xor(L, off);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+      }
+      const int h = h0 + g;
+      if (a.num_slots == 0) {
+        if (lane < LPT) {
+          uint16_t ob[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            float o = acc[g][e] / L;
+            if constexpr (F8) o = o * a.v_scale;
+            ob[e] = f32_to_store<QK>(o);
+          }
+          u32x4* op = (u32x4*)((uint16_t*)a.out + ((size_t)s * a.num_heads + h) * D + c * EPL);
+#pragma unroll
+          for (int k = 0; k < EPL / 8; ++k) {
+            u32x4 t;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              t[w] = (uint32_t)ob[8 * k + 2 * w] | ((uint32_t)ob[8 * k + 2 * w + 1] << 16);
+            op[k] = t;
+          }
+        }
+      } else {
+        const size_t pi = ((size_t)s * a.num_heads + h) * a.num_slots + slot;
+        if (lane < LPT) {
+          float* pa_ = a.part_acc + pi * D + c * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4) {
+            float4 t = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
+            *(float4*)(pa_ + e) = t;
+          }
+        }
+        if (lane == 0) {
+          a.part_ml[pi * 2] = M;
+          a.part_ml[pi * 2 + 1] = L;
+        }
+      }
+    }
+    // appending decode: the new rows into the cache, after everything that read the block
+    if (app && r == tn % TPL) {
+      const size_t dst = (((size_t)app_phys * a.num_kv_heads + kvh) * BS + tn) * (Geo::TILE / BS) +
+                         (size_t)c * Geo::LB;
+      *(LT*)((char*)a.k + dst) = nk;
+      *(LT*)((char*)a.v + dst) = nv;
+    }
   }
 }
 
 template <int D, int BS, int QK, int KVK, int G, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 block(64 * PA_DECODE_WAVES);
+  if (a.flat_min_blocks > 0) {
+    // the flat split: 16-bit caches only (the host never asks it for e4m3 caches)
+    if constexpr (KVK == KIND_E4M3) {
+      return hipErrorInvalidValue;
+    } else {
+      // The grid (and so the chunk length the walk derives from it) is the plain decode's
+      // for the appending one too, so both split the stream alike and give the same bits.
+      static std::atomic<int> resident[kMaxCachedDevices];
+      const dim3 grid = decode_grid(
+          a, PA_DECODE_WAVES, (const void*)paged_decode_kernel<D, BS, QK, KVK, G, NT, false, true>,
+          resident);
+      if (a.append)
+        hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT, true, true>), grid, block,
+                           0, stream, a);
+      else
+        hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT, false, true>), grid, block,
+                           0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (a.append)
-    hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT, true>), decode_grid(a, PA_DECODE_WAVES),
-                       dim3(64 * PA_DECODE_WAVES), 0, stream, a);
+    hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT, true, false>),
+                       decode_grid(a, PA_DECODE_WAVES), block, 0, stream, a);
   else
-    hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT, false>), decode_grid(a, PA_DECODE_WAVES),
-                       dim3(64 * PA_DECODE_WAVES), 0, stream, a);
+    hipLaunchKernelGGL((paged_decode_kernel<D, BS, QK, KVK, G, NT, false, false>),
+                       decode_grid(a, PA_DECODE_WAVES), block, 0, stream, a);
   return hipGetLastError();
 }
 

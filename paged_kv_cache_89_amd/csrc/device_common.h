@@ -173,8 +173,35 @@ struct TableSlice {
     ids = row[jj];
   }
   // j is wave-uniform, j0 <= j < j0 + 64
+  __device__ __forceinline__ int raw(int j) const { return __builtin_amdgcn_readlane(ids, j - j0); }
   __device__ __forceinline__ int get(int j) const {
-    const int p = __builtin_amdgcn_readlane(ids, j - j0);
+    const int p = raw(j);
+    return ((unsigned)p < (unsigned)nb) ? p : 0;
+  }
+};
+
+// The same over at most 128 blocks in two VGPRs (entries j0 + lane and j0 + 64 + lane):
+// the flat walk's chunks may be that long.
+struct TableSlice2 {
+  int j0, nb, ids, ids2;
+
+  __device__ __forceinline__ void init(const int32_t* row, int j0_, int j1, int nb_, int lane) {
+    j0 = j0_;
+    nb = nb_;
+    const int jj = j0 + lane < j1 ? j0 + lane : j1 - 1;
+    const int jj2 = j0 + 64 + lane < j1 ? j0 + 64 + lane : j1 - 1;
+    ids = row[jj];
+    ids2 = row[jj2];
+  }
+  // j is wave-uniform, j0 <= j < j0 + 128
+  __device__ __forceinline__ int raw(int j) const {
+    const int d = j - j0;
+    const int lo = __builtin_amdgcn_readlane(ids, d & 63);
+    const int hi = __builtin_amdgcn_readlane(ids2, d & 63);
+    return d < 64 ? lo : hi;
+  }
+  __device__ __forceinline__ int get(int j) const {
+    const int p = raw(j);
     return ((unsigned)p < (unsigned)nb) ? p : 0;
   }
 };
@@ -317,6 +344,155 @@ __device__ __forceinline__ UnitCoords unit_coords(const DecodeArgs& a, int waves
   if (a.xcd_remap == 2) return balanced_coords(a, waves, wave, block_size);
   return remapped_coords(a, waves, wave, rows);
 }
+
+// ---- flat split (DecodeArgs::flat_min_blocks > 0) -----------------------------------
+constexpr int kFlatK = kFlatMaxSeqs / 64;  // sequences per lane in the scans below
+
+// Block counts of sequences 0 .. S-1 as an inclusive prefix sum: cend[k] of lane l holds the
+// blocks of sequences 0 .. 64k + l (sequences at or past S count none), shifted left by 5,
+// with (n - 1) mod block_size of sequence 64k + l in the low 5 bits (block_size <= 32), so
+// that a sequence's length comes back from the scan too (flat_len).  Returns the total T.
+__device__ __forceinline__ int flat_scan(const int32_t* ctx, int S, int max_ctx, int block_size,
+                                         int lane, int (&cend)[kFlatK]) {
+  int nb[kFlatK], rem[kFlatK];
+#pragma unroll
+  for (int k = 0; k < kFlatK; ++k) {
+    const int s = lane + 64 * k;
+    int n = s < S ? ctx[s] : 0;
+    n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
+    nb[k] = (n + block_size - 1) / block_size;
+    rem[k] = n > 0 ? (n - 1) % block_size : 0;
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < kFlatK; ++k) {
+      const int y = __shfl_up(nb[k], off);
+      if (lane >= off) nb[k] += y;
+    }
+  }
+  int carry = 0;
+#pragma unroll
+  for (int k = 0; k < kFlatK; ++k) {
+    cend[k] = ((carry + nb[k]) << 5) | rem[k];
+    carry += __builtin_amdgcn_readlane(nb[k], 63);
+  }
+  return carry;
+}
+
+// Chunk length for a stream of T blocks, H KV heads and a grid of `waves` wavefronts: with
+// R = floor(waves / H) chunks per round, the fewest rounds k for which C = ceil(T / (k R))
+// is at most kFlatMaxChunk, and C no shorter than min_blocks (<= kFlatMaxChunk).  Then
+// ceil(T / C) <= k R chunks: every wavefront walks at most k units.
+__device__ __forceinline__ int flat_chunk(int T, int H, int waves, int min_blocks) {
+  const int R = waves / H > 0 ? waves / H : 1;
+  const int per = kFlatMaxChunk * R;  // blocks one round covers at the longest chunk
+  int k = T > per ? (T + per - 1) / per : 1;
+  while ((T + k * R - 1) / (k * R) > kFlatMaxChunk) ++k;  // guards the rounding above
+  const int C = (T + k * R - 1) / (k * R);
+  return C > min_blocks ? C : (min_blocks > 0 ? min_blocks : 1);
+}
+
+// Units (chunk, KV head) of this wavefront out of U: XCD x (workgroup i runs on XCD i % 8)
+// takes the contiguous share of [0, U) proportional to its wavefronts, and its wavefronts
+// take every (wavefronts on x)-th unit of it from their own index on.
+__device__ __forceinline__ void flat_units(long long U, int waves, int wave, int* first,
+                                           int* step, int* end) {
+  const int G8 = gridDim.x, x = blockIdx.x % 8, loc = blockIdx.x / 8;
+  const int per = G8 / 8, rem = G8 % 8;
+  const long long total = (long long)G8 * waves;
+  const long long before = (long long)(x * per + (x < rem ? x : rem)) * waves;
+  const int mine = (per + (x < rem ? 1 : 0)) * waves;
+  const long long lo = U * before / total, hi = U * (before + mine) / total;
+  *first = (int)(lo + (long long)loc * waves + wave);
+  *step = mine;
+  *end = (int)hi;
+}
+
+// The scan's word for sequence s (wave-uniform).
+__device__ __forceinline__ int flat_word(const int (&cend)[kFlatK], int s) {
+  int v = 0;
+#pragma unroll
+  for (int k = 0; k < kFlatK; ++k)
+    if (s >> 6 == k) v = __builtin_amdgcn_readlane(cend[k], s & 63);
+  return v;
+}
+
+// Inclusive block end of sequence s (wave-uniform), read from the scan.
+__device__ __forceinline__ int flat_end(const int (&cend)[kFlatK], int s) {
+  return flat_word(cend, s) >> 5;
+}
+
+// The sequence holding stream position p (0 <= p < T): the first whose inclusive end
+// exceeds p (the scan does not decrease, and empty sequences end where their predecessor
+// does, so they are never chosen).
+__device__ __forceinline__ int flat_seq(const int (&cend)[kFlatK], int p) {
+  int s = 0;
+  bool found = false;
+  const int key = (p << 5) | 31;  // word > key  <=>  block end > p
+#pragma unroll
+  for (int k = 0; k < kFlatK; ++k) {
+    const uint64_t m = __ballot(cend[k] > key);
+    if (!found && m) {
+      s = 64 * k + __builtin_ctzll(m);
+      found = true;
+    }
+  }
+  return s;
+}
+
+// One segment of the flat walk: blocks [j0, j1) of sequence s (n tokens, clamped) for KV
+// head kvh, ending in partial slot `slot` of the sequence's rows.
+struct FlatSeg {
+  int s, n, kvh, j0, j1, slot;
+};
+
+// The flat walk of one wavefront: its units (chunk, KV head) in turn (flat_units), each
+// as one segment per sequence it touches.  init() runs the scan and stores the chunk
+// length (and the grid's wavefronts) for the merge; next() yields the segments in order.
+struct FlatWalk {
+  int cend[kFlatK];
+  int T, C, H, unit, ustep, uend, pos, pend, chunk, ukvh;
+
+  int B;
+
+  __device__ __forceinline__ void init(const DecodeArgs& a, int block_size, int waves, int wave,
+                                       int lane) {
+    B = block_size;
+    T = flat_scan(a.ctx, a.num_seqs, a.max_ctx, block_size, lane, cend);
+    H = a.num_kv_heads;
+    C = flat_chunk(T, H, gridDim.x * waves, a.flat_min_blocks);
+    flat_units((long long)((T + C - 1) / C) * H, waves, wave, &unit, &ustep, &uend);
+    pos = pend = chunk = ukvh = 0;
+    if (blockIdx.x == 0 && wave == 0 && lane == 0) {  // for the merge, and for the record
+      a.flat_meta[0] = C;
+      a.flat_meta[1] = (int)gridDim.x * waves;
+    }
+  }
+
+  __device__ __forceinline__ bool next(FlatSeg& g) {
+    if (pos >= pend) {  // next unit
+      if (unit >= uend) return false;
+      chunk = unit / H;
+      ukvh = unit % H;
+      pos = chunk * C;
+      pend = min(pos + C, T);
+      unit += ustep;
+    }
+    // (all wave-uniform: read into scalar registers, so what they index is loaded with
+    // scalar loads)
+    g.s = __builtin_amdgcn_readfirstlane(flat_seq(cend, pos));
+    const int cum = g.s > 0 ? flat_end(cend, g.s - 1) : 0;
+    const int w = flat_word(cend, g.s);
+    g.n = __builtin_amdgcn_readfirstlane(((w >> 5) - cum - 1) * B + (w & 31) + 1);
+    g.kvh = __builtin_amdgcn_readfirstlane(ukvh);
+    g.j0 = __builtin_amdgcn_readfirstlane(pos - cum);
+    g.j1 = __builtin_amdgcn_readfirstlane(min(pend, w >> 5) - cum);
+    g.slot = __builtin_amdgcn_readfirstlane(chunk - cum / C);
+    pos = cum + g.j1;
+    return true;
+  }
+};
 
 // Blocks per unit of a row whose units walk blocks [jb, nblk): the fixed partition, or
 // under a balanced split an equal share of them, at least part_min_blocks.

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace pa {
 
 // Storage kinds used as template parameters.
@@ -13,6 +15,8 @@ enum Kind : int { KIND_F16 = 0, KIND_BF16 = 1, KIND_E4M3 = 2 };
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxUnitBlocks = 64;  // blocks one work unit (wavefront) walks at most
 constexpr int kBalancedMaxSeqs = 128;  // rows the work-balanced XCD ranges handle (xcd_remap 2)
+constexpr int kFlatMaxSeqs = 256;      // sequences the flat split handles (flat_min_blocks > 0)
+constexpr int kFlatMaxChunk = 128;     // blocks of a flat-split chunk at most (two-VGPR table slice)
 
 // Decode over work units (sequence, KV head, partition).  A unit walks blocks
 // [part * blocks_per_part, min(ceil(n / B), (part + 1) * blocks_per_part)) of its
@@ -27,6 +31,20 @@ constexpr int kBalancedMaxSeqs = 128;  // rows the work-balanced XCD ranges hand
 //     sequence's shared prefix; the walk starts at block ceil(min(prefix tokens, n) / B).
 // In both modes every unit writes its (m, l, acc) partial, empty or not, into slot
 // slot_base + part of the num_slots slots of each of its rows.
+//
+// Flat split (flat_min_blocks > 0; plain and multi-token decodes of at most kFlatMaxSeqs
+// sequences): instead of fixed partitions per sequence, the blocks of all sequences,
+// sequence after sequence, form one stream of T blocks cut into chunks of C blocks, and a
+// unit is (chunk, KV head), so every unit reads the same number of blocks however the
+// lengths fall.  A chunk that runs from one sequence into the next is walked as one segment
+// per sequence, each ending in a partial of its own: the segment of sequence s that starts
+// at stream position p fills slot floor(p / C) - floor(cum_s / C) of the sequence's rows
+// (cum_s: blocks of the sequences before s), so the slots of a sequence are consecutive
+// from 0.  The grid holds exactly the wavefronts that run at once (W); with T known, C is
+// the shortest chunk for which k rounds of W units cover the stream, k the fewest rounds
+// that keep C <= kFlatMaxChunk, and C >= flat_min_blocks (flat_chunk).  The decode stores
+// C at flat_meta[0] for the merge, which finds each row's slot count from the same scan,
+// and W at flat_meta[1].
 //
 // MODE_MULTI: query_len tokens per sequence (q and out are [S, query_len, Hq, D]); a
 // unit's query heads are its KV head's G heads for every query token, and query token
@@ -68,6 +86,10 @@ struct DecodeArgs {
   const void* k_new = nullptr;
   const void* v_new = nullptr;
   float k_inv_scale = 1.f, v_inv_scale = 1.f;
+  // flat split (see above): shortest chunk in blocks (0: fixed partitions), and where the
+  // decode leaves the chunk length it chose
+  int32_t flat_min_blocks = 0;
+  int32_t* flat_meta = nullptr;
 };
 
 struct DecodeShape {
@@ -75,8 +97,17 @@ struct DecodeShape {
   bool nontemporal;          // K/V loads with the non-temporal hint
 };
 
-// Grid of a decode launch with `waves` units per workgroup.
-inline dim3 decode_grid(const DecodeArgs& a, int waves) {
+// Workgroups of `kernel` (`threads` each) that fit on the current device at once:
+// occupancy per compute unit times the compute units, looked up once per device and kept
+// in `cache` (kMaxCachedDevices entries, zero-initialised).
+constexpr int kMaxCachedDevices = 64;
+int resident_workgroups(const void* kernel, int threads, std::atomic<int>* cache);
+
+// Grid of a decode launch with `waves` units per workgroup; the flat split takes the
+// workgroups that fit at once (`cache` as above).
+inline dim3 decode_grid(const DecodeArgs& a, int waves, const void* kernel = nullptr,
+                        std::atomic<int>* cache = nullptr) {
+  if (a.flat_min_blocks > 0 && kernel) return dim3(resident_workgroups(kernel, 64 * waves, cache));
   return dim3((a.num_units + waves - 1) / waves);
 }
 
@@ -94,6 +125,10 @@ struct MergeArgs {
   int32_t num_seqs, num_heads, num_parts, partition_size, max_ctx;
   float v_scale;
   int32_t all_slots;         // 1: merge every slot, skipping empty ones (cascade partials)
+  // flat split: a row's slots follow from the chunk length at flat_meta[0] and the blocks
+  // of the sequences before it (block_size tokens each); 0 / null otherwise
+  int32_t flat = 0, block_size = 0;
+  const int32_t* flat_meta = nullptr;
 };
 hipError_t launch_merge(int head_dim, int q_kind, const MergeArgs& a, hipStream_t stream);
 

@@ -7,7 +7,8 @@
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  o = sum_p acc_p 2^(m_p - M) / L.
 // One wavefront per (sequence, query head); lane k owns D/64 consecutive output elements.
 // Cascade partials (shared prefix + own suffix) fill every slot of a row, some of them
-// empty (m = -inf, l = 0, acc not written): those are skipped.
+// empty (m = -inf, l = 0, acc not written): those are skipped.  Under the flat split a
+// row's slots are the chunks its sequence's blocks fall into (see launch.h).
 #include "device_common.h"
 #include "launch.h"
 
@@ -52,7 +53,26 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a
     for (int e = 0; e < EPL; ++e) x[k][e] = pacc[(size_t)min(k, P - 1) * D + e];
 
   n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  const int np = a.all_slots ? (n > 0 ? P : 0) : (n + a.partition_size - 1) / a.partition_size;
+  int np;
+  if (a.flat) {
+    // flat split: the row's slots are the chunks its sequence's blocks fall into
+    const int B = a.block_size;
+    int before = 0;  // blocks of the sequences before s
+#pragma unroll
+    for (int k = 0; k < kFlatK; ++k) {
+      const int t = lane + 64 * k;
+      int nt = t < s ? a.ctx[t] : 0;
+      nt = nt < 0 ? 0 : (nt > a.max_ctx ? a.max_ctx : nt);
+      before += (nt + B - 1) / B;
+    }
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) before += __shfl_xor(before, k);
+    const int C = a.flat_meta[0];
+    const int nb = (n + B - 1) / B;
+    np = nb > 0 ? (before + nb - 1) / C - before / C + 1 : 0;
+  } else {
+    np = a.all_slots ? (n > 0 ? P : 0) : (n + a.partition_size - 1) / a.partition_size;
+  }
 
   // M = max over the row's slots (64 per pass; empty cascade slots carry m = -inf)
   float M = -INFINITY;
@@ -110,7 +130,8 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a
 
 template <int D, int QK>
 hipError_t launch_merge_pf(const MergeArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.num_parts <= 4)
+  // The flat split sizes its slots for the shortest chunk; most rows fill a few of them.
+  if (a.num_parts <= 4 || a.flat)
     hipLaunchKernelGGL((merge_partitions_kernel<D, QK, 4>), grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((merge_partitions_kernel<D, QK, 16>), grid, dim3(256), 0, stream, a);

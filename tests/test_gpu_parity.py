@@ -283,14 +283,22 @@ def test_physical_permutation_bit_identical():
 
 @pytest.mark.parametrize("name", ["opt13b_layer", "fp8_prefix"])
 def test_load_policy_flag_gives_identical_results(name):
-    """PA_DECODE_SHARED_KV only changes cache hints and the order units are visited:
-    every unit computes the same thing, so the output is bit-identical."""
+    """At a given partition size PA_DECODE_SHARED_KV only changes cache hints and the order
+    units are visited: every unit computes the same thing, so the output is bit-identical.
+    Under the library's choice the flag also keeps fixed partitions where fp16/bf16 caches
+    would take the flat split: both then agree with the oracle."""
     case = workloads.generate(workloads.SMALL[name], 8900 + 26)
     tables, _, _ = oracle_tables(case)
     k, v = oracle_caches(case, tables)
-    a = to_bits(_gpu_decode(case, tables, k, v, flags=0))
-    b = to_bits(_gpu_decode(case, tables, k, v, flags=pa.DECODE_SHARED_KV))
-    assert np.array_equal(a, b)
+    for P in (256, 512):
+        a = to_bits(_gpu_decode(case, tables, k, v, partition_size=P, flags=0))
+        b = to_bits(_gpu_decode(case, tables, k, v, partition_size=P, flags=pa.DECODE_SHARED_KV))
+        assert np.array_equal(a, b)
+    ref = oracle_decode(case, tables, k, v)
+    atol, rrel = tolerance(case.spec)
+    for flags in (0, pa.DECODE_SHARED_KV):
+        out = _f64(_gpu_decode(case, tables, k, v, partition_size=0, flags=flags))
+        compare(out, ref, atol, rrel, case.spec.q_dtype)
 
 
 @pytest.mark.parametrize("qd", ["f16", "bf16"])

@@ -130,26 +130,41 @@ def test_block_table_worked_example_through_library():
 
 # ------------------------------------------------------------------ planning and errors
 def test_decode_plan_and_workspace():
-    P, n = pa.decode_plan(8, 32, 32, 128, 32, 32768, 512)
-    assert (P, n) == (512, 64)
+    P, n, f = pa.decode_plan(8, 32, 32, 128, 32, 32768, 512)
+    assert (P, n, f) == (512, 64, 0)
     assert pa.decode_workspace_size(8, 32, 32, 128, 32, 32768, 512) == 8 * 32 * 64 * 130 * 4
-    # library choice: contexts <= 256 unsplit; else 768-token partitions, halved (staying
-    # at least 128) while the grid has < 4096 units; bounds of >= 16 such partitions take
+    E4 = pa.FP8_E4M3
+    # library choice, fixed partitions (e4m3 caches, 32-token blocks, more than 256
+    # sequences): contexts <= 256 unsplit; else 768-token partitions, halved (staying at
+    # least 128) while the grid has < 4096 units; bounds of >= 16 such partitions take
     # 64-block partitions when that still gives >= 4096 units
-    assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0) == (768, 3)
-    assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (2048, 16)
-    assert pa.decode_plan(4, 32, 32, 128, 32, 32768, 0) == (768, 43)   # 2048 units only
+    assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0, E4) == (768, 3, 0)
+    assert pa.decode_plan(8, 32, 32, 128, 32, 32768, 0) == (2048, 16, 0)
+    assert pa.decode_plan(4, 32, 32, 128, 32, 32768, 0) == (768, 43, 0)   # 2048 units only
+    assert pa.decode_plan(300, 8, 8, 64, 16, 2000, 0) == (768, 3, 0)
     # grouped queries over 16-token blocks (the matrix-core kernel) start from 1024 tokens
-    assert pa.decode_plan(128, 32, 8, 128, 16, 8192, 0) == (1024, 8)
-    assert pa.decode_plan(128, 32, 8, 128, 32, 8192, 0) == (768, 11)  # 32-token blocks: vector
-    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (0, 1)
-    assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0) == (192, 11)
-    assert pa.decode_plan(16, 8, 8, 64, 16, 8192, 0) == (192, 43)
-    assert pa.decode_plan(1, 8, 8, 64, 16, 48, 0) == (0, 1)
-    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 4096) == (0, 1)  # explicit P >= context
-    # a unit walks at most 64 blocks: longer partitions / unsplit contexts are cut
-    assert pa.decode_plan(2, 8, 8, 64, 16, 4000, 4096) == (1024, 4)
-    assert pa.decode_plan(2, 8, 8, 64, 8, 2000, 1024) == (512, 4)
+    assert pa.decode_plan(128, 32, 8, 128, 16, 8192, 0, E4) == (1024, 8, 0)
+    assert pa.decode_plan(128, 32, 8, 128, 32, 8192, 0) == (768, 11, 0)  # 32-token blocks
+    assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0, E4) == (192, 11, 0)
+    assert pa.decode_plan(16, 8, 8, 64, 16, 8192, 0, E4) == (192, 43, 0)
+    # fp16/bf16 caches, at most 256 sequences: the flat split, chunks of >= 16 blocks, so a
+    # row has at most ceil(max blocks / 16) + 1 partials
+    assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0) == (0, 9, 16)
+    assert pa.decode_plan(64, 40, 40, 128, 16, 2048, 0, pa.BF16) == (0, 9, 16)
+    assert pa.decode_plan(128, 32, 8, 128, 16, 8192, 0) == (0, 33, 16)
+    assert pa.decode_plan(4, 8, 8, 64, 16, 2000, 0) == (0, 9, 16)
+    assert pa.decode_plan(256, 8, 8, 64, 8, 2000, 0)[2] == 16
+    assert pa.decode_workspace_size(64, 40, 40, 128, 16, 2048, 0) == 64 * 40 * 9 * 130 * 4 + 16
+    # its workspace covers the fixed partitions of the same call (shared blocks, e4m3)
+    assert pa.decode_workspace_size(128, 32, 8, 128, 16, 8192, 0) >= 128 * 32 * 8 * 130 * 4
+    # unsplit contexts stay unsplit
+    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 0) == (0, 1, 0)
+    assert pa.decode_plan(1, 8, 8, 64, 16, 48, 0) == (0, 1, 0)
+    assert pa.decode_plan(4, 8, 8, 64, 16, 256, 4096) == (0, 1, 0)  # explicit P >= context
+    # an explicit partition size keeps fixed partitions; a unit walks at most 64 blocks:
+    # longer partitions / unsplit contexts are cut
+    assert pa.decode_plan(2, 8, 8, 64, 16, 4000, 4096) == (1024, 4, 0)
+    assert pa.decode_plan(2, 8, 8, 64, 8, 2000, 1024) == (512, 4, 0)
     assert pa.decode_workspace_size(4, 8, 8, 64, 16, 256, 4096) == 0
     with pytest.raises(pa.PagedAttnError):
         pa.decode_plan(4, 8, 8, 64, 16, 256, 24)  # not a multiple of B
@@ -189,7 +204,7 @@ def test_shared_prefix_workspace_and_errors_without_gpu():
     # of 64 blocks.  The shared-prefix decode splits by 512 tokens (its prompts are block
     # aligned; pa_decode alone would take 768): 2 prefix slots, and each row's own blocks
     # in 2 equal shares (no share above two 32-block partitions: 96 blocks fit).
-    assert pa.decode_plan(256, 32, 32, 128, 16, 1536, 0) == (768, 2)
+    assert pa.decode_plan(256, 32, 32, 128, 16, 1536, 0, pa.FP8_E4M3) == (768, 2, 0)
     ws = pa.decode_shared_prefix_workspace_size(256, 32, 32, 128, 16, 1536, 64)
     assert ws == 256 * 32 * (2 + 2) * 130 * 4
     # an explicit partition size applies to both launches: 1536 / 512 = 3 per-sequence slots
@@ -313,14 +328,21 @@ def test_hot_kernels_use_no_scratch():
             spilled[name] = scratch
     assert not spilled, spilled
     # the kernels the five workloads run, with their occupancy-setting register counts
-    # (four waves per SIMD need <= 128 VGPRs, three <= 168).  The bf16 GQA kernel stages
-    # K/V through a two-stage LDS ring (64 KiB per workgroup), which holds it to two waves
-    # per SIMD; its registers stay within the four-wave budget.
-    hot = {"_ZN2pa19paged_decode_kernelILi128ELi16ELi0ELi0ELi1ELb1ELb0EEEvNS_10DecodeArgsE": 128,
-           # the fp8 shared-prompt per-sequence units (e4m3 cache, bf16 queries)
-           "_ZN2pa19paged_decode_kernelILi128ELi16ELi1ELi2ELi1ELb1ELb0EEEvNS_10DecodeArgsE": 128,
-           "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0EEEvNS_10DecodeArgsE": 128,
-           # the fp8 shared-prompt prefix units (4 members x 1 head, per-column masks)
-           "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi2ELi4ELb1ELb1EEEvNS_10DecodeArgsE": 128}
+    # (four waves per SIMD need <= 128 VGPRs, three <= 168, two <= 256).  The matrix-core
+    # kernels over 16-bit caches stage K/V through a two-stage LDS ring (64 KiB per
+    # workgroup), which holds them to two waves per SIMD whatever their registers.
+    hot = {
+        # OPT-13B layer: fp16, flat split
+        "_ZN2pa19paged_decode_kernelILi128ELi16ELi0ELi0ELi1ELb1ELb0ELb1EEEvNS_10DecodeArgsE": 128,
+        # long contexts: fp16, 32-token blocks, fixed partitions
+        "_ZN2pa19paged_decode_kernelILi128ELi32ELi0ELi0ELi1ELb1ELb0ELb0EEEvNS_10DecodeArgsE": 168,
+        # the fp8 shared-prompt per-sequence units (e4m3 cache, bf16 queries)
+        "_ZN2pa19paged_decode_kernelILi128ELi16ELi1ELi2ELi1ELb1ELb0ELb0EEEvNS_10DecodeArgsE": 128,
+        # grouped queries (bf16, flat split) and four draft tokens over them
+        "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0ELb1EEEvNS_10DecodeArgsE": 168,
+        "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi16ELb1ELb1ELb1EEEvNS_10DecodeArgsE": 256,
+        # the fp8 shared-prompt prefix units (4 members x 1 head, per-column masks)
+        "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi2ELi4ELb1ELb1ELb0EEEvNS_10DecodeArgsE": 128,
+    }
     for name, vgpr_max in hot.items():
         assert k[name][0] == 0 and k[name][1] <= vgpr_max, (name, k[name])

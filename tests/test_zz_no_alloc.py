@@ -54,7 +54,9 @@ def _run_both(case, tables, k, v, P, rows=None):
 
 
 CASES = [("long_split", 512, 256, 1), ("gqa_llama", 256, 128, 2), ("fp8_prefix", 256, 128, 4),
-         ("opt13b_layer", 256, 512, 3)]
+         ("opt13b_layer", 256, 512, 3),
+         # library-chosen splits: the flat split (fp16/bf16) on both calls
+         ("opt13b_layer", 0, 0, 3), ("gqa_llama", 0, 0, 2)]
 
 
 @pytest.mark.parametrize("name,P1,P2,rows2", CASES)
@@ -85,3 +87,37 @@ def test_noalloc_refuses_plans_beyond_the_array():
                                     None)
     assert st == -2  # PA_ERR_UNSUPPORTED
     assert b"scratch" in pa.lib().pa_last_error()
+
+
+def test_noalloc_takes_fixed_partitions_when_the_flat_split_does_not_fit():
+    """128 sequences x 32 query heads under an 8192-token bound: the flat split's partials
+    (33 slots a row) exceed the array, its fixed 1024-token partitions (8 slots) fit, so the
+    call gives exactly pa_decode's output with those partitions, twice in a row."""
+    S, Hq, Hkv, D, B, mc = 128, 32, 8, 128, 16, 8192
+    flat = pa.decode_workspace_size(S, Hq, Hkv, D, B, mc, 0)
+    fixed = pa.decode_workspace_size(S, Hq, Hkv, D, B, mc, 1024)
+    assert fixed <= pa.NOALLOC_SCRATCH_BYTES < flat
+    assert pa.decode_plan(S, Hq, Hkv, D, B, mc, 0, pa.BF16)[:2] == (0, 33)
+    rng = np.random.default_rng(8900 + 41)
+    lens = rng.integers(1, 1500, S).astype(np.int32)
+    lens[3] = 0
+    nb = int(sum((n + B - 1) // B for n in lens))
+    perm = rng.permutation(nb + 5).astype(np.int32)
+    tables = np.full((S, mc // B), -1, np.int32)
+    k = 0
+    for s, n in enumerate(lens):
+        m = (int(n) + B - 1) // B
+        tables[s, :m] = perm[k:k + m]
+        k += m
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8900 + 42)
+    kd = torch.randn((nb + 5, Hkv, B, D), generator=g, device="cuda").to(torch.bfloat16)
+    vd = torch.randn((nb + 5, Hkv, B, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((S, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    td, cd = dev_i32(tables), dev_i32(lens)
+    ref = pa.decode(q, kd, vd, td, cd, mc, 0.088, partition_size=1024)
+    for _ in range(2):
+        out = torch.full_like(q, float("nan"))
+        pa.decode_noalloc(q, kd, vd, td, cd, mc, 0.088, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)

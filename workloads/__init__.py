@@ -161,7 +161,16 @@ def generate(spec: Spec, seed: int, context_lens=None) -> Case:
     token_index = np.full((S, int(ctx.max()) if S else 0), -1, np.int32)
     prompt_row = {}
     nrows = 0
-    for s in range(S):
+    if prefix_group is None:  # no sharing: every sequence's tokens in order, all new rows
+        lens = np.maximum(ctx, 0).astype(np.int64)
+        seq_ids = np.repeat(np.arange(S), lens).tolist()
+        positions = np.concatenate([np.arange(n) for n in lens]).tolist() if S else []
+        starts = np.concatenate([[0], np.cumsum(lens)[:-1]]) if S else np.zeros(0, np.int64)
+        for s in range(S):
+            token_index[s, :lens[s]] = starts[s] + np.arange(lens[s])
+        nrows = int(lens.sum())
+        rows_of = [("new", None)] * nrows
+    for s in (range(S) if prefix_group is not None else ()):
         n = int(ctx[s])
         g = -1 if prefix_group is None else int(prefix_group[s])
         for t in range(n):
@@ -188,6 +197,8 @@ def generate(spec: Spec, seed: int, context_lens=None) -> Case:
     k32 = np.empty((T, Hkv, d), np.float32)
     v32 = np.empty((T, Hkv, d), np.float32)
     j = 0
+    if n_new == T:  # every row new: the drawn rows in order
+        k32, v32, rows_of = k32_new, v32_new, []
     for r, (kind, src) in enumerate(rows_of):
         if kind == "new":
             k32[r] = k32_new[j]
