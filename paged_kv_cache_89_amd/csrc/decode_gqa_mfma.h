@@ -325,7 +325,7 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
   FlatWalk walk;
   FlatSeg nx{0, 0, 0, 0, 0, 0};
   bool nx_ok = false;
-  using Slice = std::conditional_t<FLAT, TableSlice2, TableSlice>;
+  using Slice = std::conditional_t<FLAT, TableSliceN<kFlatMaxChunkMatrix / 64>, TableSlice>;
   Slice nx_ts;
   u32x4 nx_q[QL];
   uint32_t nx_tm = 0;
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
   bool pre_issued = false;  // the segment's first block went out before the last one's partials
   UnitCoords uc{0, 0, 0, true};
   if constexpr (flat) {
-    walk.init(a, BS, PA_GQA_WAVES, wave, lane);
+    walk.init(a, BS, PA_GQA_WAVES, wave, lane, kFlatMaxChunkMatrix);
     prefetch();
   } else {
     uc = unit_coords(a, PA_GQA_WAVES, wave, rows, BS);

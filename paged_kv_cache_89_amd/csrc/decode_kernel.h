@@ -101,7 +101,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
   FlatWalk walk;
   FlatSeg nx{0, 0, 0, 0, 0, 0};
   bool nx_ok = false;
-  using Slice = std::conditional_t<FLAT, TableSlice2, TableSlice>;
+  using Slice = std::conditional_t<FLAT, TableSliceN<kFlatMaxChunkVector / 64>, TableSlice>;
   Slice nx_ts;
   u32x4 nx_q[G][EPL / 8];
   auto prefetch = [&]() {
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
   bool pre_issued = false;
   UnitCoords uc{0, 0, 0, true};
   if constexpr (flat) {
-    walk.init(a, BS, PA_DECODE_WAVES, wave, lane);
+    walk.init(a, BS, PA_DECODE_WAVES, wave, lane, kFlatMaxChunkVector);
     prefetch();
   } else {
     uc = unit_coords(a, PA_DECODE_WAVES, wave, a.num_seqs, BS);

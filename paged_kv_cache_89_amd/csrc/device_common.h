@@ -180,25 +180,29 @@ struct TableSlice {
   }
 };
 
-// The same over at most 128 blocks in two VGPRs (entries j0 + lane and j0 + 64 + lane):
-// the flat walk's chunks may be that long.
-struct TableSlice2 {
-  int j0, nb, ids, ids2;
+// The same over at most 64 * NS blocks in NS VGPRs (entry j0 + 64 q + lane in ids[q]): the
+// flat walk's chunks may be that long.
+template <int NS>
+struct TableSliceN {
+  int j0, nb, ids[NS];
 
   __device__ __forceinline__ void init(const int32_t* row, int j0_, int j1, int nb_, int lane) {
     j0 = j0_;
     nb = nb_;
-    const int jj = j0 + lane < j1 ? j0 + lane : j1 - 1;
-    const int jj2 = j0 + 64 + lane < j1 ? j0 + 64 + lane : j1 - 1;
-    ids = row[jj];
-    ids2 = row[jj2];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      const int jj = j0 + 64 * q + lane;
+      ids[q] = row[jj < j1 ? jj : j1 - 1];
+    }
   }
-  // j is wave-uniform, j0 <= j < j0 + 128
+  // j is wave-uniform, j0 <= j < j0 + 64 * NS
   __device__ __forceinline__ int raw(int j) const {
     const int d = j - j0;
-    const int lo = __builtin_amdgcn_readlane(ids, d & 63);
-    const int hi = __builtin_amdgcn_readlane(ids2, d & 63);
-    return d < 64 ? lo : hi;
+    int v = 0;
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+      if (d >> 6 == q) v = __builtin_amdgcn_readlane(ids[q], d & 63);
+    return v;
   }
   __device__ __forceinline__ int get(int j) const {
     const int p = raw(j);
@@ -382,13 +386,13 @@ __device__ __forceinline__ int flat_scan(const int32_t* ctx, int S, int max_ctx,
 
 // Chunk length for a stream of T blocks, H KV heads and a grid of `waves` wavefronts: with
 // R = floor(waves / H) chunks per round, the fewest rounds k for which C = ceil(T / (k R))
-// is at most kFlatMaxChunk, and C no shorter than min_blocks (<= kFlatMaxChunk).  Then
+// is at most max_chunk, and C no shorter than min_blocks (<= max_chunk).  Then
 // ceil(T / C) <= k R chunks: every wavefront walks at most k units.
-__device__ __forceinline__ int flat_chunk(int T, int H, int waves, int min_blocks) {
+__device__ __forceinline__ int flat_chunk(int T, int H, int waves, int min_blocks, int max_chunk) {
   const int R = waves / H > 0 ? waves / H : 1;
-  const int per = kFlatMaxChunk * R;  // blocks one round covers at the longest chunk
+  const int per = max_chunk * R;  // blocks one round covers at the longest chunk
   int k = T > per ? (T + per - 1) / per : 1;
-  while ((T + k * R - 1) / (k * R) > kFlatMaxChunk) ++k;  // guards the rounding above
+  while ((T + k * R - 1) / (k * R) > max_chunk) ++k;  // guards the rounding above
   const int C = (T + k * R - 1) / (k * R);
   return C > min_blocks ? C : (min_blocks > 0 ? min_blocks : 1);
 }
@@ -457,11 +461,11 @@ struct FlatWalk {
   int B;
 
   __device__ __forceinline__ void init(const DecodeArgs& a, int block_size, int waves, int wave,
-                                       int lane) {
+                                       int lane, int max_chunk) {
     B = block_size;
     T = flat_scan(a.ctx, a.num_seqs, a.max_ctx, block_size, lane, cend);
     H = a.num_kv_heads;
-    C = flat_chunk(T, H, gridDim.x * waves, a.flat_min_blocks);
+    C = flat_chunk(T, H, gridDim.x * waves, a.flat_min_blocks, max_chunk);
     flat_units((long long)((T + C - 1) / C) * H, waves, wave, &unit, &ustep, &uend);
     pos = pend = chunk = ukvh = 0;
     if (blockIdx.x == 0 && wave == 0 && lane == 0) {  // for the merge, and for the record

@@ -16,7 +16,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxUnitBlocks = 64;  // blocks one work unit (wavefront) walks at most
 constexpr int kBalancedMaxSeqs = 128;  // rows the work-balanced XCD ranges handle (xcd_remap 2)
 constexpr int kFlatMaxSeqs = 256;      // sequences the flat split handles (flat_min_blocks > 0)
-constexpr int kFlatMaxChunk = 128;     // blocks of a flat-split chunk at most (two-VGPR table slice)
+// blocks of a flat-split chunk at most: the vector kernel's table slice takes two VGPRs, the
+// matrix-core kernel's four (it is held to two waves per SIMD by its LDS, not its registers)
+constexpr int kFlatMaxChunkVector = 128;
+constexpr int kFlatMaxChunkMatrix = 256;
 
 // Decode over work units (sequence, KV head, partition).  A unit walks blocks
 // [part * blocks_per_part, min(ceil(n / B), (part + 1) * blocks_per_part)) of its
@@ -42,7 +45,8 @@ constexpr int kFlatMaxChunk = 128;     // blocks of a flat-split chunk at most (
 // (cum_s: blocks of the sequences before s), so the slots of a sequence are consecutive
 // from 0.  The grid holds exactly the wavefronts that run at once (W); with T known, C is
 // the shortest chunk for which k rounds of W units cover the stream, k the fewest rounds
-// that keep C <= kFlatMaxChunk, and C >= flat_min_blocks (flat_chunk).  The decode stores
+// that keep C within the kernel's table slice (kFlatMaxChunk*), and C >= flat_min_blocks
+// (flat_chunk).  The decode stores
 // C at flat_meta[0] for the merge, which finds each row's slot count from the same scan,
 // and W at flat_meta[1].
 //

@@ -339,7 +339,7 @@ def test_hot_kernels_use_no_scratch():
         # the fp8 shared-prompt per-sequence units (e4m3 cache, bf16 queries)
         "_ZN2pa19paged_decode_kernelILi128ELi16ELi1ELi2ELi1ELb1ELb0ELb0EEEvNS_10DecodeArgsE": 128,
         # grouped queries (bf16, flat split) and four draft tokens over them
-        "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0ELb1EEEvNS_10DecodeArgsE": 168,
+        "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi4ELb1ELb0ELb1EEEvNS_10DecodeArgsE": 256,
         "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi1ELi16ELb1ELb1ELb1EEEvNS_10DecodeArgsE": 256,
         # the fp8 shared-prompt prefix units (4 members x 1 head, per-column masks)
         "_ZN2pa28paged_decode_gqa_mfma_kernelILi128ELi1ELi2ELi4ELb1ELb1ELb0EEEvNS_10DecodeArgsE": 128,
