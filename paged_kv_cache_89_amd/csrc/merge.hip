@@ -108,12 +108,16 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a
       }
       q = PF;
     }
-    for (; q < cnt; q += PF) {  // further slots, PF loads in flight at a time
+    for (; q < cnt; q += PF) {  // further slots, PF loads in flight at a time; only the
+                                // slots that carry weight (cascade rows leave many empty)
       float y[PF][EPL];
 #pragma unroll
-      for (int k = 0; k < PF; ++k)
+      for (int k = 0; k < PF; ++k) {
+        const bool want = q + k < cnt && __builtin_amdgcn_readlane(__float_as_int(w), q + k) != 0;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) y[k][e] = pacc[(size_t)min(base + q + k, P - 1) * D + e];
+        for (int e = 0; e < EPL; ++e)
+          y[k][e] = want ? pacc[(size_t)min(base + q + k, P - 1) * D + e] : 0.f;
+      }
 #pragma unroll
       for (int k = 0; k < PF; ++k) {
         if (q + k < cnt) {
@@ -130,8 +134,9 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a
 
 template <int D, int QK>
 hipError_t launch_merge_pf(const MergeArgs& a, dim3 grid, hipStream_t stream) {
-  // The flat split sizes its slots for the shortest chunk; most rows fill a few of them.
-  if (a.num_parts <= 4 || a.flat)
+  // The flat split sizes its slots for the shortest chunk, and cascade rows hold empty
+  // slots: most rows fill a few of their slots, so the first batch stays small.
+  if (a.num_parts <= 4 || a.flat || a.all_slots)
     hipLaunchKernelGGL((merge_partitions_kernel<D, QK, 4>), grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((merge_partitions_kernel<D, QK, 16>), grid, dim3(256), 0, stream, a);
