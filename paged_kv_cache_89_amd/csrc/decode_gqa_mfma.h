@@ -317,6 +317,31 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
                           : (uint32_t)((2ull << t) - 1);
   };
 
+  using Slice = std::conditional_t<FLAT, TableSliceN<kFlatMaxChunkMatrix / 64>, TableSlice>;
+  const size_t blk_stride = (size_t)a.num_kv_heads * STILE;
+  // LDS-ring path: block j sits in stage (j - j0) mod 2.  Byte 16 * lane of 1 KiB piece i
+  // of a tile is row i * TPLS + lane / LPTS, chunk lane % LPTS, which must hold the row's
+  // chunk (lane % LPTS) ^ kswz(row) (K) or ^ swz(row) (V) of the swizzled layouts: that is
+  // what the lane fetches, so the wave still reads whole 1 KiB pieces.
+  uint32_t goffk[NLDS], goffv[NLDS];
+#pragma unroll
+  for (int i = 0; i < NLDS; ++i) {
+    const int row = i * TPLS + lane / LPTS;
+    const uint32_t base = i * 1024 + (lane / LPTS) * (D * E);
+    goffk[i] = base + (((lane % LPTS) ^ kswz(row)) * 16);
+    goffv[i] = base + (((lane % LPTS) ^ swz(row)) * 16);
+  }
+  // block jj of the table slice t, KV head kvh_, into stage st of the ring
+  auto issue_at = [&](const Slice& t, int kvh_, int jj, int st) {
+    const size_t boff = (size_t)t.get(jj) * blk_stride + (size_t)kvh_ * STILE;
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st]));
+    const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st + 1]));
+#pragma unroll
+    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>((const char*)a.k + boff + goffk[i], kl + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>((const char*)a.v + boff + goffv[i], vl + 1024 * i);
+  };
+
   // Work: the one unit of unit_coords, or under the flat split (plain and multi-token
   // decodes) this wavefront's walk.  The walk loads the next segment's set-up (table slice,
   // query, draft masks) while the current segment streams, right behind the
@@ -325,7 +350,6 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
   FlatWalk walk;
   FlatSeg nx{0, 0, 0, 0, 0, 0};
   bool nx_ok = false;
-  using Slice = std::conditional_t<FLAT, TableSliceN<kFlatMaxChunkMatrix / 64>, TableSlice>;
   Slice nx_ts;
   u32x4 nx_q[QL];
   uint32_t nx_tm = 0;
@@ -403,8 +427,8 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
       }
       // the query's loads go out together with the table-slice load (neither depends on
       // the other), and the first block's loads before the query is converted
-      load_query(s, kvh, qraw);
       ts.init(table_row, j0, j1, a.num_blocks, lane);
+      if constexpr (!DMA) load_query(s, kvh, qraw);  // register path: with the table slice
     }
     if (!prefix) {
       if (multi) {
@@ -415,7 +439,16 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
       }
     }
     auto row_of = [&](int cc) -> size_t { return row_at(s, kvh, cc); };
-    const size_t blk_stride = (size_t)a.num_kv_heads * STILE;
+    auto issue = [&](int jj, int st) { issue_at(ts, kvh, jj, st); };
+    if constexpr (DMA) {
+      // The segment's first block goes out before anything else it needs (unless the walk
+      // requested it before the last segment's partials); then the next segment's set-up,
+      // then (fixed partitions) this one's query.
+      if (!pre_issued) issue(j0, 0);
+      pre_issued = false;
+      if constexpr (flat) prefetch();
+      if constexpr (!flat) load_query(s, kvh, qraw);
+    }
     const char* kbase = (const char*)a.k + (size_t)kvh * STILE;
     const char* vbase = (const char*)a.v + (size_t)kvh * STILE;
     const uint32_t voff = (uint32_t)lane * 16;  // natural 1 KiB wave loads (K and V)
@@ -470,36 +503,10 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
       load_tile(vbase, p, vr);
       __builtin_amdgcn_sched_barrier(0);
     };
-    // LDS-ring path: block j sits in stage (j - j0) mod 2.  Byte 16 * lane of 1 KiB piece i
-    // of a tile is row i * TPLS + lane / LPTS, chunk lane % LPTS, which must hold the row's
-    // chunk (lane % LPTS) ^ kswz(row) (K) or ^ swz(row) (V) of the swizzled layouts: that is
-    // what the lane fetches, so the wave still reads whole 1 KiB pieces.
-    uint32_t goffk[NLDS], goffv[NLDS];
-#pragma unroll
-    for (int i = 0; i < NLDS; ++i) {
-      const int row = i * TPLS + lane / LPTS;
-      const uint32_t base = i * 1024 + (lane / LPTS) * (D * E);
-      goffk[i] = base + (((lane % LPTS) ^ kswz(row)) * 16);
-      goffv[i] = base + (((lane % LPTS) ^ swz(row)) * 16);
-    }
-    // block jj of the table slice t, KV head kvh_, into stage st of the ring
-    auto issue_at = [&](const Slice& t, int kvh_, int jj, int st) {
-      const size_t boff = (size_t)t.get(jj) * blk_stride + (size_t)kvh_ * STILE;
-      const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st]));
-      const uint32_t vl = __builtin_amdgcn_readfirstlane(lds_offset(lds_buf[wave][2 * st + 1]));
-#pragma unroll
-      for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>((const char*)a.k + boff + goffk[i], kl + 1024 * i);
-#pragma unroll
-      for (int i = 0; i < NLDS; ++i) load_lds_x4<NT>((const char*)a.v + boff + goffv[i], vl + 1024 * i);
-    };
-    auto issue = [&](int jj, int st) { issue_at(ts, kvh, jj, st); };
-    if constexpr (DMA) {
-      if (!pre_issued) issue(j0, 0);
-    } else {
+    if constexpr (!DMA) {
       fetch(j0, ka, va);
+      if constexpr (flat) prefetch();  // the next segment's set-up, behind this first block
     }
-    pre_issued = false;
-    if constexpr (flat) prefetch();  // the next segment's set-up, behind this first block
 
     // Q^T operand: lane (r, c) holds head c's dims 32kk + 8r .. +8 (zero for padding heads)
     u32x4 qop[NATIVE ? 1 : KSTEPS];

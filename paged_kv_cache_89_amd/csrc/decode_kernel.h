@@ -93,6 +93,25 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
     }
   };
 
+  const size_t blk_stride = (size_t)a.num_kv_heads * Geo::TILE;
+  const uint32_t loff = (uint32_t)lane * Geo::LB;
+  // block `phys` of KV head kvh_ into (kr, vr)
+  auto issue_at = [&](int phys, int kvh_, LT (&kr)[NLD], LT (&vr)[NLD]) {
+    const char* kp = (const char*)a.k + (size_t)kvh_ * Geo::TILE + loff;
+    const char* vp = (const char*)a.v + (size_t)kvh_ * Geo::TILE + loff;
+    const size_t off = (size_t)phys * blk_stride;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (NT) kr[i] = __builtin_nontemporal_load((const LT*)(kp + off + i * Geo::SPAN));
+      else kr[i] = *(const LT*)(kp + off + i * Geo::SPAN);
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      if constexpr (NT) vr[i] = __builtin_nontemporal_load((const LT*)(vp + off + i * Geo::SPAN));
+      else vr[i] = *(const LT*)(vp + off + i * Geo::SPAN);
+    }
+  };
+
   // Work: the one unit of unit_coords, or under the flat split this wavefront's walk.  The
   // walk loads the next segment's set-up (table slice, query) while the current
   // segment streams, right behind the current segment's first block, so a segment starts
@@ -175,6 +194,13 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
       continue;
     }
 
+    // The segment's first block goes out before anything else it needs (unless the walk
+    // requested it before the last segment's epilogue); then the next segment's set-up.
+    if constexpr (!flat) ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
+    if (!pre_issued) issue_at(ts.get(j0), kvh, ka, va);
+    pre_issued = false;
+    if constexpr (flat) prefetch();
+
     // ---- query slice, kept packed (fp16/bf16 caches) or widened to fp32 (e4m3 caches)
     if constexpr (!flat) load_query(s, kvh, qraw);
     uint32_t qw[G][EPL / 2];
@@ -209,26 +235,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
       for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
     }
 
-    const size_t blk_stride = (size_t)a.num_kv_heads * Geo::TILE;
-    const uint32_t loff = (uint32_t)lane * Geo::LB;
     const float qk_scale = a.qk_scale;
-
-    // block `phys` of KV head kvh_ into (kr, vr)
-    auto issue_at = [&](int phys, int kvh_, LT (&kr)[NLD], LT (&vr)[NLD]) {
-      const size_t off = (size_t)phys * blk_stride + (size_t)kvh_ * Geo::TILE;
-      const char* kp = (const char*)a.k + off;
-      const char* vp = (const char*)a.v + off;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        if constexpr (NT) kr[i] = __builtin_nontemporal_load((const LT*)(kp + loff + i * Geo::SPAN));
-        else kr[i] = *(const LT*)(kp + loff + i * Geo::SPAN);
-      }
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        if constexpr (NT) vr[i] = __builtin_nontemporal_load((const LT*)(vp + loff + i * Geo::SPAN));
-        else vr[i] = *(const LT*)(vp + loff + i * Geo::SPAN);
-      }
-    };
     auto issue = [&](int phys, LT (&kr)[NLD], LT (&vr)[NLD]) { issue_at(phys, kvh, kr, vr); };
 
     // Fold one block into the running state.  MASK: the block holds slots >= n.
@@ -382,15 +389,11 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
     // (two register sets).  The steady-state loop always has a next block to request, so every
     // load in it is unconditional and the compiler's in-order load counter waits for exactly
     // the block being consumed; the last one or two blocks are peeled off the loop.
-    if constexpr (!flat) ts.init(a.tables + (size_t)s * a.max_blocks, j0, j1, a.num_blocks, lane);
     if (app) {
       app_phys = ts.raw(jn);
       app = (unsigned)app_phys < (unsigned)a.num_blocks;
     }
     LT kb[NLD], vb[NLD];
-    if (!pre_issued) issue(ts.get(j0), ka, va);
-    pre_issued = false;
-    if constexpr (flat) prefetch();  // the next segment's set-up, behind this first block
     int j = j0;
     while (j + 2 < j1) {
       issue(ts.get(j + 1), kb, vb);

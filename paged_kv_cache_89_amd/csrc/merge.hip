@@ -108,12 +108,13 @@ __global__ __launch_bounds__(256) void merge_partitions_kernel(const MergeArgs a
       }
       q = PF;
     }
-    for (; q < cnt; q += PF) {  // further slots, PF loads in flight at a time; only the
-                                // slots that carry weight (cascade rows leave many empty)
+    for (; q < cnt; q += PF) {  // further slots, PF loads in flight at a time; of cascade
+                                // rows (many empty slots) only those that carry weight
       float y[PF][EPL];
 #pragma unroll
       for (int k = 0; k < PF; ++k) {
-        const bool want = q + k < cnt && __builtin_amdgcn_readlane(__float_as_int(w), q + k) != 0;
+        const bool want = !a.all_slots ||
+                          (q + k < cnt && __builtin_amdgcn_readlane(__float_as_int(w), q + k) != 0);
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
           y[k][e] = want ? pacc[(size_t)min(base + q + k, P - 1) * D + e] : 0.f;
