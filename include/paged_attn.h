@@ -376,7 +376,8 @@ pa_status pa_decode_append(void* out, const void* query, const void* k_new, cons
  *   seq_group      sequences per group; the batch is num_seqs / seq_group groups of
  *                  consecutive sequences (group g = sequences g*seq_group .. +seq_group-1)
  *   prefix_blocks  device [num_seqs / seq_group] int32: blocks shared by the group's
- *                  members.  Precondition: the first prefix_blocks[g] entries of the
+ *                  members (may be NULL when max_prefix_blocks is 0: nothing is shared
+ *                  and no launch reads it).  Precondition: the first prefix_blocks[g] entries of the
  *                  members' table rows are the same physical ids; the prefix launch reads
  *                  the first member's row only, so a violation gives that member's blocks
  *                  to every member (wrong numbers, no fault).  Values are clamped to

@@ -31,8 +31,9 @@
 //     v_readlane into scalar registers so the address of the next tile never waits on
 //     memory;
 //   * GQA (G query heads per KV head) reuses each loaded tile for all G heads;
-//   * e4m3 tiles are decoded in registers by the hardware fp8 converter; k_scale is
-//     folded into the logit scale and v_scale into the epilogue.
+//   * e4m3 tiles are decoded in registers by the hardware fp8 converters: K codes to the
+//     query's 16-bit type (exact), contracted with the same dot2 as a 16-bit cache, V
+//     codes to fp32; k_scale is folded into the logit scale and v_scale into the epilogue.
 #pragma once
 
 #include <type_traits>
@@ -204,25 +205,12 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
     // ---- query slice, kept packed (fp16/bf16 caches) or widened to fp32 (e4m3 caches)
     if constexpr (!flat) load_query(s, kvh, qraw);
     uint32_t qw[G][EPL / 2];
-    float qf[F8 ? G : 1][F8 ? EPL : 1];
     for (int g = 0; g < G; ++g) {
 #pragma unroll
       for (int k = 0; k < EPL / 8; ++k) {
         const u32x4 t = qraw[g][k];
 #pragma unroll
         for (int w = 0; w < 4; ++w) qw[g][4 * k + w] = t[w];
-      }
-      if constexpr (F8) {
-#pragma unroll
-        for (int w = 0; w < EPL / 2; ++w) {
-          if constexpr (QK == KIND_BF16) {
-            qf[g][2 * w] = bf16_lo(qw[g][w]);
-            qf[g][2 * w + 1] = bf16_hi(qw[g][w]);
-          } else {
-            qf[g][2 * w] = f16_lo(qw[g][w]);
-            qf[g][2 * w + 1] = f16_hi(qw[g][w]);
-          }
-        }
       }
     }
 
@@ -246,16 +234,22 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         if constexpr (F8) {
-          float kf[EPL];
+          // the codes widened to the query's 16-bit type (exact: every E4M3 value is an
+          // fp16 and a bf16 value), then the dot2 of a 16-bit cache
+          uint32_t kh[EPL / 2];
 #pragma unroll
-          for (int w = 0; w < W; ++w) e4m3x4_to_f32(kr[i][w], &kf[4 * w]);
+          for (int w = 0; w < W; ++w) {
+            const u32x2 t = e4m3x4_to_16<QK>(kr[i][w]);
+            kh[2 * w] = t[0];
+            kh[2 * w + 1] = t[1];
+          }
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; e += 2) {
-              d0 = fmaf(qf[g][e], kf[e], d0);
-              d1 = fmaf(qf[g][e + 1], kf[e + 1], d1);
+            for (int w = 0; w < EPL / 2; w += 2) {
+              d0 = dot2_16<QK>(qw[g][w], kh[w], d0);
+              d1 = dot2_16<QK>(qw[g][w + 1], kh[w + 1], d1);
             }
             sc[g][i] = d0 + d1;
           }
@@ -264,15 +258,7 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
           for (int g = 0; g < G; ++g) {
             float d = 0.f;
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-              if constexpr (KVK == KIND_F16)
-                d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw[g][w]),
-                                           __builtin_bit_cast(f16x2, (uint32_t)kr[i][w]), d, false);
-              else
-                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[g][w]),
-                                                    __builtin_bit_cast(bf16x2, (uint32_t)kr[i][w]),
-                                                    d, false);
-            }
+            for (int w = 0; w < W; ++w) d = dot2_16<KVK>(qw[g][w], (uint32_t)kr[i][w], d);
             sc[g][i] = d;
           }
         }

@@ -78,6 +78,28 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* o) {
   o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
 }
 
+// Four e4m3 codes of a dword -> their values as two dwords of packed fp16 or bf16 pairs
+// (codes 0, 1 and 2, 3), by the gfx950 scaled converter at scale 1.  Exact: every E4M3
+// value (at most 448 in magnitude, subnormals down to 2^-9) is an fp16 and a bf16 value.
+template <int K>
+__device__ __forceinline__ u32x2 e4m3x4_to_16(uint32_t w) {
+  if constexpr (K == KIND_BF16)
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+  else
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
+}
+
+// c + a.x * b.x + a.y * b.y over packed fp16 or bf16 pairs, fp32 result.
+template <int K>
+__device__ __forceinline__ float dot2_16(uint32_t a, uint32_t b, float c) {
+  if constexpr (K == KIND_BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
 // binary32 -> OCP E4M3 code, round to nearest even, saturating at +-448, NaN -> NaN.
 __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -509,6 +531,7 @@ __device__ __forceinline__ int part_share_blocks(const DecodeArgs& a, int jb, in
 // Tokens of its group's shared prefix that a sequence of length n attends (cascade modes):
 // the group's shared blocks, clamped to [0, max_prefix_blocks], in tokens, capped at n.
 __device__ __forceinline__ int prefix_tokens(const DecodeArgs& a, int group, int block_size, int n) {
+  if (a.max_prefix_blocks <= 0) return 0;  // prefix_blocks may then be null
   int pb = a.prefix_blocks[group];
   pb = pb < 0 ? 0 : (pb > a.max_prefix_blocks ? a.max_prefix_blocks : pb);
   const int t = pb * block_size;

@@ -57,7 +57,8 @@ def _cascade(case, tables, k, v, prefix_blocks, max_prefix_blocks, **kw):
     sp = case.spec
     out = pa.decode_shared_prefix(
         to_dev(case.q, sp.q_dtype), to_dev(k, sp.kv_dtype), to_dev(v, sp.kv_dtype),
-        dev_i32(tables), dev_i32(case.context_lens), dev_i32(prefix_blocks), sp.group_size,
+        dev_i32(tables), dev_i32(case.context_lens),
+        None if prefix_blocks is None else dev_i32(prefix_blocks), sp.group_size,
         int(case.context_lens.max()), max_prefix_blocks, sp.scale, case.k_scale, case.v_scale,
         **kw)
     torch.cuda.synchronize()
@@ -136,6 +137,20 @@ def test_prefix_bound_clamps_and_equals_plain_decode():
         compare(x, ref, atol, rrel, "bf16")
     again = _f64(_cascade(case, tables, k, v, np.array([5, 5], np.int32), 5))
     assert np.array_equal(a, again)
+
+
+def test_no_shared_blocks_without_a_prefix_array():
+    """max_prefix_blocks = 0 lets prefix_blocks be NULL: nothing is shared, no launch reads
+    the array, and the result is the plain decode's."""
+    B, K = 16, 2
+    lens = [40, 0, 17, 300]
+    for kvd in ("bf16", "e4m3"):
+        case, tables, k, v = _shared_case(1, K, 128, B, "bf16", kvd, lens, 0, 19)
+        ref = oracle_decode(case, tables, k, v)
+        atol, rrel = tolerance(case.spec)
+        out = _f64(_cascade(case, tables, k, v, None, 0))
+        assert (out[1] == 0).all()
+        compare(out, ref, atol, rrel, "bf16")
 
 
 def test_full_size_fp8_shared_prompts_all_rows():
