@@ -192,6 +192,8 @@ __device__ __forceinline__ float rows_sum(float x) {
 // One 16-byte-per-lane load from global memory into LDS: lane l's 16 bytes land at LDS
 // byte lds + 16 l (the wave fills 1 KiB).  The LDS address travels in M0; the statement
 // saves M0 first and restores it after, so whatever the compiler keeps there survives.
+// (M0 is a reserved register: clang treats naming it as clobbered as undefined behaviour,
+// and never assigns reserved registers to asm operands, so saving it is the sound form.)
 // vmcnt drops once the bytes are in LDS (wait_vmcnt).  The stage being refilled was read by
 // the block before: lgkmcnt(0) first, so those reads have returned before the new bytes can
 // land.  (The compiler's global_load_lds builtin is not used: the compiler then waits for
