@@ -77,6 +77,28 @@ def test_multi_token_matches_oracle_all_variants(d, dt):
                     compare(out.reshape(-1, d), ref.reshape(-1, d), atol, rrel, qd)
 
 
+def test_flat_merge_of_more_rows_than_resident_wavefronts():
+    """255 sequences x 4 draft tokens x 9 heads = 9,180 rows under the flat split, more
+    than the merge's wavefronts an MI355X holds at once."""
+    B, Hkv, T, d = 16, 9, 4, 64
+    rng = np.random.default_rng(8960)
+    lens = rng.integers(3, 401, 255).tolist()
+    lens[0] = 0
+    sp = workloads.Spec("rows", len(lens), Hkv, Hkv, d, B, 0, 0,
+                        sum(math.ceil(n / B) for n in lens) + 5, math.ceil(max(lens) / B) + 2,
+                        "bf16", "bf16", 1 / math.sqrt(d))
+    case = workloads.generate(sp, 8961, context_lens=lens)
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    qm = workloads._round_bits(rng.standard_normal((len(lens), T, Hkv, d), dtype=np.float32), "bf16")
+    assert pa.decode_plan(len(lens), Hkv, Hkv, d, B, max(lens), 0, pa.BF16)[2] > 0
+    ref = oracle.decode_multi(qm, DT["bf16"], k, v, DT["bf16"], tables, case.context_lens, Hkv, B,
+                              sp.scale, case.k_scale, case.v_scale, tree_masks=None)
+    out = _run(case, tables, k, v, qm, None)
+    assert (out[0] == 0).all()
+    compare(out.reshape(-1, d), ref.reshape(-1, d), *tolerance(sp), "bf16")
+
+
 def test_multi_token_causal_row_equals_plain_decode_of_truncated_length():
     """Query token t of a causal draft gives what pa_decode gives for the same query with
     context length n - T + 1 + t, to rounding."""

@@ -321,6 +321,27 @@ def test_merge_of_many_partitions(qd, G):
     compare(out, ref, *tolerance(sp), qd)
 
 
+def test_merge_of_more_rows_than_resident_wavefronts():
+    """8,195 rows of at most three partitions, more than the merge's wavefronts an MI355X
+    holds at once (two rounds of them, the last workgroup partly filled); rows of 0, 1, 2
+    and 3 partials."""
+    B, P = 8, 32
+    rng = np.random.default_rng(8950)
+    lens = rng.integers(0, 97, 8195).tolist()
+    lens[:4] = [0, 32, 33, 96]
+    sp = workloads.Spec("rows", len(lens), 1, 1, 64, B, 1, 1,
+                        sum(math.ceil(n / B) for n in lens) + 5, math.ceil(96 / B) + 1,
+                        "f16", "f16", 1 / 8)
+    case = workloads.generate(sp, 8951, context_lens=lens)
+    tables, _, _ = oracle_tables(case)
+    k, v = oracle_caches(case, tables)
+    ref = oracle_decode(case, tables, k, v)
+    assert pa.decode_plan(sp.num_seqs, 1, 1, 64, B, 96, P)[1] == 3
+    out = _f64(_gpu_decode(case, tables, k, v, partition_size=P))
+    assert (out[0] == 0).all()
+    compare(out, ref, *tolerance(sp), "f16")
+
+
 def test_partition_size_invariance_and_determinism():
     case = workloads.generate(workloads.SMALL["long_split"], 8900 + 24)
     sp = case.spec
