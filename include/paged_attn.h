@@ -368,10 +368,12 @@ pa_status pa_decode_append(void* out, const void* query, const void* k_new, cons
  * [P1] sec. 3) for batches in which groups of sequences share their leading blocks: the
  * K samples of one prompt ([P1] sec. 5, parallel sampling) or the sessions behind one
  * pinned system prompt ([P1] sec. 5, prefix sharing).  The shared blocks are read from HBM
- * once per group: one launch attends the queries of all members to the group's prefix
- * (the member queries become the columns of one matrix-core contraction per block), a
- * second attends every sequence to its own remaining tokens, and the partial (max, sum,
- * output) triples are combined by the log-sum-exp merge (the rescaling of [P1] sec. 7).
+ * once per group: prefix units attend the queries of all members to the group's prefix
+ * (the member queries become the columns of one matrix-core contraction per block),
+ * per-sequence units attend every sequence to its own remaining tokens, and the partial
+ * (max, sum, output) triples are combined by the log-sum-exp merge (the rescaling of [P1]
+ * sec. 7).  The two kinds of unit run as two launches, or as one (prefix units' workgroups
+ * first) for an e4m3 cache with num_heads == num_kv_heads; the merge is one more launch.
  *   Arguments as for pa_decode, plus:
  *   seq_group      sequences per group; the batch is num_seqs / seq_group groups of
  *                  consecutive sequences (group g = sequences g*seq_group .. +seq_group-1)

@@ -24,7 +24,7 @@ MFMA_SOURCES = ["decode_gqa_d64_nt.hip", "decode_gqa_d64_t.hip", "decode_gqa_d12
                 "decode_gqa_d128_t.hip"]
 SOURCES = ["api.hip", "validate.hip", "block_manager.cpp", "write_kv.hip", "merge.hip", "copy_blocks.hip",
            "decode_d64_nt.hip", "decode_d64_t.hip", "decode_d128_nt.hip", "decode_d128_t.hip",
-           "decode_gqa.hip", *MFMA_SOURCES]
+           "decode_gqa.hip", "decode_cascade.hip", *MFMA_SOURCES]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",
@@ -35,7 +35,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}",
 
 # Per-source extra flags.  The matrix-core kernels keep their MFMA accumulators in
 # ordinary VGPRs (no AGPR round trips around the loop's rarely taken rescale branch).
-EXTRA = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for src in MFMA_SOURCES}
+EXTRA = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for src in [*MFMA_SOURCES, "decode_cascade.hip"]}
 
 
 def _compile(src: str) -> str:

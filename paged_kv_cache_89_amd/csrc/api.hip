@@ -76,6 +76,11 @@ constexpr int32_t kAutoPartitionMfma = 1024;
 #define PA_BALANCED_XCD 1
 #endif
 constexpr int32_t kCascadePartition = 512;
+// 1: e4m3 shared-prefix decodes with one query head per KV head run their prefix and
+// per-sequence units in one launch (compile-time switch for measurements)
+#ifndef PA_CASCADE_ONE_LAUNCH
+#define PA_CASCADE_ONE_LAUNCH 1
+#endif
 // Partials are stored and merged with 8- and 16-byte vector accesses.
 constexpr uintptr_t kWorkspaceAlign = 16;
 // Shortest share of a row's own blocks in the shared-prefix decode's per-sequence launch.
@@ -750,21 +755,42 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
                  "max_prefix_blocks=%d P=%d prefix_parts=%d suffix_parts=%d\n",
                  num_seqs, seq_group, num_heads, num_kv_heads, head_dim, block_size, max_ctx,
                  max_prefix_blocks, cp.partition_size, cp.pre_parts, cp.suf_parts);
+  // The per-sequence units' arguments.  The remaining tokens are mostly private:
+  // neighbouring units take neighbouring heads of the same blocks (contiguous lines);
+  // PA_DECODE_SHARED_KV only keeps the loads cacheable.
+  DecodeArgs own = a;
+  own.mode = MODE_SUFFIX; own.slot_base = cp.pre_parts; own.num_parts = cp.suf_parts;
+  own.part_min_blocks = cp.suf_min_blocks;
+  own.num_units = (int32_t)suf_units; own.seq_fastest = 0;
   if (cp.pre_parts > 0) {
     a.mode = MODE_PREFIX; a.slot_base = 0; a.num_parts = cp.pre_parts;
     a.num_units = (int32_t)pre_units; a.seq_fastest = 0;
-    st = hip_status(launch_decode_gqa_mfma(pre_shape, a, (hipStream_t)stream),
-                    "pa_decode_shared_prefix prefix launch");
+    if (PA_CASCADE_ONE_LAUNCH && cascade_fp8_supported(pre_shape, G)) {
+      // e4m3, one query head per KV head: both kinds of unit in one launch, prefix units'
+      // workgroups first (their count rounded up to a multiple of 8, so the per-sequence
+      // workgroups keep their XCDs)
+      const int64_t pre_wg = ((pre_units + 3) / 4 + 7) / 8 * 8;
+      const int64_t own_wg = (suf_units + 3) / 4;
+      if (pre_wg + own_wg > (int64_t)1 << 30)
+        return fail(PA_ERR_UNSUPPORTED, std::string(who) + ": grid too large");
+      a.wg_base = 0; a.wg_count = (int32_t)pre_wg;
+      own.wg_base = (int32_t)pre_wg; own.wg_count = (int32_t)own_wg;
+      st = hip_status(launch_cascade_fp8(pre_shape, a, own, suf_shape.nontemporal, (hipStream_t)stream),
+                      "pa_decode_shared_prefix launch");
+      if (st != PA_OK) return st;
+    } else {
+      st = hip_status(launch_decode_gqa_mfma(pre_shape, a, (hipStream_t)stream),
+                      "pa_decode_shared_prefix prefix launch");
+      if (st != PA_OK) return st;
+      st = hip_status(launch_decode(suf_shape, own, (hipStream_t)stream),
+                      "pa_decode_shared_prefix suffix launch");
+      if (st != PA_OK) return st;
+    }
+  } else {
+    st = hip_status(launch_decode(suf_shape, own, (hipStream_t)stream),
+                    "pa_decode_shared_prefix suffix launch");
     if (st != PA_OK) return st;
   }
-  // The remaining tokens are mostly private: neighbouring units take neighbouring heads of
-  // the same blocks (contiguous lines); PA_DECODE_SHARED_KV only keeps the loads cacheable.
-  a.mode = MODE_SUFFIX; a.slot_base = cp.pre_parts; a.num_parts = cp.suf_parts;
-  a.part_min_blocks = cp.suf_min_blocks;
-  a.num_units = (int32_t)suf_units; a.seq_fastest = 0;
-  st = hip_status(launch_decode(suf_shape, a, (hipStream_t)stream),
-                  "pa_decode_shared_prefix suffix launch");
-  if (st != PA_OK) return st;
   MergeArgs m;
   m.out = out; m.part_acc = a.part_acc; m.part_ml = a.part_ml; m.ctx = context_lens;
   m.num_seqs = num_seqs; m.num_heads = num_heads; m.num_parts = slots;

@@ -227,9 +227,9 @@ constexpr int gqa_min_waves(int kvk, bool lane, int g) {
                           : (PA_LDS_DMA_16 != 0 ? 2 : PA_GQA_MIN_WAVES);
 }
 
+// The kernel body, also run by the one-launch cascade (decode_cascade.hip).
 template <int D, int QK, int KVK, int G, bool NT, bool LANE, bool FLAT>
-__global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) void paged_decode_gqa_mfma_kernel(
-    const DecodeArgs a) {
+__device__ __forceinline__ void gqa_body(const DecodeArgs& a) {
   constexpr int BS = 16;
   constexpr int KSTEPS = D / 32;             // 16x16x32 steps over the head dimension
   constexpr int NTILES = D / 16;             // 16-wide output slices
@@ -828,6 +828,12 @@ __global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) voi
       *(u32x4*)((char*)a.v + dst) = nv;
     }
   }
+}
+
+template <int D, int QK, int KVK, int G, bool NT, bool LANE, bool FLAT>
+__global__ __launch_bounds__(64 * PA_GQA_WAVES, gqa_min_waves(KVK, LANE, G)) void paged_decode_gqa_mfma_kernel(
+    const DecodeArgs a) {
+  gqa_body<D, QK, KVK, G, NT, LANE, FLAT>(a);
 }
 
 template <int D, int QK, int KVK, int G, bool NT>

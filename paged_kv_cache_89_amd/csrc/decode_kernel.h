@@ -71,8 +71,9 @@ template <> struct LoadVec<2> { using T = u32x2; };
 // NT: K/V loads carry the non-temporal hint (data read once per step).  APP: the appending
 // decode, FLAT: the flat split (separate instantiations, so the plain decode over fixed
 // partitions carries none of their registers).
+// The kernel body, also run by the one-launch cascade (decode_cascade.hip).
 template <int D, int BS, int QK, int KVK, int G, bool NT, bool APP, bool FLAT>
-__global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using Geo = TileGeometry<D, BS, KVK>;
   using LT = typename LoadVec<Geo::W>::T;
   constexpr int W = Geo::W, EPL = Geo::EPL, LPT = Geo::LPT, TPL = Geo::TPL, NLD = Geo::NLD;
@@ -464,6 +465,11 @@ __global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(cons
       *(LT*)((char*)a.v + dst) = nv;
     }
   }
+}
+
+template <int D, int BS, int QK, int KVK, int G, bool NT, bool APP, bool FLAT>
+__global__ __launch_bounds__(64 * PA_DECODE_WAVES) void paged_decode_kernel(const DecodeArgs a) {
+  decode_body<D, BS, QK, KVK, G, NT, APP, FLAT>(a);
 }
 
 template <int D, int BS, int QK, int KVK, int G, bool NT>

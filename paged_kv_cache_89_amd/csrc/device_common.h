@@ -247,9 +247,11 @@ struct UnitCoords {
 
 __device__ __forceinline__ UnitCoords remapped_coords(const DecodeArgs& a, int waves, int wave,
                                                       int rows) {
-  int wg = blockIdx.x;
+  // (a launch's workgroups may be a range of a larger grid: the one-launch cascade)
+  int wg = (int)blockIdx.x - a.wg_base;
   if (a.xcd_remap != 0) {
-    const int G8 = gridDim.x, x = wg % 8, loc = wg / 8, per = G8 / 8, rem = G8 % 8;
+    const int G8 = a.wg_count > 0 ? a.wg_count : (int)gridDim.x;
+    const int x = wg % 8, loc = wg / 8, per = G8 / 8, rem = G8 % 8;
     wg = (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
   }
   const int unit = wg * waves + wave;

@@ -94,6 +94,10 @@ struct DecodeArgs {
   // decode leaves the chunk length it chose
   int32_t flat_min_blocks = 0;
   int32_t* flat_meta = nullptr;
+  // Fixed partitions inside a larger grid (the one-launch cascade): this part's workgroups
+  // are [wg_base, wg_base + wg_count) of the grid; wg_base is a multiple of 8, so each keeps
+  // its XCD (0 / 0: the whole grid)
+  int32_t wg_base = 0, wg_count = 0;
 };
 
 struct DecodeShape {
@@ -117,6 +121,12 @@ inline dim3 decode_grid(const DecodeArgs& a, int waves, const void* kernel = nul
 
 bool decode_supported(const DecodeShape& s);
 hipError_t launch_decode(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
+// The shared-prefix decode of an e4m3 cache with one query head per KV head in one launch:
+// `pre` (prefix units, workgroups [0, own.wg_base)) and `own` (per-sequence units,
+// workgroups [own.wg_base, own.wg_base + own.wg_count)); own.wg_base is a multiple of 8.
+bool cascade_fp8_supported(const DecodeShape& pre_shape, int heads_per_kv);
+hipError_t launch_cascade_fp8(const DecodeShape& pre_shape, const DecodeArgs& pre,
+                              const DecodeArgs& own, bool nt_own, hipStream_t stream);
 // The matrix-core kernel alone (the only one that runs shared-prefix units).
 bool gqa_mfma_supported(const DecodeShape& s);
 hipError_t launch_decode_gqa_mfma(const DecodeShape& s, const DecodeArgs& a, hipStream_t stream);
