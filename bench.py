@@ -190,9 +190,13 @@ def main():
         shared_tok = np.minimum(prefix_blocks * B, ctx.reshape(-1, sp.group_size).max(axis=1))
         own = ctx - np.minimum(np.repeat(prefix_blocks * B, sp.group_size), ctx)
         unique_bytes = workloads.kv_bytes(sp, np.concatenate([shared_tok, own]))
-        cascade_plan = pa.decode_shared_prefix_plan(S, Hq, Hkv, D, B, max_ctx, max_pb, P)
-        kernels = ("paged_decode_gqa_mfma_kernel (group prefixes) + paged_decode_kernel "
-                   "(own tokens) + merge_partitions_kernel")
+        cascade_plan = pa.decode_shared_prefix_plan(S, Hq, Hkv, D, B, max_ctx, max_pb, P,
+                                                    pa.FP8_E4M3 if sp.kv_dtype == "e4m3" else
+                                                    pa.BF16 if sp.kv_dtype == "bf16" else pa.F16)
+        kernels = ("cascade_fp8_kernel (group prefixes and own tokens in one launch)"
+                   if cascade_plan["decode_launches"] == 1 else
+                   "paged_decode_gqa_mfma_kernel (group prefixes) + paged_decode_kernel "
+                   "(own tokens)") + " + merge_partitions_kernel"
 
         def decode(layer):
             lk, lv, ks, vs = layers[layer]

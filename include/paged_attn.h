@@ -393,7 +393,7 @@ pa_status pa_decode_append(void* out, const void* query, const void* k_new, cons
  *                  block once).  Results are identical either way.
  *   partition_size 0 = library choice: prefix partitions of a planned size, and each
  *                  row's own blocks split into equal shares (at least 8 blocks each);
- *                  else a positive multiple of block_size used by both launches
+ *                  else a positive multiple of block_size used by both kinds of unit
  *   workspace      at least pa_decode_shared_prefix_workspace_size(...) bytes (never 0
  *                  for num_seqs > 0: the two launches always leave partials)
  * Supported: what the matrix-core decode covers for the group's queries: block_size 16,
@@ -406,18 +406,21 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_head
                                               int32_t max_prefix_blocks,
                                               int32_t partition_size);
 
-/* The plan pa_decode_shared_prefix makes for these arguments (host only, nothing launched):
- * the partition length of the prefix launch (tokens), the partial slots per row that the
- * prefix launch and the per-sequence launch own (prefix_slots + suffix_slots in all, the
- * merge's input), and the shortest share of a row's own blocks in the per-sequence launch
- * (0 = fixed partitions of prefix_partition_size tokens instead of equal shares).  Any
- * output pointer may be NULL. */
+/* The plan pa_decode_shared_prefix makes for these arguments and a cache of kv_dtype (host
+ * only, nothing launched): the partition length of the prefix units (tokens), the partial
+ * slots per row that the prefix units and the per-sequence units own (prefix_slots +
+ * suffix_slots in all, the merge's input), the shortest share of a row's own blocks in the
+ * per-sequence units (0 = fixed partitions of prefix_partition_size tokens instead of equal
+ * shares), and the decode launches before the merge (1: both kinds of unit in one launch,
+ * e4m3 caches with num_heads == num_kv_heads and a prefix to share; else 2, or 1 when
+ * max_prefix_blocks is 0).  Any output pointer may be NULL. */
 pa_status pa_decode_shared_prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size,
                                        int32_t max_context_len, int32_t max_prefix_blocks,
-                                       int32_t partition_size, int32_t* prefix_partition_size,
-                                       int32_t* prefix_slots, int32_t* suffix_slots,
-                                       int32_t* suffix_min_blocks);
+                                       int32_t partition_size, pa_dtype kv_dtype,
+                                       int32_t* prefix_partition_size, int32_t* prefix_slots,
+                                       int32_t* suffix_slots, int32_t* suffix_min_blocks,
+                                       int32_t* decode_launches);
 
 pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_cache,
                                   const void* v_cache, const int32_t* block_tables,

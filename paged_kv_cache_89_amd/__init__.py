@@ -90,7 +90,7 @@ def lib() -> ctypes.CDLL:
     L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                    i32, i32, i32, f32, c.c_int, c.c_int, f32, f32, f32, f32,
                                    i32, c.c_uint32, vp, sz, vp]
-    L.pa_decode_shared_prefix_plan.argtypes = [i32] * 8 + [vp] * 4
+    L.pa_decode_shared_prefix_plan.argtypes = [i32] * 8 + [c.c_int] + [vp] * 5
     L.pa_decode_shared_prefix_workspace_size.argtypes = [i32] * 8
     L.pa_decode_shared_prefix_workspace_size.restype = sz
     L.pa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -439,16 +439,18 @@ def decode_append(query, k_new, v_new, k_cache, v_cache, block_tables, context_l
 
 
 def decode_shared_prefix_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                              max_context_len, max_prefix_blocks, partition_size=0) -> dict:
-    """The plan pa_decode_shared_prefix makes: prefix partition length (tokens), partial slots
-    per row of the prefix and per-sequence launches, shortest per-sequence share (blocks)."""
-    v = np.zeros(4, np.int32)
+                              max_context_len, max_prefix_blocks, partition_size=0,
+                              kv_dtype: int = F16) -> dict:
+    """The plan pa_decode_shared_prefix makes for a cache of kv_dtype: prefix partition
+    length (tokens), partial slots per row of the prefix and per-sequence units, shortest
+    per-sequence share (blocks), decode launches before the merge."""
+    v = np.zeros(5, np.int32)
     _check(lib().pa_decode_shared_prefix_plan(
         num_seqs, num_heads, num_kv_heads, head_dim, block_size, int(max_context_len),
-        int(max_prefix_blocks), int(partition_size), _ptr(v[0:1]), _ptr(v[1:2]), _ptr(v[2:3]),
-        _ptr(v[3:4])))
+        int(max_prefix_blocks), int(partition_size), int(kv_dtype), _ptr(v[0:1]), _ptr(v[1:2]),
+        _ptr(v[2:3]), _ptr(v[3:4]), _ptr(v[4:5])))
     return {"prefix_partition_size": int(v[0]), "prefix_slots": int(v[1]),
-            "suffix_slots": int(v[2]), "suffix_min_blocks": int(v[3])}
+            "suffix_slots": int(v[2]), "suffix_min_blocks": int(v[3]), "decode_launches": int(v[4])}
 
 
 def decode_shared_prefix_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,

@@ -76,6 +76,10 @@ constexpr int32_t kAutoPartitionMfma = 1024;
 #define PA_BALANCED_XCD 1
 #endif
 constexpr int32_t kCascadePartition = 512;
+// The one-launch e4m3 cascade starts from 1024-token prefix partitions: its prefix units
+// then fill about half of the wavefront slots and per-sequence units the rest from the
+// start (measured on the fp8 shared-prompt workload: 184.9 vs 192.5 us, merge 5.3 vs 5.6 us).
+constexpr int32_t kCascadeFusedPartition = 1024;
 // 1: e4m3 shared-prefix decodes with one query head per KV head run their prefix and
 // per-sequence units in one launch (compile-time switch for measurements)
 #ifndef PA_CASCADE_ONE_LAUNCH
@@ -182,11 +186,12 @@ struct CascadePlan {
 pa_status make_cascade_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t block_size, int32_t max_context_len,
                             int32_t max_prefix_blocks, int32_t partition_size,
-                            CascadePlan* cp) {
+                            CascadePlan* cp, bool one_launch = false) {
   if (max_prefix_blocks < 0) return fail(PA_ERR_INVALID_ARG, "shared-prefix plan: max_prefix_blocks < 0");
   Plan p;
   const pa_status st = make_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                 max_context_len, partition_size, &p, kCascadePartition);
+                                 max_context_len, partition_size, &p,
+                                 one_launch ? kCascadeFusedPartition : kCascadePartition);
   if (st != PA_OK) return st;
   int64_t P = p.partition_size;
   if (P == 0) {
@@ -215,6 +220,15 @@ pa_status make_cascade_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_
     cp->suf_min_blocks = kSuffixMinBlocks;
   }
   return PA_OK;
+}
+
+// Whether pa_decode_shared_prefix runs its prefix and per-sequence units in one launch:
+// an e4m3 cache with one query head per KV head (the shapes pa_decode_shared_prefix
+// supports otherwise), with a shared prefix to read.
+bool cascade_one_launch(int32_t num_heads, int32_t num_kv_heads, int32_t block_size,
+                        int32_t head_dim, int kv_kind, int32_t max_prefix_blocks) {
+  return PA_CASCADE_ONE_LAUNCH && kv_kind == KIND_E4M3 && num_heads == num_kv_heads &&
+         block_size == 16 && (head_dim == 64 || head_dim == 128) && max_prefix_blocks > 0;
 }
 
 size_t cascade_workspace_bytes(const CascadePlan& cp, int32_t num_seqs, int32_t num_heads,
@@ -634,28 +648,40 @@ size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_head
                                               int32_t block_size, int32_t max_context_len,
                                               int32_t max_prefix_blocks,
                                               int32_t partition_size) {
-  CascadePlan cp;
+  // enough for either plan (the cache dtype is not an argument): the one-launch plan's
+  // longer prefix partitions never need more slots than the two-launch plan's
+  CascadePlan two, one;
   if (make_cascade_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                        max_context_len, max_prefix_blocks, partition_size, &cp) != PA_OK)
+                        max_context_len, max_prefix_blocks, partition_size, &two) != PA_OK ||
+      make_cascade_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                        max_context_len, max_prefix_blocks, partition_size, &one, true) != PA_OK)
     return 0;
-  return cascade_workspace_bytes(cp, num_seqs, num_heads, head_dim);
+  return std::max(cascade_workspace_bytes(two, num_seqs, num_heads, head_dim),
+                  cascade_workspace_bytes(one, num_seqs, num_heads, head_dim));
 }
 
 pa_status pa_decode_shared_prefix_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t block_size,
                                        int32_t max_context_len, int32_t max_prefix_blocks,
-                                       int32_t partition_size, int32_t* prefix_partition_size,
-                                       int32_t* prefix_slots, int32_t* suffix_slots,
-                                       int32_t* suffix_min_blocks) {
+                                       int32_t partition_size, pa_dtype kv_dtype,
+                                       int32_t* prefix_partition_size, int32_t* prefix_slots,
+                                       int32_t* suffix_slots, int32_t* suffix_min_blocks,
+                                       int32_t* decode_launches) {
   g_last_error.clear();
+  int kk;
+  if (!dtype_kind(kv_dtype, &kk)) return fail(PA_ERR_INVALID_ARG, "shared-prefix plan: unknown dtype");
+  const bool one = cascade_one_launch(num_heads, num_kv_heads, block_size, head_dim, kk,
+                                      max_prefix_blocks);
   CascadePlan cp;
   const pa_status st = make_cascade_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                         max_context_len, max_prefix_blocks, partition_size, &cp);
+                                         max_context_len, max_prefix_blocks, partition_size, &cp,
+                                         one);
   if (st != PA_OK) return st;
   if (prefix_partition_size) *prefix_partition_size = cp.partition_size;
   if (prefix_slots) *prefix_slots = cp.pre_parts;
   if (suffix_slots) *suffix_slots = cp.suf_parts;
   if (suffix_min_blocks) *suffix_min_blocks = cp.suf_min_blocks;
+  if (decode_launches) *decode_launches = (one && cp.pre_parts > 0) ? 1 : (cp.pre_parts > 0 ? 2 : 1);
   return PA_OK;
 }
 
@@ -706,9 +732,12 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
 
   const int64_t reach = (int64_t)max_blocks_per_seq * block_size;
   const int32_t max_ctx = (int32_t)(max_context_len < reach ? max_context_len : reach);
+  const bool one_launch = cascade_one_launch(num_heads, num_kv_heads, block_size, head_dim, kk,
+                                            max_prefix_blocks);
   CascadePlan cp;
   pa_status st = make_cascade_plan(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                   max_context_len, max_prefix_blocks, partition_size, &cp);
+                                   max_context_len, max_prefix_blocks, partition_size, &cp,
+                                   one_launch);
   if (st != PA_OK) return st;
   const size_t need = cascade_workspace_bytes(cp, num_seqs, num_heads, head_dim);
   if (!workspace || workspace_bytes_given < need)
@@ -765,7 +794,7 @@ pa_status pa_decode_shared_prefix(void* out, const void* query, const void* k_ca
   if (cp.pre_parts > 0) {
     a.mode = MODE_PREFIX; a.slot_base = 0; a.num_parts = cp.pre_parts;
     a.num_units = (int32_t)pre_units; a.seq_fastest = 0;
-    if (PA_CASCADE_ONE_LAUNCH && cascade_fp8_supported(pre_shape, G)) {
+    if (one_launch && cascade_fp8_supported(pre_shape, G)) {
       // e4m3, one query head per KV head: both kinds of unit in one launch, prefix units'
       // workgroups first (their count rounded up to a multiple of 8, so the per-sequence
       // workgroups keep their XCDs)

@@ -227,8 +227,16 @@ def test_shared_prefix_workspace_and_errors_without_gpu():
         assert pa.decode_shared_prefix_workspace_size(*args) == S * Hq * slots * (d + 2) * 4
     assert pa.decode_shared_prefix_plan(256, 32, 32, 128, 16, 1536, 64) == {
         "prefix_partition_size": 512, "prefix_slots": 2, "suffix_slots": 2,
-        "suffix_min_blocks": 8}
+        "suffix_min_blocks": 8, "decode_launches": 2}
     assert pa.decode_shared_prefix_plan(256, 32, 32, 128, 16, 1536, 64, 512)["suffix_min_blocks"] == 0
+    # an e4m3 cache with one query head per KV head: both kinds of unit in one launch, with
+    # 1024-token prefix partitions (1 prefix slot); the workspace covers either plan
+    one = pa.decode_shared_prefix_plan(256, 32, 32, 128, 16, 1536, 64, 0, pa.FP8_E4M3)
+    assert one == {"prefix_partition_size": 1024, "prefix_slots": 1, "suffix_slots": 2,
+                   "suffix_min_blocks": 8, "decode_launches": 1}
+    assert pa.decode_shared_prefix_plan(256, 32, 8, 128, 16, 1536, 64, 0, pa.FP8_E4M3)["decode_launches"] == 2
+    assert pa.decode_shared_prefix_plan(256, 32, 32, 128, 16, 1536, 0, 0, pa.FP8_E4M3)["decode_launches"] == 1
+    assert pa.decode_shared_prefix_plan(256, 32, 32, 128, 16, 1536, 64, 512, pa.FP8_E4M3)["prefix_partition_size"] == 512
     L = pa.lib()
 
     def call(S=8, K=4, Hq=8, Hkv=8, d=128, B=16, q=1, kv=2, flags=0):
