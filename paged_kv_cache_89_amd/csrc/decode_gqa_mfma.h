@@ -440,6 +440,15 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a) {
         lo = hi = (c < G) ? n : 0;
       }
     }
+    // Every query column (c < G) sees all tokens below lo_min: a block that ends there
+    // needs only the column mask (the per-column bounds matter at a segment's edges only).
+    int lo_min = n;
+    if constexpr (LANE) {
+      int v = (c < G) ? lo : 0x7fffffff;  // columns of lanes 0..15 (the rows repeat them)
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) v = min(v, __shfl_xor(v, off));
+      lo_min = __builtin_amdgcn_readfirstlane(v);
+    }
     auto row_of = [&](int cc) -> size_t { return row_at(s, kvh, cc); };
     auto issue = [&](int jj, int st) { issue_at(ts, kvh, jj, st); };
     if constexpr (DMA) {
@@ -634,12 +643,17 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a) {
     // online-softmax weights and P . V for block j (MASK: the block holds slots >= n)
     auto finish = [&](int j, f32x4 sv) {
       float z[4];
+      if (j * BS + BS <= lo_min) {  // (wave-uniform) the block lies below every bound
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = j * BS + 4 * r + i;
-        const bool ok = LANE ? (t < lo || (t < hi && ((tm >> ((t - lo) & 31)) & 1u)))
-                             : (c < G && t < n);
-        z[i] = ok ? sv[i] * qk_scale : -INFINITY;
+        for (int i = 0; i < 4; ++i) z[i] = c < G ? sv[i] * qk_scale : -INFINITY;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = j * BS + 4 * r + i;
+          const bool ok = LANE ? (t < lo || (t < hi && ((tm >> ((t - lo) & 31)) & 1u)))
+                               : (c < G && t < n);
+          z[i] = ok ? sv[i] * qk_scale : -INFINITY;
+        }
       }
       float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
       bm = rows_max(bm);
