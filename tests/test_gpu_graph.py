@@ -131,12 +131,15 @@ def test_appending_decode_replays():
         assert np.array_equal(to_bits(kd), ref[1]) and np.array_equal(to_bits(vd), ref[2])
 
 
-def test_shared_prefix_and_multi_token_replay():
+@pytest.mark.parametrize("Hq", [4, 2])
+def test_shared_prefix_and_multi_token_replay(Hq):
+    """Hq = 4 over 2 KV heads: the cascade's two decode launches; Hq = 2: its one launch
+    (e4m3 cache, one query head per KV head)."""
     K, B, prompt = 4, 16, 64
     lens = [70, 90, 64, 100, 80, 65, 120, 66]
     S = len(lens)
     need = (S // K) * (prompt // B) + sum(max(0, math.ceil(n / B) - prompt // B) for n in lens) + 5
-    sp = workloads.Spec("casc", S, 4, 2, 128, B, 0, 0, need, 10, "bf16", "e4m3",
+    sp = workloads.Spec("casc", S, Hq, 2, 128, B, 0, 0, need, 10, "bf16", "e4m3",
                         1 / math.sqrt(128), group_size=K, prompt_len=prompt)
     case = workloads.generate(sp, 8900 + 51, context_lens=lens)
     tables, _, _ = oracle_tables(case)
@@ -144,7 +147,7 @@ def test_shared_prefix_and_multi_token_replay():
     q, kd, vd = to_dev(case.q, "bf16"), to_dev(k, "e4m3"), to_dev(v, "e4m3")
     td, cd = dev_i32(tables), dev_i32(case.context_lens)
     pb = dev_i32(np.full(S // K, prompt // B, np.int32))
-    Hq, Hkv, D, mc, T = 4, 2, 128, max(lens), 2
+    Hkv, D, mc, T = 2, 128, max(lens), 2
     ws_sp = torch.empty(pa.decode_shared_prefix_workspace_size(S, Hq, Hkv, D, B, mc, prompt // B),
                         dtype=torch.uint8, device="cuda")
     out_sp = torch.empty_like(q)
