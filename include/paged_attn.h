@@ -380,7 +380,7 @@ pa_status pa_decode_append(void* out, const void* query, const void* k_new, cons
  *   prefix_blocks  device [num_seqs / seq_group] int32: blocks shared by the group's
  *                  members (may be NULL when max_prefix_blocks is 0: nothing is shared
  *                  and no launch reads it).  Precondition: the first prefix_blocks[g] entries of the
- *                  members' table rows are the same physical ids; the prefix launch reads
+ *                  members' table rows are the same physical ids; the prefix units read
  *                  the first member's row only, so a violation gives that member's blocks
  *                  to every member (wrong numbers, no fault).  Values are clamped to
  *                  [0, max_prefix_blocks]; a member shorter than the prefix attends its
@@ -388,17 +388,17 @@ pa_status pa_decode_append(void* out, const void* query, const void* k_new, cons
  *                  precondition holds.
  *   max_prefix_blocks  host upper bound of prefix_blocks (sizes the prefix grid)
  *   flags          0, or PA_DECODE_SHARED_KV when blocks after the group prefixes are still
- *                  shared (e.g. between beams): the per-sequence launch then keeps its K/V
- *                  loads cacheable.  The prefix launch always streams (it reads each shared
+ *                  shared (e.g. between beams): the per-sequence units then keep their K/V
+ *                  loads cacheable.  The prefix units always stream (they read each shared
  *                  block once).  Results are identical either way.
  *   partition_size 0 = library choice: prefix partitions of a planned size, and each
  *                  row's own blocks split into equal shares (at least 8 blocks each);
  *                  else a positive multiple of block_size used by both kinds of unit
  *   workspace      at least pa_decode_shared_prefix_workspace_size(...) bytes (never 0
- *                  for num_seqs > 0: the two launches always leave partials)
+ *                  for num_seqs > 0: both kinds of unit always leave partials)
  * Supported: what the matrix-core decode covers for the group's queries: block_size 16,
  * head_dim in {64, 128}, (num_heads / num_kv_heads) * seq_group in {2, 4, 8, 16}, q in
- * {f16, bf16} with a cache of the same type or e4m3; the per-sequence launch then follows
+ * {f16, bf16} with a cache of the same type or e4m3; the per-sequence units then follow
  * pa_decode's support.  Other shapes return PA_ERR_UNSUPPORTED (use pa_decode). */
 size_t pa_decode_shared_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
