@@ -824,11 +824,24 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a) {
         } else {
           const size_t pi = row_of(hh) * a.num_slots + slot;
           float* pa_ = a.part_acc + pi * D + c;
+          // Units of 8 or more query rows store their partials with the non-temporal hint
+          // (measured: four draft tokens over the GQA workload, 16 rows per unit, decode
+          // 392.5 vs 400.7 us, merge 14.9 vs 13.8 us); fewer rows keep ordinary stores
+          // (plain GQA even, the fp8 prefix units 0.9 % slower with the hint).
+          if constexpr (G >= 8) {
 #pragma unroll
-          for (int t = 0; t < NTILES; ++t) pa_[16 * t] = cacc[t][i];
-          if (c == 0) {
-            a.part_ml[pi * 2] = Mi;
-            a.part_ml[pi * 2 + 1] = Li;
+            for (int t = 0; t < NTILES; ++t) __builtin_nontemporal_store(cacc[t][i], &pa_[16 * t]);
+            if (c == 0) {
+              __builtin_nontemporal_store(Mi, &a.part_ml[pi * 2]);
+              __builtin_nontemporal_store(Li, &a.part_ml[pi * 2 + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < NTILES; ++t) pa_[16 * t] = cacc[t][i];
+            if (c == 0) {
+              a.part_ml[pi * 2] = Mi;
+              a.part_ml[pi * 2 + 1] = Li;
+            }
           }
         }
       }
