@@ -59,7 +59,8 @@ def measured_traffic(workload: str, decode_path: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 100; 1000 for tiny_mha, whose steps take µs)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="opt13b_layer")
     ap.add_argument("--partition-size", type=int, default=-1,
@@ -87,7 +88,10 @@ def parse():
     ap.add_argument("--swap", type=int, default=0, metavar="N",
                     help="also time pa_swap_blocks moving the blocks of the first N sequences "
                          "to pinned host memory and back, beside a DMA copy of the same bytes")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 1000 if args.workload == "tiny_mha" else 100
+    return args
 
 
 def main():
