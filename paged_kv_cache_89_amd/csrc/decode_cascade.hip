@@ -2,9 +2,11 @@
 // body, per-column masks) take the first workgroups of the grid and the per-sequence
 // units (vector kernel body) the rest.  Both bodies and their unit maps are those of the
 // two separate launches (each reads its own DecodeArgs, whose wg_base / wg_count place
-// its workgroups in the grid); only the kernel boundary between them goes: the long
-// prefix units are dispatched first and the short per-sequence units fill the compute
-// units as prefix units finish, so the launch ramps up and drains once.
+// its workgroups in the grid); only the kernel boundary between them goes, so the launch
+// ramps up and drains once.  The long prefix units are dispatched first; with the plan's
+// 1024-token prefix partitions they take about half of the wavefront slots and the short
+// per-sequence units stream through the rest, then through the slots the prefix units
+// free.
 //
 // e4m3 caches only: their prefix units need 32 KiB of LDS per workgroup and four waves
 // per SIMD, which the vector body fits too; a 16-bit prefix workgroup needs 64 KiB, which
