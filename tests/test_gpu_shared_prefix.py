@@ -77,7 +77,7 @@ def test_shared_prefix_matches_oracle_all_variants(d, dt):
     B, prompt = 16, 53                      # 3 shared blocks, partial prompt block private
     pool = [53, 54, 63, 64, 65, 97, 300, 513]
     short = [0, 1, 17, 47, 48, 49]
-    for G, K in ((1, 2), (1, 4), (2, 2), (1, 16), (2, 4), (4, 4), (8, 2)):
+    for G, K in ((1, 2), (1, 4), (1, 8), (2, 2), (1, 16), (2, 4), (4, 4), (8, 2)):
         lens = [pool[(3 * i + G + K) % len(pool)] for i in range(3 * K)]
         dec = list(lens)
         for k in range(0, K, 2):            # group 0: every other member ends inside the prompt
