@@ -156,22 +156,9 @@ __device__ __forceinline__ void e4m3x16_widen(const u32x4 src, u32x4 (&dst)[2]) 
 // mask), needed by the prefix units of the shared-prefix decode and by multi-token
 // queries; plain and suffix units share one token count and use the cheaper mask.
 // Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one matrix-core column's four
-// row groups) with the gfx950 row swaps, which stay on the VALU.  Measured lane layout:
-// permlane16_swap(x, x) returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of x, permlane32_swap(x,
-// x) halves (0, 0) and (1, 1); combining the two results is combining x with x ^ 16
-// (x ^ 32).  Every lane ends with the same value.
-__device__ __forceinline__ float rows_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
+// row groups), by the row swaps of xor_combine; every lane ends with the same value.
+__device__ __forceinline__ float rows_max(float x) { return across_lanes<16>(x, MaxOp{}); }
+__device__ __forceinline__ float rows_sum(float x) { return across_lanes<16>(x, AddOp{}); }
 
 // e4m3 tiles on the fp8 matrix cores: 1 = K/V go from HBM straight into two LDS stages per
 // wave (global_load_lds; no register staging, about 110 VGPRs, four waves per SIMD);

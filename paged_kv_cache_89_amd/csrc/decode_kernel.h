@@ -414,19 +414,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     // ---- merge the TPL lane-group states of the wave (same rescaling rule)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float M = m[g];
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float M = across_lanes<LPT>(m[g], MaxOp{});
       const float f = (m[g] == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
       float L = l[g] * f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
+      L = across_lanes<LPT>(L, AddOp{});
 #pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) {
-        L += __shfl_xor(L, off);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
-      }
+      for (int e = 0; e < EPL; ++e) acc[g][e] = across_lanes<LPT>(acc[g][e], AddOp{});
       const int h = h0 + g;
       if (a.num_slots == 0) {
         if (lane < LPT) {

@@ -40,6 +40,61 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// op(x, x of lane ^ OFF) for a commutative op, OFF in {1, 2, 4, 8, 16, 32}, by VALU lane
+// moves rather than an LDS-crossbar permute (which costs an LDS round trip and a wait per
+// step): quad permutes for 1 and 2, two bank-masked row shifts for 4 (banks 0 and 2 take
+// the lanes 4 above, banks 1 and 3 the lanes 4 below), a half-row rotate for 8, and the
+// gfx950 permlane16 / permlane32 swaps for 16 and 32.  Measured lane layout:
+// permlane16_swap(x, x) returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of x (16-lane rows),
+// permlane32_swap(x, x) halves (0, 0) and (1, 1); each lane so holds its own value and
+// its partner's, in one order or the other, and op(first, second) is op(own, partner)
+// bit for bit.
+constexpr int DPP_ROW_SHL4 = 0x104;
+constexpr int DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_ROW_ROR8 = 0x128;
+
+template <int OFF, typename Op>
+__device__ __forceinline__ float xor_combine(float x, Op op) {
+  static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32,
+                "lane distance");
+  const int xi = __float_as_int(x);
+  if constexpr (OFF == 1) {
+    return op(x, dpp_mov<DPP_QUAD_XOR1>(x));
+  } else if constexpr (OFF == 2) {
+    return op(x, dpp_mov<DPP_QUAD_XOR2>(x));
+  } else if constexpr (OFF == 4) {
+    int p = __builtin_amdgcn_update_dpp(0, xi, DPP_ROW_SHL4, 0xF, 0x5, false);
+    p = __builtin_amdgcn_update_dpp(p, xi, DPP_ROW_SHR4, 0xF, 0xA, false);
+    return op(x, __int_as_float(p));
+  } else if constexpr (OFF == 8) {
+    return op(x, dpp_mov<DPP_ROW_ROR8>(x));
+  } else if constexpr (OFF == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap((unsigned)xi, (unsigned)xi, false, false);
+    return op(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  } else {
+    const auto s = __builtin_amdgcn_permlane32_swap((unsigned)xi, (unsigned)xi, false, false);
+    return op(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  }
+}
+
+struct AddOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// op over the lanes whose indices differ from this lane's only in bits FROM .. 32 (FROM a
+// power of two), combined from the lowest of those bits up; every lane gets the result.
+template <int FROM, typename Op>
+__device__ __forceinline__ float across_lanes(float x, Op op) {
+  if constexpr (FROM >= 64) {
+    return x;
+  } else {
+    return across_lanes<FROM * 2>(xor_combine<FROM>(x, op), op);
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- conversions ---------------------------------------------------------------------

@@ -14,17 +14,18 @@
 
 namespace pa {
 
-// Wave-wide max / sum (every lane gets the result).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) v = fmaxf(v, __shfl_xor(v, k));
-  return v;
+// Wave-wide max / sum (every lane gets the result), halves first, by VALU lane moves.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = xor_combine<32>(v, op);
+  v = xor_combine<16>(v, op);
+  v = xor_combine<8>(v, op);
+  v = xor_combine<4>(v, op);
+  v = xor_combine<2>(v, op);
+  return xor_combine<1>(v, op);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, MaxOp{}); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, AddOp{}); }
 
 // PF: partial outputs loaded per batch; the first batch goes out with the row's length and
 // its (m, l) pairs, so a row of at most PF slots costs one round trip to memory.

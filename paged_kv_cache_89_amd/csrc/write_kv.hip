@@ -21,15 +21,20 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const WriteArgs a) {
   if (rowi >= (long)a.num_tokens * a.num_kv_heads) return;
   const int t = (int)(rowi / a.num_kv_heads);
   const int h = (int)(rowi % a.num_kv_heads);
-  const int seq = a.seq_ids[t];
-  const int pos = a.positions[t];
+  // The source rows go out with the token's sequence and position, ahead of the checks
+  // (row t < num_tokens is in bounds whatever they find), and the empty asm takes all four
+  // as operands, so they share one round trip (the compiler would otherwise load them one
+  // after another, the rows last); the table lookup is the only other one before the store.
+  const size_t src = ((size_t)t * a.num_kv_heads + h) * D + ch * 8;
+  u32x4 kx = *(const u32x4*)((const uint16_t*)a.k_src + src);
+  u32x4 vx = *(const u32x4*)((const uint16_t*)a.v_src + src);
+  int seq = a.seq_ids[t];
+  int pos = a.positions[t];
+  asm volatile("" : "+v"(kx), "+v"(vx), "+v"(seq), "+v"(pos));
   if (seq < 0 || seq >= a.num_seqs || pos < 0 || pos / BS >= a.max_blocks) return;
   const int blk = a.tables[(size_t)seq * a.max_blocks + pos / BS];
   if (blk < 0 || blk >= a.num_blocks) return;
-  const size_t src = ((size_t)t * a.num_kv_heads + h) * D + ch * 8;
   const size_t dst = (((size_t)blk * a.num_kv_heads + h) * BS + pos % BS) * D + ch * 8;
-  const u32x4 kx = *(const u32x4*)((const uint16_t*)a.k_src + src);
-  const u32x4 vx = *(const u32x4*)((const uint16_t*)a.v_src + src);
   if constexpr (CK == SK) {
     *(u32x4*)((uint16_t*)a.k_cache + dst) = kx;
     *(u32x4*)((uint16_t*)a.v_cache + dst) = vx;
