@@ -350,6 +350,42 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a) {
     if (multi) nx_tm = load_mask(nx.s);
   };
   bool pre_issued = false;  // the segment's first block went out before the last one's partials
+  // (m, L, acc) of rows 4r + i, i < 4, of unit (s_, kvh_) into partial slot slot_
+  auto store_partials = [&](int s_, int kvh_, int slot_, const f32x4 (&acc)[NTILES],
+                            const float (&L_)[4], const float (&M_)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * r + i;
+      if (hh < G) {
+        const size_t pi = row_at(s_, kvh_, hh) * a.num_slots + slot_;
+        float* pa_ = a.part_acc + pi * D + c;
+        // Units of 8 or more query rows store their partials with the non-temporal hint
+        // (measured: four draft tokens over the GQA workload, 16 rows per unit, decode
+        // 392.5 vs 400.7 us, merge 14.9 vs 13.8 us); fewer rows keep ordinary stores
+        // (plain GQA even, the fp8 prefix units 0.9 % slower with the hint).
+        if constexpr (G >= 8) {
+#pragma unroll
+          for (int t = 0; t < NTILES; ++t) __builtin_nontemporal_store(acc[t][i], &pa_[16 * t]);
+          if (c == 0) {
+            __builtin_nontemporal_store(M_[i], &a.part_ml[pi * 2]);
+            __builtin_nontemporal_store(L_[i], &a.part_ml[pi * 2 + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < NTILES; ++t) pa_[16 * t] = acc[t][i];
+          if (c == 0) {
+            a.part_ml[pi * 2] = M_[i];
+            a.part_ml[pi * 2 + 1] = L_[i];
+          }
+        }
+      }
+    }
+  };
+  // the flat walk's pending partials (one segment's, stored at the next segment's end)
+  bool pd_ok = false;
+  int pd_s = 0, pd_kvh = 0, pd_slot = 0;
+  f32x4 pd_acc[FLAT ? NTILES : 1];
+  float pd_L[4], pd_M[4];
   UnitCoords uc{0, 0, 0, true};
   if constexpr (flat) {
     walk.init(a, BS, PA_GQA_WAVES, wave, lane, kFlatMaxChunkMatrix);
@@ -793,45 +829,47 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a) {
         pre_issued = true;
       }
     }
-    // head c's denominator: sum of its four lanes' shares
+    // head c's denominator: sum of its four lanes' shares; accumulator row 4r + i (lane c
+    // holds dim 16t + c of slice t) belongs to head 4r + i, whose (m, L) sit in lane 4r + i
     const float L = rows_sum(l_part);
-    // accumulator row 4r + i (lane c holds dim 16t + c of slice t) belongs to head 4r + i
+    float Lr[4], Mr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hh = 4 * r + i;
-      const float Li = __shfl(L, hh);
-      const float Mi = __shfl(m_ref, hh);
-      if (hh < G) {
-        if (a.num_slots == 0) {
+      Lr[i] = __shfl(L, 4 * r + i);
+      Mr[i] = __shfl(m_ref, 4 * r + i);
+    }
+    if (a.num_slots == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = 4 * r + i;
+        if (hh < G) {
           uint16_t* o = (uint16_t*)a.out + row_of(hh) * D + c;
           // a column that sees no token (possible under a draft mask) gives a zero row
-          const float inv = (Li > 0.f) ? a.v_scale / Li : 0.f;
+          const float inv = (Lr[i] > 0.f) ? a.v_scale / Lr[i] : 0.f;
 #pragma unroll
           for (int t = 0; t < NTILES; ++t) o[16 * t] = f32_to_store<QK>(cacc[t][i] * inv);
-        } else {
-          const size_t pi = row_of(hh) * a.num_slots + slot;
-          float* pa_ = a.part_acc + pi * D + c;
-          // Units of 8 or more query rows store their partials with the non-temporal hint
-          // (measured: four draft tokens over the GQA workload, 16 rows per unit, decode
-          // 392.5 vs 400.7 us, merge 14.9 vs 13.8 us); fewer rows keep ordinary stores
-          // (plain GQA even, the fp8 prefix units 0.9 % slower with the hint).
-          if constexpr (G >= 8) {
-#pragma unroll
-            for (int t = 0; t < NTILES; ++t) __builtin_nontemporal_store(cacc[t][i], &pa_[16 * t]);
-            if (c == 0) {
-              __builtin_nontemporal_store(Mi, &a.part_ml[pi * 2]);
-              __builtin_nontemporal_store(Li, &a.part_ml[pi * 2 + 1]);
-            }
-          } else {
-#pragma unroll
-            for (int t = 0; t < NTILES; ++t) pa_[16 * t] = cacc[t][i];
-            if (c == 0) {
-              a.part_ml[pi * 2] = Mi;
-              a.part_ml[pi * 2 + 1] = Li;
-            }
-          }
         }
       }
+    } else if constexpr (flat) {
+      // The walk's partials leave one segment late: the previous segment's now, this one's
+      // at the next segment's end or after the walk.  (A wave's next wait on its loads also
+      // waits for every store it issued before them, and stores issued among a full-rate
+      // read stream are slow to complete: storing each segment's partials at its end cost
+      // the four-draft-token GQA decode 22 us of 393.)
+      if (pd_ok) store_partials(pd_s, pd_kvh, pd_slot, pd_acc, pd_L, pd_M);
+      pd_ok = true;
+      pd_s = s;
+      pd_kvh = kvh;
+      pd_slot = slot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pd_L[i] = Lr[i];
+        pd_M[i] = Mr[i];
+#pragma unroll
+        for (int t = 0; t < NTILES; ++t) pd_acc[t][i] = cacc[t][i];
+      }
+    } else {
+      store_partials(s, kvh, slot, cacc, Lr, Mr);
     }
     // appending decode, LDS-ring path: the new rows into the cache, after everything that
     // read the block
@@ -841,6 +879,9 @@ __device__ __forceinline__ void gqa_body(const DecodeArgs& a) {
       *(u32x4*)((char*)a.k + dst) = nk;
       *(u32x4*)((char*)a.v + dst) = nv;
     }
+  }
+  if constexpr (flat) {
+    if (pd_ok) store_partials(pd_s, pd_kvh, pd_slot, pd_acc, pd_L, pd_M);
   }
 }
 

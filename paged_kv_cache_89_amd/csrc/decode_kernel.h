@@ -137,6 +137,54 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     nx_ts.init(a.tables + (size_t)nx.s * a.max_blocks, nx.j0, nx.j1, a.num_blocks, lane);
     load_query(nx.s, nx.kvh, nx_q);
   };
+  // Partial stores: acc slice c of a row (lanes < LPT) and the row's (m, L) (lane 0).
+  auto store_acc = [&](size_t pi, const float (&v)[EPL]) {
+    float* pa_ = a.part_acc + pi * D + c * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const f32x4v t = f32x4v{v[e], v[e + 1], v[e + 2], v[e + 3]};
+      if constexpr (NT_PARTIALS) __builtin_nontemporal_store(t, (f32x4v*)(pa_ + e));
+      else *(f32x4v*)(pa_ + e) = t;
+    }
+  };
+  auto store_ml = [&](size_t pi, float M_, float L_) {
+    if constexpr (NT_PARTIALS) {
+      __builtin_nontemporal_store(M_, &a.part_ml[pi * 2]);
+      __builtin_nontemporal_store(L_, &a.part_ml[pi * 2 + 1]);
+    } else {
+      a.part_ml[pi * 2] = M_;
+      a.part_ml[pi * 2 + 1] = L_;
+    }
+  };
+  // The flat walk's partials leave one segment late: a segment's wait in LDS (never in
+  // registers, which would cost occupancy) and go out at the next segment's end or after
+  // the walk.  A wave's next wait on its loads also waits for every store it issued
+  // before them, and stores issued among a full-rate read stream are slow to complete.
+  [[maybe_unused]] bool pd_ok = false;
+  [[maybe_unused]] int pd_s = 0, pd_h0 = 0, pd_slot = 0;
+  __shared__ __attribute__((aligned(16))) float pend_acc[PA_DECODE_WAVES][FLAT ? G * D : 4];
+  __shared__ float pend_ml[PA_DECODE_WAVES][FLAT ? 2 * G : 2];
+  [[maybe_unused]] auto flush_pending = [&]() {
+    if (!pd_ok) return;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const size_t pi = ((size_t)pd_s * a.num_heads + pd_h0 + g) * a.num_slots + pd_slot;
+      if (lane < LPT) {
+        float v[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+          const f32x4v t = *(const f32x4v*)&pend_acc[wave][g * D + c * EPL + e];
+          v[e] = t[0];
+          v[e + 1] = t[1];
+          v[e + 2] = t[2];
+          v[e + 3] = t[3];
+        }
+        store_acc(pi, v);
+      }
+      if (lane == 0) store_ml(pi, pend_ml[wave][2 * g], pend_ml[wave][2 * g + 1]);
+    }
+    pd_ok = false;
+  };
   // the pipeline's first register set: under the flat split it can already hold the next
   // segment's first block, requested before the last segment's epilogue
   LT ka[NLD], va[NLD];
@@ -411,6 +459,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       }
     }
 
+    if constexpr (flat) flush_pending();
     // ---- merge the TPL lane-group states of the wave (same rescaling rule)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -442,27 +491,30 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
             op[k] = t;
           }
         }
-      } else {
-        const size_t pi = ((size_t)s * a.num_heads + h) * a.num_slots + slot;
+      } else if constexpr (flat) {
+        // this segment's partials wait in LDS until the next segment ends (the previous
+        // segment's went out at the top of this epilogue)
         if (lane < LPT) {
-          float* pa_ = a.part_acc + pi * D + c * EPL;
 #pragma unroll
-          for (int e = 0; e < EPL; e += 4) {
-            const f32x4v t = f32x4v{acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]};
-            if constexpr (NT_PARTIALS) __builtin_nontemporal_store(t, (f32x4v*)(pa_ + e));
-            else *(f32x4v*)(pa_ + e) = t;
-          }
+          for (int e = 0; e < EPL; e += 4)
+            *(f32x4v*)&pend_acc[wave][g * D + c * EPL + e] =
+                f32x4v{acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]};
         }
         if (lane == 0) {
-          if constexpr (NT_PARTIALS) {
-            __builtin_nontemporal_store(M, &a.part_ml[pi * 2]);
-            __builtin_nontemporal_store(L, &a.part_ml[pi * 2 + 1]);
-          } else {
-            a.part_ml[pi * 2] = M;
-            a.part_ml[pi * 2 + 1] = L;
-          }
+          pend_ml[wave][2 * g] = M;
+          pend_ml[wave][2 * g + 1] = L;
         }
+      } else {
+        const size_t pi = ((size_t)s * a.num_heads + h) * a.num_slots + slot;
+        if (lane < LPT) store_acc(pi, acc[g]);
+        if (lane == 0) store_ml(pi, M, L);
       }
+    }
+    if constexpr (flat) {
+      pd_ok = a.num_slots > 0;
+      pd_s = s;
+      pd_h0 = h0;
+      pd_slot = slot;
     }
     // appending decode: the new rows into the cache, after everything that read the block
     if (app && r == tn % TPL) {
@@ -472,6 +524,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       *(LT*)((char*)a.v + dst) = nv;
     }
   }
+  if constexpr (flat) flush_pending();
 }
 
 template <int D, int BS, int QK, int KVK, int G, bool NT, bool APP, bool FLAT>
