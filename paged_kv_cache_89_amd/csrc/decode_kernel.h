@@ -137,14 +137,32 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     nx_ts.init(a.tables + (size_t)nx.s * a.max_blocks, nx.j0, nx.j1, a.num_blocks, lane);
     load_query(nx.s, nx.kvh, nx_q);
   };
-  // Partial stores: acc slice c of a row (lanes < LPT) and the row's (m, L) (lane 0).
-  auto store_acc = [&](size_t pi, const float (&v)[EPL]) {
+  // Partial stores: a row's accumulator and its (m, L) (lane 0).  A unit's row: after the
+  // end-of-unit reduce-scatter every lane holds NV consecutive elements of the row, from
+  // element rs_first of its slice c on, so the row leaves in one store instruction of the
+  // whole wave.  A flat-walk segment's row: slice c of lanes < LPT (the walk keeps the
+  // full lane-group merge: the reduce-scatter's lane selects would cost those kernels an
+  // occupancy step, measured in VGPRs).
+  constexpr int NV = EPL * LPT / 64;
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  auto store_slice = [&](size_t pi, const float (&v)[EPL]) {
     float* pa_ = a.part_acc + pi * D + c * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) {
       const f32x4v t = f32x4v{v[e], v[e + 1], v[e + 2], v[e + 3]};
       if constexpr (NT_PARTIALS) __builtin_nontemporal_store(t, (f32x4v*)(pa_ + e));
       else *(f32x4v*)(pa_ + e) = t;
+    }
+  };
+  auto store_acc = [&](size_t pi, const float (&v)[NV]) {
+    float* pa_ = a.part_acc + pi * D + c * EPL + rs_first<LPT, EPL>(lane);
+    if constexpr (NV == 2) {
+      if constexpr (NT_PARTIALS) __builtin_nontemporal_store(f32x2v{v[0], v[1]}, (f32x2v*)pa_);
+      else *(f32x2v*)pa_ = f32x2v{v[0], v[1]};
+    } else {
+      static_assert(NV == 1, "elements per lane");
+      if constexpr (NT_PARTIALS) __builtin_nontemporal_store(v[0], pa_);
+      else *pa_ = v[0];
     }
   };
   auto store_ml = [&](size_t pi, float M_, float L_) {
@@ -179,7 +197,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
           v[e + 2] = t[2];
           v[e + 3] = t[3];
         }
-        store_acc(pi, v);
+        store_slice(pi, v);
       }
       if (lane == 0) store_ml(pi, pend_ml[wave][2 * g], pend_ml[wave][2 * g + 1]);
     }
@@ -469,31 +487,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[g][e] *= f;
       L = across_lanes<LPT>(L, AddOp{});
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = across_lanes<LPT>(acc[g][e], AddOp{});
       const int h = h0 + g;
-      if (a.num_slots == 0) {
-        if (lane < LPT) {
-          uint16_t ob[EPL];
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) {
-            float o = acc[g][e] / L;
-            if constexpr (F8) o = o * a.v_scale;
-            ob[e] = f32_to_store<QK>(o);
-          }
-          u32x4* op = (u32x4*)((uint16_t*)a.out + ((size_t)s * a.num_heads + h) * D + c * EPL);
-#pragma unroll
-          for (int k = 0; k < EPL / 8; ++k) {
-            u32x4 t;
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-              t[w] = (uint32_t)ob[8 * k + 2 * w] | ((uint32_t)ob[8 * k + 2 * w + 1] << 16);
-            op[k] = t;
-          }
-        }
-      } else if constexpr (flat) {
+      if constexpr (flat) {
         // this segment's partials wait in LDS until the next segment ends (the previous
-        // segment's went out at the top of this epilogue)
+        // segment's went out at the top of this epilogue); the walk always has slots
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = across_lanes<LPT>(acc[g][e], AddOp{});
         if (lane < LPT) {
 #pragma unroll
           for (int e = 0; e < EPL; e += 4)
@@ -504,9 +503,27 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
           pend_ml[wave][2 * g] = M;
           pend_ml[wave][2 * g + 1] = L;
         }
+        continue;
+      }
+      reduce_scatter<LPT>(acc[g], lane);  // acc[g][0 .. NV): elements fst.. of slice c
+      const int fst = rs_first<LPT, EPL>(lane);
+      float ov[NV];
+#pragma unroll
+      for (int e = 0; e < NV; ++e) ov[e] = acc[g][e];
+      if (a.num_slots == 0) {
+        uint16_t* op = (uint16_t*)a.out + ((size_t)s * a.num_heads + h) * D + c * EPL + fst;
+        uint16_t ob[NV];
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          float o = ov[e] / L;
+          if constexpr (F8) o = o * a.v_scale;
+          ob[e] = f32_to_store<QK>(o);
+        }
+        if constexpr (NV == 2) *(uint32_t*)op = (uint32_t)ob[0] | ((uint32_t)ob[1] << 16);
+        else *op = ob[0];
       } else {
         const size_t pi = ((size_t)s * a.num_heads + h) * a.num_slots + slot;
-        if (lane < LPT) store_acc(pi, acc[g]);
+        store_acc(pi, ov);
         if (lane == 0) store_ml(pi, M, L);
       }
     }

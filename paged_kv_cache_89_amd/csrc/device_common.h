@@ -95,6 +95,74 @@ __device__ __forceinline__ float across_lanes(float x, Op op) {
   }
 }
 
+// Reduce-scatter of N values over the lanes whose indices differ from this lane's only in
+// bits FROM .. 32 (FROM in {4, 8, 16}): afterwards v[0 .. N * FROM / 64) hold the sums of
+// values rs_first<FROM, N>(lane) onwards.  Each step pairs lane l with l ^ OFF; the lane
+// with bit OFF clear keeps the lower half of its live values, the other the upper half,
+// and each adds what its partner sends of its own half (DPP moves inside a row for 4 and
+// 8, the permlane swaps for 16 and 32, which bring both lanes' values in one move).  Every
+// sum is own + partner at each step, from the lowest bit up, as across_lanes forms it, so
+// the results are the same bits, with N/2 + N/4 + ... lane moves instead of N per step.
+template <int OFF>
+__device__ __forceinline__ float xor_partner(float x) {
+  static_assert(OFF == 4 || OFF == 8, "DPP lane distance");
+  if constexpr (OFF == 8) {
+    return dpp_mov<DPP_ROW_ROR8>(x);
+  } else {
+    const int xi = __float_as_int(x);
+    int p = __builtin_amdgcn_update_dpp(0, xi, DPP_ROW_SHL4, 0xF, 0x5, false);
+    p = __builtin_amdgcn_update_dpp(p, xi, DPP_ROW_SHR4, 0xF, 0xA, false);
+    return __int_as_float(p);
+  }
+}
+
+template <int OFF, int LIVE, int N>
+__device__ __forceinline__ void rs_steps(float (&v)[N], int lane) {
+  if constexpr (OFF < 64) {
+    constexpr int H = LIVE / 2;
+    static_assert(H >= 1, "more lanes than values");
+    if constexpr (OFF == 16 || OFF == 32) {
+#pragma unroll
+      for (int k = 0; k < H; ++k) {
+        const unsigned lo = __float_as_uint(v[k]), hi = __float_as_uint(v[k + H]);
+        if constexpr (OFF == 16) {
+          const auto t = __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+          v[k] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+        } else {
+          const auto t = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+          v[k] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+        }
+      }
+    } else {
+      const bool upper = (lane & OFF) != 0;
+#pragma unroll
+      for (int k = 0; k < H; ++k) {
+        const float keep = upper ? v[k + H] : v[k];
+        const float send = upper ? v[k] : v[k + H];
+        v[k] = keep + xor_partner<OFF>(send);
+      }
+    }
+    rs_steps<OFF * 2, H, N>(v, lane);
+  }
+}
+
+template <int FROM, int N>
+__device__ __forceinline__ void reduce_scatter(float (&v)[N], int lane) {
+  static_assert(N * FROM / 64 >= 1, "more lanes than values");
+  rs_steps<FROM, N, N>(v, lane);
+}
+
+template <int FROM, int N>
+__device__ __forceinline__ int rs_first(int lane) {
+  int first = 0, live = N;
+#pragma unroll
+  for (int off = FROM; off < 64; off <<= 1) {
+    live /= 2;
+    if (lane & off) first += live;
+  }
+  return first;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- conversions ---------------------------------------------------------------------
